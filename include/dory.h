@@ -1,0 +1,180 @@
+/*
+ * dory.h -- C ABI of libdory.so: the token forward of the Dory looped normalized
+ * GPT on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages of the cortiq-engine crate, "dory.rs" = the Dory module page,
+ * "kv_cache.rs" = the KV cache module page):
+ *   - dory.rs, module documentation and `stack`: a token passes an input block,
+ *     a recurrent block run `loops` times with the input block's output re-added
+ *     and renormalised before each pass, and an output block.  A sub-layer is one
+ *     attention or one SwiGLU MLP; every residual state lives on the unit sphere.
+ *   - dory.rs `attn_layer`: q,k,v,g projections, RoPE, per-head unit norm, q
+ *     scaled by sq, k unit; grouped-query softmax over a sliding or full window;
+ *     output gated by sigmoid(g*sg), renormalised over the row, projected by O.
+ *   - dory.rs `mlp_layer`: silu(a*sg)*(b*su), renormalised, projected down.
+ *   - dory.rs `slerp`: the residual x = norm(norm(x) + |alpha|*(norm(out) - norm(x))).
+ *   - dory.rs `KvMode`, `slot_loop`, `stack`: per_loop keeps one cache per loop of
+ *     each recurrent attention layer; last_loop keeps one, each loop rewriting the
+ *     call's rows.
+ *   - kv_cache.rs `quant_row`, `freeze_cols`, `append`, `attend_group_upto`: the
+ *     optional q8_2f cache encoding (int8 codes, K scales per 32 channels, V scale
+ *     per row, per-channel field frozen after 64 rows and applied retroactively).
+ *
+ * Conventions for every entry point:
+ *   - Status codes: DORY_OK (0) or a negative DORY_E* value.  Every argument check
+ *     runs before any work is enqueued; a failed check changes no state.  The
+ *     message of the last failure is available from dory_last_error().
+ *   - "device" pointers are HIP device memory on the current device; "host"
+ *     pointers are ordinary CPU memory.
+ *   - Calls on one handle must be serialised by the caller (one stream, or
+ *     synchronised streams); the handle is not thread-safe.
+ */
+#ifndef DORY_H
+#define DORY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DORY_OK 0
+#define DORY_EINVAL (-1)   /* bad argument or configuration */
+#define DORY_ESTATE (-2)   /* call disagrees with the sequence's state (kv mode, per_loop loop count) */
+#define DORY_ERANGE (-3)   /* n > max_chunk, position past max_ctx, a row no longer held */
+#define DORY_ENOMEM (-4)   /* device allocation failed */
+#define DORY_EDEVICE (-5)  /* a HIP call failed */
+
+#define DORY_PER_LOOP 0    /* dory.rs `KvMode::PerLoop` */
+#define DORY_LAST_LOOP 1   /* dory.rs `KvMode::LastLoop` */
+#define DORY_KV_F32 0      /* fp32 cache rows */
+#define DORY_KV_Q8_2F 1    /* kv_cache.rs q8_2f encoding */
+#define DORY_W_F32 0       /* fp32 weight matrices */
+#define DORY_W_BF16 1      /* bf16 weight matrices (fp32 accumulation) */
+#define DORY_MAX_LOOPS 16  /* dory.rs `MAX_LOOPS` */
+
+typedef void *dory_stream_t; /* a hipStream_t; NULL is the null stream */
+
+/* Model geometry and capacities (dory.rs `DoryCfg`, plus what a device library
+ * must size up front). */
+typedef struct {
+    int32_t hidden, ffn, vocab;    /* H, F, V */
+    int32_t nh, nk, hd;            /* q heads, kv heads (nh % nk == 0), head dim */
+    const char *layer_pattern;     /* one char per sub-layer: '-' SwiGLU MLP, 'S' sliding
+                                      attention, any other character full attention */
+    int32_t n_in, n_rec, n_out;    /* sub-layers of the input, recurrent, output blocks */
+    int32_t window;                /* sliding layers read keys p-window+1 ..= p */
+    int32_t full_window;           /* full layers read at most this many keys; 0 = all */
+    double rope_theta_sliding, rope_theta_full;
+    int32_t max_ctx;               /* most positions a sequence may hold */
+    int32_t max_chunk;             /* most rows one call may carry */
+    int32_t max_seqs;              /* independent sequences (each with its own cache) */
+    int32_t kv_encoding;           /* DORY_KV_F32 or DORY_KV_Q8_2F */
+    int32_t weight_dtype;          /* DORY_W_F32 or DORY_W_BF16 */
+} dory_config;
+
+/* Weights of one sub-layer: device pointers, matrices row-major [out][in] in
+ * weight_dtype, vectors fp32.  The vectors are the EFFECTIVE scales (the pages'
+ * folded values: sq, sg, su, |alpha|).  Attention reads wq [Q][H], wk [KV][H],
+ * wv [KV][H], wg [Q][H], wo [H][Q], sq [Q], sg [Q], alpha [H]; an MLP reads
+ * wgate [F][H], wup [F][H], wdown [H][F], sg [F], su [F], alpha [H]
+ * (Q = nh*hd, KV = nk*hd). */
+typedef struct {
+    const void *wq, *wk, *wv, *wg, *wo;
+    const float *sq;
+    const void *wgate, *wup, *wdown;
+    const float *su;
+    const float *sg;
+    const float *alpha;
+} dory_layer_weights;
+
+typedef struct {
+    const void *embed;             /* [V][H] weight_dtype */
+    const void *head;              /* [V][H] weight_dtype */
+    const float *logit_scale;      /* [V] */
+    const dory_layer_weights *layers; /* host array, one entry per sub-layer */
+} dory_weights;
+
+typedef struct dory dory_t;
+
+/* Builds a model over caller-owned device weights (which must outlive the handle,
+ * unchanged) and allocates the caches and scratch.  Errors: DORY_EINVAL (bad
+ * geometry: pattern length != n_in+n_rec+n_out, a block empty, nh % nk, hd not in
+ * {8,16,32,64,128,256}, H, Q or F not a multiple of 8 or above 8192, ...),
+ * DORY_ENOMEM, DORY_EDEVICE.  *out is NULL on failure. */
+int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out);
+
+void dory_destroy(dory_t *h);
+
+/* Message of the last failed call on h (owned by h; valid until the next call).
+ * With h == NULL: the last dory_create failure of this thread. */
+const char *dory_last_error(const dory_t *h);
+
+/* One forward call: n rows (tokens, host int32, copied before return) at the
+ * sequence's next positions -- dory.rs `forward_host` for one chunk, `stack`
+ * for the walk.  loops in 1..16.  kv_mode is fixed per sequence until
+ * dory_kv_reset; under per_loop the loop count is fixed too (DORY_ESTATE).
+ * Token ids outside [0, vocab) embed as zero rows.  logits: device fp32 [vocab]
+ * for row n-1, scaled by logit_scale, or NULL for no head (`Want::None`).
+ * Asynchronous on stream; logits are valid once the stream has reached the end
+ * of this call.  Rows of one call are written to the cache at each loop before
+ * any row of that loop reads it, and each row reads keys up to its own position. */
+int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
+                       int32_t loops, int32_t kv_mode, dory_stream_t stream, float *logits);
+
+/* A new sequence (dory.rs `DoryState::clear`, kv_cache.rs `clear`): position 0,
+ * kv mode and loop count free again, q8 fields unfrozen.  seq == -1: all. */
+int dory_kv_reset(dory_t *h, int32_t seq);
+
+/* Next position of a sequence (rows held), or a negative status. */
+int64_t dory_position(const dory_t *h, int32_t seq);
+
+/* Test tap: later calls also write the residual state after every sub-layer pass
+ * to buf, device fp32 [passes][n][hidden] with passes = n_in + n_rec*loops +
+ * n_out.  cap is buf's size in floats; a call that needs more fails with
+ * DORY_EINVAL.  buf == NULL turns the tap off. */
+int dory_debug_tap(dory_t *h, float *buf, int64_t cap);
+
+/* Test tap: copies one stored cache row of (sequence, attention ordinal, slot)
+ * at position pos to host memory, after synchronising the device.
+ * Layout -- fp32 cache: K [nk][hd] then V [nk][hd] floats (8*nk*hd bytes);
+ * q8_2f: K codes [nk][hd] int8, V codes [nk][hd] int8, K scales [nk][ceil(hd/32)]
+ * fp32, V scales [nk] fp32.  DORY_ERANGE if pos is not held (at or past the
+ * position, or overwritten by the ring). */
+int dory_kv_read(dory_t *h, int32_t seq, int32_t ord, int32_t slot, int64_t pos, void *host_out);
+
+/* Test tap: the q8_2f fields of a slot, host fp32 [nk][hd] each (either may be
+ * NULL).  Returns 1 if frozen, 0 if not, or a negative status. */
+int dory_kv_field(dory_t *h, int32_t seq, int32_t ord, int32_t slot, float *kcol, float *vcol);
+
+/* Test and benchmark set-up: fills a fresh sequence (position 0) with npos rows
+ * per slot through the same append rules a forward uses (q8_2f: encoding, and
+ * the freeze at the 65th row), then sets its position to npos, kv mode and (for
+ * per_loop) loop count.  k, v: host fp32 [n_ord][n_slot][npos][nk][hd], stored
+ * keys (already rotated and normed) and values; n_slot >= loops under per_loop,
+ * >= 1 under last_loop; slots a mode does not use are skipped.  Synchronous. */
+int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t npos,
+                 int32_t n_slot, const float *k, const float *v);
+
+/* The q8_2f row encoder on its own (kv_cache.rs `quant_row`): rows rows of n
+ * fp32 values (device, row-major), divided by col (device [n], or NULL = no
+ * field), split in groups of `group` channels (32 or n; the last may be short),
+ * scale = max(absmax/127, 1e-12), code = clamp(round-half-away(r/scale), -127,
+ * 127).  codes: device int8 [rows][n]; scales: device fp32 [rows][ceil(n/group)].
+ * n <= 256.  Asynchronous on stream. */
+int dory_q8_encode_rows(const float *x, const float *col, int32_t rows, int32_t n, int32_t group,
+                        int8_t *codes, float *scales, dory_stream_t stream);
+
+/* Benchmark tap: launches one kernel of the one-row forward `reps` times back to
+ * back on stream, over the handle's current scratch (left by the last call) and
+ * sequence 0's cache at its last position, cycling through the sub-layers that
+ * have that kernel so each launch streams its own weights from HBM.  Stage:
+ * 0 q|k|v|g projection, 1 attention, 2 O projection, 3 gate|up projection with
+ * SwiGLU, 4 down projection, 5 head.  Needs a prior one-row call on sequence 0.
+ * Leaves the scratch undefined (the cache and positions are untouched). */
+int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,783 @@
+// api.hip -- the host runtime of libdory.so behind the C ABI of include/dory.h:
+// configuration checks, device memory, the cache rings, the per-call record,
+// the walk through the sub-layers (dory.rs `stack`) and one captured HIP graph
+// per (loops, kv mode) for one-row calls.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "dory.h"
+#include "internal.h"
+
+using namespace dk;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct LayerInfo {
+    bool attn = false, sliding = false, rec = false;
+    int ord = -1;
+    dory_layer_weights w{};
+};
+
+struct SeqState {
+    int64_t pos = 0;
+    int mode = -1;   // fixed from the first call until a reset
+    int loops = 0;   // per_loop: fixed from the first call until a reset
+};
+
+constexpr int kStages = 32;
+constexpr int64_t kHuge = (int64_t)1 << 62;
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+}  // namespace
+
+struct dory {
+    dory_config cfg{};
+    std::string pattern;
+    dory_weights w{};
+    std::vector<dory_layer_weights> wl;
+    std::vector<LayerInfo> L;
+    int n_ord = 0;
+    int H = 0, F = 0, V = 0, Q = 0, KV = 0, nh = 0, nk = 0, hd = 0, ngk = 0, wt = 0, q8 = 0;
+    int cap_s = 0, cap_f = 0;
+    int split_dec = 64, split_pf = 256, ms_dec = 1, ms_pf = 1;
+    int64_t win_s = 0, win_f = 0;
+    // device scratch
+    float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
+    float *z = nullptr, *zn = nullptr, *ga = nullptr, *gb = nullptr, *un = nullptr, *kstage = nullptr;
+    float *part = nullptr, *inv_s = nullptr, *inv_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
+    int32_t *cnt = nullptr;
+    CallRec *rec = nullptr;
+    SlotDesc *tab = nullptr;
+    std::vector<SlotDesc> tab_host;
+    std::vector<void *> allocs;
+    // pinned staging of call records
+    char *stage = nullptr;
+    size_t rec_sz = 0;
+    hipEvent_t stage_ev[kStages]{};
+    bool stage_used[kStages]{};
+    int stage_i = 0;
+    hipStream_t cap_stream = nullptr;
+    std::map<std::tuple<int, int>, hipGraphExec_t> graphs;
+    float *tap = nullptr;
+    int64_t tap_cap = 0;
+    std::vector<SeqState> seqs;
+    std::string err;
+    int device = 0;
+    int last_loops = 0, last_mode = -1;  // of the last one-row call on sequence 0
+};
+
+namespace {
+
+int fail(dory_t *h, int code, const std::string &msg) {
+    if (h) h->err = msg;
+    else g_create_error = msg;
+    return code;
+}
+
+int hip_fail(dory_t *h, hipError_t e, const char *what) {
+    return fail(h, e == hipErrorOutOfMemory ? DORY_ENOMEM : DORY_EDEVICE,
+                std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIPCHECK(h, call)                                   \
+    do {                                                    \
+        hipError_t e_ = (call);                             \
+        if (e_ != hipSuccess) return hip_fail(h, e_, #call); \
+    } while (0)
+
+template <typename T>
+hipError_t dmalloc(dory_t *h, T **p, size_t count) {
+    void *q = nullptr;
+    hipError_t e = hipMalloc(&q, count ? sizeof(T) * count : 16);
+    if (e == hipSuccess) {
+        h->allocs.push_back(q);
+        *p = reinterpret_cast<T *>(q);
+    }
+    return e;
+}
+
+int passes(const dory_t *h, int loops) { return h->cfg.n_in + h->cfg.n_rec * loops + h->cfg.n_out; }
+
+int check_config(const dory_config *c, const dory_weights *w) {
+    auto bad = [](const std::string &m) { return fail(nullptr, DORY_EINVAL, "dory_create: " + m); };
+    if (!c || !w || !c->layer_pattern || !w->layers) return bad("null argument");
+    const int nl = (int)strlen(c->layer_pattern);
+    if (c->n_in < 1 || c->n_rec < 1 || c->n_out < 1) return bad("every block needs at least one sub-layer");
+    if (nl != c->n_in + c->n_rec + c->n_out) return bad("pattern length != n_in + n_rec + n_out");
+    if (c->nh <= 0 || c->nk <= 0 || c->nh % c->nk) return bad("nh must be a positive multiple of nk");
+    const int rep = c->nh / c->nk;
+    if (rep != 1 && rep != 2 && rep != 4 && rep != 8) return bad("nh/nk must be 1, 2, 4 or 8");
+    if (c->hd != 8 && c->hd != 16 && c->hd != 32 && c->hd != 64 && c->hd != 128 && c->hd != 256)
+        return bad("hd must be 8, 16, 32, 64, 128 or 256");
+    const int Q = c->nh * c->hd;
+    for (int v : {c->hidden, c->ffn, Q})
+        if (v <= 0 || v % 8 || v > 8192) return bad("hidden, ffn and nh*hd must be multiples of 8 up to 8192");
+    if (c->vocab <= 0) return bad("vocab must be positive");
+    if (c->window <= 0 || c->full_window < 0) return bad("window must be positive, full_window >= 0");
+    if (c->max_chunk <= 0 || c->max_ctx < c->max_chunk || c->max_seqs <= 0)
+        return bad("need 0 < max_chunk <= max_ctx and max_seqs > 0");
+    if (c->kv_encoding != DORY_KV_F32 && c->kv_encoding != DORY_KV_Q8_2F) return bad("kv_encoding");
+    if (c->weight_dtype != DORY_W_F32 && c->weight_dtype != DORY_W_BF16) return bad("weight_dtype");
+    if (!w->embed || !w->head || !w->logit_scale) return bad("null embed, head or logit_scale");
+    for (int li = 0; li < nl; ++li) {
+        const dory_layer_weights &x = w->layers[li];
+        if (c->layer_pattern[li] == '-') {
+            if (!x.wgate || !x.wup || !x.wdown || !x.sg || !x.su || !x.alpha)
+                return bad("null MLP weight at sub-layer " + std::to_string(li));
+        } else if (!x.wq || !x.wk || !x.wv || !x.wg || !x.wo || !x.sq || !x.sg || !x.alpha) {
+            return bad("null attention weight at sub-layer " + std::to_string(li));
+        }
+    }
+    return DORY_OK;
+}
+
+void free_all(dory_t *h) {
+    for (auto &g : h->graphs) (void)hipGraphExecDestroy(g.second);
+    h->graphs.clear();
+    for (void *p : h->allocs) (void)hipFree(p);
+    h->allocs.clear();
+    for (int i = 0; i < kStages; ++i)
+        if (h->stage_ev[i]) (void)hipEventDestroy(h->stage_ev[i]);
+    if (h->stage) (void)hipHostFree(h->stage);
+    if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
+}
+
+// The slot (attention ordinal x loop) a sub-layer uses (dory.rs `slot_loop`).
+int slot_of(const dory_t *h, const LayerInfo &l, int mode, int loop_i) {
+    return (mode == DORY_PER_LOOP && l.rec) ? loop_i : 0;
+}
+
+int alloc_slot(dory_t *h, int seq, int ord, int slot, bool sliding) {
+    SlotDesc &d = h->tab_host[(seq * h->n_ord + ord) * kMaxLoops + slot];
+    if (d.k || d.kc) return DORY_OK;
+    const int cap = sliding ? h->cap_s : h->cap_f;
+    const size_t rows = (size_t)h->nk * cap;
+    d.cap = cap;
+    if (h->q8) {
+        int8_t *kc, *vc;
+        float *ks, *vs, *kcol, *vcol;
+        HIPCHECK(h, dmalloc(h, &kc, rows * h->hd));
+        HIPCHECK(h, dmalloc(h, &vc, rows * h->hd));
+        HIPCHECK(h, dmalloc(h, &ks, rows * h->ngk));
+        HIPCHECK(h, dmalloc(h, &vs, rows));
+        HIPCHECK(h, dmalloc(h, &kcol, (size_t)h->KV));
+        HIPCHECK(h, dmalloc(h, &vcol, (size_t)h->KV));
+        d.kc = kc; d.vc = vc; d.ks = ks; d.vs = vs; d.kcol = kcol; d.vcol = vcol;
+    } else {
+        float *k, *v;
+        HIPCHECK(h, dmalloc(h, &k, rows * h->hd));
+        HIPCHECK(h, dmalloc(h, &v, rows * h->hd));
+        d.k = k; d.v = v;
+    }
+    const size_t idx = (size_t)(seq * h->n_ord + ord) * kMaxLoops + slot;
+    HIPCHECK(h, hipMemcpy(h->tab + idx, &d, sizeof(SlotDesc), hipMemcpyHostToDevice));
+    return DORY_OK;
+}
+
+// Every slot a (mode, loops) call touches on seq.
+int ensure_slots(dory_t *h, int seq, int mode, int loops) {
+    for (const LayerInfo &l : h->L) {
+        if (!l.attn) continue;
+        const int ns = (mode == DORY_PER_LOOP && l.rec) ? loops : 1;
+        for (int s = 0; s < ns; ++s) {
+            int rc = alloc_slot(h, seq, l.ord, s, l.sliding);
+            if (rc) return rc;
+        }
+    }
+    return DORY_OK;
+}
+
+// ------------------------------------------------------------------ enqueue
+
+struct Enq {
+    dory_t *h;
+    hipStream_t s;
+    int T, loops, mode;
+    int64_t pos0;      // host copy, for the q8 freeze decisions
+    bool want_logits;  // head GEMV for a multi-row call
+    std::vector<uint8_t> froze;  // slots frozen by this call: [n_ord][kMaxLoops]
+};
+
+#define LAUNCH(call)                                            \
+    do {                                                        \
+        hipError_t e_ = (call);                                 \
+        if (e_ != hipSuccess) return hip_fail(q.h, e_, #call);  \
+    } while (0)
+
+int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const float *x) {
+    dory_t *h = q.h;
+    const int T = q.T, ld = 2 * h->Q + 2 * h->KV;
+    const int slot = slot_of(h, l, q.mode, loop_i);
+    const dory_layer_weights &w = l.w;
+    if (T == 1) {
+        GemvArgs a{};
+        a.w[0] = w.wq; a.w[1] = w.wk; a.w[2] = w.wv; a.w[3] = w.wg;
+        a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
+        a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
+        LAUNCH(launch_gemv(h->wt, kProResolve, kEpiStore, a, q.s));
+    } else {
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wq, h->Q, h->H, h->qkvg, ld, T, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wk, h->KV, h->H, h->qkvg + h->Q, ld, T, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wv, h->KV, h->H, h->qkvg + h->Q + h->KV, ld, T, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wg, h->Q, h->H, h->qkvg + h->Q + 2 * h->KV, ld, T, q.s));
+    }
+    PrepArgs pa{};
+    pa.qkvg = h->qkvg; pa.qp = h->qp; pa.kstage = h->q8 ? h->kstage : nullptr;
+    pa.inv = l.sliding ? h->inv_s : h->inv_f; pa.sq = w.sq; pa.tab = h->tab;
+    pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = h->rec;
+    LAUNCH(launch_prep(pa, T, q.s));
+    bool field = false;
+    if (h->q8) {
+        // kv_cache.rs `append`: the field freezes when the 65th row (position 64)
+        // is appended; rows before it were encoded without a field, rows after
+        // against it.  A later loop's rewrite of the same rows finds it frozen.
+        uint8_t &froze = q.froze[l.ord * kMaxLoops + slot];
+        const bool frozen = q.pos0 >= kWarmup + 1 || froze;
+        Q8WriteArgs wa{};
+        wa.ksrc = h->kstage; wa.kld = h->KV; wa.vsrc = h->qkvg + h->Q + h->KV; wa.vld = ld;
+        wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = slot; wa.nk = h->nk; wa.hd = h->hd;
+        wa.rec = h->rec;
+        if (frozen) {
+            wa.r0 = 0; wa.r1 = T; wa.field = 1;
+            LAUNCH(launch_q8_write(wa, q.s));
+        } else if (q.pos0 + T <= kWarmup) {
+            wa.r0 = 0; wa.r1 = T; wa.field = 0;
+            LAUNCH(launch_q8_write(wa, q.s));
+        } else {
+            const int split = (int)(kWarmup - q.pos0);
+            wa.r0 = 0; wa.r1 = split; wa.field = 0;
+            LAUNCH(launch_q8_write(wa, q.s));
+            LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, q.s));
+            wa.r0 = split; wa.r1 = T; wa.field = 1;
+            LAUNCH(launch_q8_write(wa, q.s));
+            froze = 1;
+        }
+        field = q.pos0 >= kWarmup + 1 || froze;
+    }
+    AttnArgs aa{};
+    aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part; aa.cnt = h->cnt;
+    aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l.ord; aa.slot = slot;
+    aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
+    aa.window = l.sliding ? h->win_s : h->win_f;
+    aa.split = T == 1 ? h->split_dec : h->split_pf;
+    aa.max_split = T == 1 ? h->ms_dec : h->ms_pf;
+    aa.q8 = h->q8; aa.field = field; aa.rec = h->rec;
+    LAUNCH(launch_attn(aa, T, q.s));
+    if (T == 1) {
+        GemvArgs a{};
+        a.w[0] = w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.row = 0;
+        a.src = h->z; a.y = h->o; a.rec = h->rec; a.hidden = h->H;
+        LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
+    } else {
+        LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->Q, T, q.s));
+        LAUNCH(launch_gemm(h->wt, h->zn, h->Q, w.wo, h->H, h->Q, h->o, h->H, T, q.s));
+    }
+    return DORY_OK;
+}
+
+int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x) {
+    dory_t *h = q.h;
+    const int T = q.T;
+    const dory_layer_weights &w = l.w;
+    if (T == 1) {
+        GemvArgs a{};
+        a.w[0] = w.wgate; a.w[1] = w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H; a.row = 0;
+        a.rs = rs; a.y = h->ga; a.sg = w.sg; a.su = w.su; a.rec = h->rec; a.hidden = h->H;
+        LAUNCH(launch_gemv(h->wt, kProResolve, kEpiPair, a, q.s));
+        GemvArgs d{};
+        d.w[0] = w.wdown; d.seg_end[0] = h->H; d.nseg = 1; d.N = h->H; d.K = h->F; d.row = 0;
+        d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
+        LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
+    } else {
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wgate, h->F, h->H, h->ga, h->F, T, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wup, h->F, h->H, h->gb, h->F, T, q.s));
+        LAUNCH(launch_swiglu_norm(h->ga, h->gb, w.sg, w.su, h->un, h->F, T, q.s));
+        LAUNCH(launch_gemm(h->wt, h->un, h->F, w.wdown, h->H, h->F, h->o, h->H, T, q.s));
+    }
+    return DORY_OK;
+}
+
+// dory.rs `stack` and `head`: embedding, input block, `loops` passes of the
+// recurrent block with the loop mix, output block, head.  Sub-layer pass k
+// reads its x from hb[k % 2]; the step between passes k-1 and k (slerp, loop
+// mix) is fused into pass k's first kernel for one-row calls and is its own
+// row kernel otherwise.
+int enqueue(Enq &q) {
+    dory_t *h = q.h;
+    const dory_config &c = h->cfg;
+    const int T = q.T;
+    LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], q.s));
+    const int P = passes(h, q.loops);
+    int prev_li = -1;
+    for (int k = 0; k < P; ++k) {
+        int li, loop_i = 0, op = kLoopNone;
+        if (k < c.n_in) {
+            li = k;
+        } else if (k < c.n_in + c.n_rec * q.loops) {
+            const int j = (k - c.n_in) % c.n_rec;
+            loop_i = (k - c.n_in) / c.n_rec;
+            li = c.n_in + j;
+            if (j == 0) op = loop_i == 0 ? kLoopEnter : kLoopNext;
+        } else {
+            const int j = k - c.n_in - c.n_rec * q.loops;
+            li = c.n_in + c.n_rec + j;
+            if (j == 0) op = kLoopExit;
+        }
+        Resolve rs{};
+        rs.inp = h->inp;
+        rs.loop_op = op;
+        if (k == 0) {
+            rs.h = h->hb[0]; rs.slerp = 0; rs.h_out = nullptr; rs.tap_pass = -1;
+        } else {
+            rs.h = h->hb[(k - 1) % 2]; rs.o = h->o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
+            rs.h_out = h->hb[k % 2]; rs.tap_pass = k - 1;
+            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, T, h->rec, q.s));
+        }
+        const LayerInfo &l = h->L[li];
+        const float *x = h->hb[k % 2];
+        int rc = l.attn ? enq_attn(q, l, loop_i, rs, x) : enq_mlp(q, l, rs, x);
+        if (rc) return rc;
+        prev_li = li;
+    }
+    Resolve rf{};
+    rf.h = h->hb[(P - 1) % 2]; rf.o = h->o; rf.alpha = h->L[prev_li].w.alpha; rf.slerp = 1;
+    rf.loop_op = kLoopNone; rf.inp = h->inp; rf.tap_pass = P - 1;
+    GemvArgs a{};
+    a.w[0] = h->w.head; a.seg_end[0] = h->V; a.nseg = 1; a.N = h->V; a.K = h->H;
+    a.logit_scale = h->w.logit_scale; a.rec = h->rec; a.hidden = h->H;
+    if (T == 1) {
+        rf.h_out = nullptr;
+        a.row = 0; a.rs = rf;
+        LAUNCH(launch_gemv(h->wt, kProResolve, kEpiHead, a, q.s));
+    } else {
+        rf.h_out = h->hb[P % 2];
+        LAUNCH(launch_resolve_rows(rf, h->H, T, h->rec, q.s));
+        if (q.want_logits) {
+            a.row = T - 1; a.src = h->hb[P % 2];
+            LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));
+        }
+    }
+    return DORY_OK;
+}
+
+// Copies a call record to the device on stream s (pinned staging ring).
+int put_record(dory_t *h, int seq, int64_t pos0, int n, const int32_t *tokens, float *logits, hipStream_t s) {
+    const int i = h->stage_i;
+    h->stage_i = (i + 1) % kStages;
+    if (h->stage_used[i]) HIPCHECK(h, hipEventSynchronize(h->stage_ev[i]));
+    CallRec *r = reinterpret_cast<CallRec *>(h->stage + (size_t)i * h->rec_sz);
+    r->pos0 = pos0;
+    r->n = n;
+    r->seq = seq;
+    r->logits = logits;
+    r->tap = h->tap;
+    if (tokens) memcpy(r->tokens, tokens, sizeof(int32_t) * n);
+    HIPCHECK(h, hipMemcpyAsync(h->rec, r, h->rec_sz, hipMemcpyHostToDevice, s));
+    HIPCHECK(h, hipEventRecord(h->stage_ev[i], s));
+    h->stage_used[i] = true;
+    return DORY_OK;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+
+extern "C" {
+
+int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
+    if (out) *out = nullptr;
+    int rc = check_config(cfg, w);
+    if (rc) return rc;
+    if (!out) return fail(nullptr, DORY_EINVAL, "dory_create: null out");
+    dory_t *h = new dory();
+    h->cfg = *cfg;
+    h->pattern = cfg->layer_pattern;
+    h->cfg.layer_pattern = h->pattern.c_str();
+    const int nl = (int)h->pattern.size();
+    h->wl.assign(w->layers, w->layers + nl);
+    h->w = *w;
+    h->w.layers = h->wl.data();
+    h->H = cfg->hidden; h->F = cfg->ffn; h->V = cfg->vocab; h->nh = cfg->nh; h->nk = cfg->nk; h->hd = cfg->hd;
+    h->Q = h->nh * h->hd; h->KV = h->nk * h->hd; h->ngk = (h->hd + kKGroup - 1) / kKGroup;
+    h->wt = cfg->weight_dtype == DORY_W_BF16 ? kBF16 : kF32;
+    h->q8 = cfg->kv_encoding == DORY_KV_Q8_2F;
+    for (int li = 0; li < nl; ++li) {
+        LayerInfo l;
+        const char ch = h->pattern[li];
+        l.attn = ch != '-';
+        l.sliding = ch == 'S';
+        l.rec = li >= cfg->n_in && li < cfg->n_in + cfg->n_rec;
+        l.ord = l.attn ? h->n_ord++ : -1;
+        l.w = h->wl[li];
+        h->L.push_back(l);
+    }
+    // Rings: a call of up to max_chunk rows must not overwrite a key any of its
+    // rows still reads, so a window of W keys needs W + max_chunk - 1 rows.
+    const int chunk = cfg->max_chunk;
+    h->win_s = cfg->window;
+    h->win_f = cfg->full_window > 0 ? cfg->full_window : kHuge;
+    h->cap_s = std::min<int64_t>(cfg->max_ctx, round_up(std::max(cfg->window + chunk - 1, 128), 64));
+    h->cap_f = cfg->full_window > 0
+                   ? (int)std::min<int64_t>(cfg->max_ctx, round_up(std::max(cfg->full_window + chunk - 1, 128), 64))
+                   : cfg->max_ctx;
+    const int64_t wmax = std::min<int64_t>(std::max<int64_t>(h->win_s, std::min<int64_t>(h->win_f, cfg->max_ctx)),
+                                           cfg->max_ctx);
+    h->split_dec = 64;
+    while ((wmax + h->split_dec - 1) / h->split_dec > 1024 && h->split_dec < 256) h->split_dec *= 2;
+    h->split_pf = 256;
+    h->ms_dec = (int)((wmax + h->split_dec - 1) / h->split_dec);
+    h->ms_pf = (int)((wmax + h->split_pf - 1) / h->split_pf);
+    if (h->ms_dec > 1024 || h->ms_pf > 1024) {
+        delete h;
+        return fail(nullptr, DORY_EINVAL, "dory_create: attention window too long (more than 262144 keys)");
+    }
+    h->seqs.resize(cfg->max_seqs);
+    h->tab_host.assign((size_t)cfg->max_seqs * std::max(h->n_ord, 1) * kMaxLoops, SlotDesc{});
+    h->rec_sz = rec_bytes(chunk);
+
+    auto bail = [&](int code) {
+        g_create_error = h->err;
+        free_all(h);
+        delete h;
+        return code;
+    };
+#define CREATE_CHECK(call)                                          \
+    do {                                                            \
+        hipError_t e_ = (call);                                     \
+        if (e_ != hipSuccess) return bail(hip_fail(h, e_, #call));  \
+    } while (0)
+    CREATE_CHECK(hipGetDevice(&h->device));
+    const size_t TH = (size_t)chunk * h->H;
+    CREATE_CHECK(dmalloc(h, &h->hb[0], TH));
+    CREATE_CHECK(dmalloc(h, &h->hb[1], TH));
+    CREATE_CHECK(dmalloc(h, &h->inp, TH));
+    CREATE_CHECK(dmalloc(h, &h->o, TH));
+    CREATE_CHECK(dmalloc(h, &h->qkvg, (size_t)chunk * (2 * h->Q + 2 * h->KV)));
+    CREATE_CHECK(dmalloc(h, &h->qp, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->z, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->zn, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->ga, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->gb, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->un, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
+    CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));
+    CREATE_CHECK(dmalloc(h, &h->ld_v, (size_t)chunk * h->KV));
+    const size_t rep = h->nh / h->nk;
+    const size_t part = std::max((size_t)h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2);
+    CREATE_CHECK(dmalloc(h, &h->part, part));
+    CREATE_CHECK(dmalloc(h, &h->cnt, (size_t)chunk * h->nk));
+    CREATE_CHECK(hipMemset(h->cnt, 0, sizeof(int32_t) * chunk * h->nk));
+    CREATE_CHECK(dmalloc(h, &h->tab, h->tab_host.size()));
+    CREATE_CHECK(hipMemset(h->tab, 0, sizeof(SlotDesc) * h->tab_host.size()));
+    char *recp = nullptr;
+    CREATE_CHECK(dmalloc(h, &recp, h->rec_sz));
+    h->rec = reinterpret_cast<CallRec *>(recp);
+    // RoPE inverse frequencies theta^(-2j/hd), computed in double, kept as fp32.
+    std::vector<float> inv(h->hd / 2);
+    CREATE_CHECK(dmalloc(h, &h->inv_s, inv.size()));
+    CREATE_CHECK(dmalloc(h, &h->inv_f, inv.size()));
+    for (int j = 0; j < h->hd / 2; ++j) inv[j] = (float)std::pow(cfg->rope_theta_sliding, -2.0 * j / h->hd);
+    CREATE_CHECK(hipMemcpy(h->inv_s, inv.data(), sizeof(float) * inv.size(), hipMemcpyHostToDevice));
+    for (int j = 0; j < h->hd / 2; ++j) inv[j] = (float)std::pow(cfg->rope_theta_full, -2.0 * j / h->hd);
+    CREATE_CHECK(hipMemcpy(h->inv_f, inv.data(), sizeof(float) * inv.size(), hipMemcpyHostToDevice));
+    CREATE_CHECK(hipHostMalloc((void **)&h->stage, h->rec_sz * kStages, hipHostMallocDefault));
+    for (int i = 0; i < kStages; ++i) CREATE_CHECK(hipEventCreateWithFlags(&h->stage_ev[i], hipEventDisableTiming));
+    CREATE_CHECK(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+    // Every sequence's slot 0 of every attention layer; per_loop's further
+    // slots come on the first per_loop call that needs them.
+    for (int s = 0; s < cfg->max_seqs; ++s)
+        for (const LayerInfo &l : h->L)
+            if (l.attn && alloc_slot(h, s, l.ord, 0, l.sliding)) return bail(DORY_ENOMEM);
+#undef CREATE_CHECK
+    *out = h;
+    return DORY_OK;
+}
+
+void dory_destroy(dory_t *h) {
+    if (!h) return;
+    (void)hipSetDevice(h->device);
+    (void)hipDeviceSynchronize();
+    free_all(h);
+    delete h;
+}
+
+const char *dory_last_error(const dory_t *h) { return h ? h->err.c_str() : g_create_error.c_str(); }
+
+int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
+                       dory_stream_t stream, float *logits) {
+    if (!h) return DORY_EINVAL;
+    const dory_config &c = h->cfg;
+    if (seq < 0 || seq >= c.max_seqs) return fail(h, DORY_EINVAL, "dory_forward_chunk: seq out of range");
+    if (!tokens || n < 1) return fail(h, DORY_EINVAL, "dory_forward_chunk: need n >= 1 tokens");
+    if (n > c.max_chunk) return fail(h, DORY_ERANGE, "dory_forward_chunk: n > max_chunk");
+    if (loops < 1 || loops > DORY_MAX_LOOPS)
+        return fail(h, DORY_EINVAL, "dory_forward_chunk: loops must be in 1..16, got " + std::to_string(loops));
+    if (kv_mode != DORY_PER_LOOP && kv_mode != DORY_LAST_LOOP)
+        return fail(h, DORY_EINVAL, "dory_forward_chunk: kv_mode must be per_loop or last_loop");
+    SeqState &st = h->seqs[seq];
+    if (st.mode >= 0 && st.mode != kv_mode)
+        return fail(h, DORY_ESTATE, "dory_forward_chunk: kv mode changed without dory_kv_reset");
+    if (kv_mode == DORY_PER_LOOP && st.loops > 0 && st.loops != loops)
+        return fail(h, DORY_ESTATE, "dory_forward_chunk: per_loop needs the same loop count on every call");
+    if (st.pos + n > c.max_ctx) return fail(h, DORY_ERANGE, "dory_forward_chunk: position past max_ctx");
+    if (h->tap && (int64_t)passes(h, loops) * n * h->H > h->tap_cap)
+        return fail(h, DORY_EINVAL, "dory_forward_chunk: the tap buffer is too small for this call");
+    HIPCHECK(h, hipSetDevice(h->device));
+    int rc = ensure_slots(h, seq, kv_mode, loops);
+    if (rc) return rc;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    rc = put_record(h, seq, st.pos, n, tokens, logits, s);
+    if (rc) return rc;
+    Enq q{h, s, n, loops, kv_mode, st.pos, logits != nullptr, std::vector<uint8_t>((size_t)h->n_ord * kMaxLoops, 0)};
+    const bool graphable = n == 1 && (!h->q8 || st.pos >= kWarmup + 1);
+    if (graphable) {
+        auto key = std::make_tuple(loops, kv_mode);
+        auto it = h->graphs.find(key);
+        if (it == h->graphs.end()) {
+            Enq cq = q;
+            cq.s = h->cap_stream;
+            HIPCHECK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+            rc = enqueue(cq);
+            hipGraph_t g = nullptr;
+            hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
+            if (rc) {
+                if (g) (void)hipGraphDestroy(g);
+                return rc;
+            }
+            if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
+            hipGraphExec_t ex = nullptr;
+            e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+            (void)hipGraphDestroy(g);
+            if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
+            it = h->graphs.emplace(key, ex).first;
+        }
+        HIPCHECK(h, hipGraphLaunch(it->second, s));
+    } else {
+        rc = enqueue(q);
+        if (rc) return rc;
+    }
+    st.pos += n;
+    st.mode = kv_mode;
+    if (kv_mode == DORY_PER_LOOP) st.loops = loops;
+    if (n == 1 && seq == 0) {
+        h->last_loops = loops;
+        h->last_mode = kv_mode;
+    }
+    return DORY_OK;
+}
+
+int dory_kv_reset(dory_t *h, int32_t seq) {
+    if (!h) return DORY_EINVAL;
+    if (seq < -1 || seq >= h->cfg.max_seqs) return fail(h, DORY_EINVAL, "dory_kv_reset: seq out of range");
+    for (int s = 0; s < h->cfg.max_seqs; ++s)
+        if (seq < 0 || s == seq) h->seqs[s] = SeqState{};
+    return DORY_OK;
+}
+
+int64_t dory_position(const dory_t *h, int32_t seq) {
+    if (!h || seq < 0 || seq >= h->cfg.max_seqs) return DORY_EINVAL;
+    return h->seqs[seq].pos;
+}
+
+int dory_debug_tap(dory_t *h, float *buf, int64_t cap) {
+    if (!h) return DORY_EINVAL;
+    if (buf && cap <= 0) return fail(h, DORY_EINVAL, "dory_debug_tap: cap must be positive");
+    h->tap = buf;
+    h->tap_cap = buf ? cap : 0;
+    return DORY_OK;
+}
+
+static int slot_check(dory_t *h, int32_t seq, int32_t ord, int32_t slot, const SlotDesc **out) {
+    if (!h) return DORY_EINVAL;
+    if (seq < 0 || seq >= h->cfg.max_seqs || ord < 0 || ord >= h->n_ord || slot < 0 || slot >= kMaxLoops)
+        return fail(h, DORY_EINVAL, "kv tap: seq, ordinal or slot out of range");
+    const SlotDesc &d = h->tab_host[(seq * h->n_ord + ord) * kMaxLoops + slot];
+    if (!d.k && !d.kc) return fail(h, DORY_EINVAL, "kv tap: slot not in use");
+    *out = &d;
+    return DORY_OK;
+}
+
+int dory_kv_read(dory_t *h, int32_t seq, int32_t ord, int32_t slot, int64_t pos, void *host_out) {
+    const SlotDesc *d = nullptr;
+    int rc = slot_check(h, seq, ord, slot, &d);
+    if (rc) return rc;
+    if (!host_out) return fail(h, DORY_EINVAL, "dory_kv_read: null output");
+    const int64_t held = h->seqs[seq].pos;
+    if (pos < 0 || pos >= held || pos < held - d->cap) return fail(h, DORY_ERANGE, "dory_kv_read: row not held");
+    HIPCHECK(h, hipSetDevice(h->device));
+    HIPCHECK(h, hipDeviceSynchronize());
+    const size_t row = (size_t)(pos % d->cap);
+    char *b = reinterpret_cast<char *>(host_out);
+    const int hd = h->hd, nk = h->nk, ngk = h->ngk;
+    for (int kh = 0; kh < nk; ++kh) {
+        const size_t r = (size_t)kh * d->cap + row;
+        if (!h->q8) {
+            HIPCHECK(h, hipMemcpy(b + sizeof(float) * kh * hd, d->k + r * hd, sizeof(float) * hd, hipMemcpyDeviceToHost));
+            HIPCHECK(h, hipMemcpy(b + sizeof(float) * (nk + kh) * hd, d->v + r * hd, sizeof(float) * hd,
+                                  hipMemcpyDeviceToHost));
+        } else {
+            HIPCHECK(h, hipMemcpy(b + kh * hd, d->kc + r * hd, hd, hipMemcpyDeviceToHost));
+            HIPCHECK(h, hipMemcpy(b + (nk + kh) * hd, d->vc + r * hd, hd, hipMemcpyDeviceToHost));
+            HIPCHECK(h, hipMemcpy(b + 2 * nk * hd + sizeof(float) * kh * ngk, d->ks + r * ngk, sizeof(float) * ngk,
+                                  hipMemcpyDeviceToHost));
+            HIPCHECK(h, hipMemcpy(b + 2 * nk * hd + sizeof(float) * (nk * ngk + kh), d->vs + r, sizeof(float),
+                                  hipMemcpyDeviceToHost));
+        }
+    }
+    return DORY_OK;
+}
+
+int dory_kv_field(dory_t *h, int32_t seq, int32_t ord, int32_t slot, float *kcol, float *vcol) {
+    const SlotDesc *d = nullptr;
+    int rc = slot_check(h, seq, ord, slot, &d);
+    if (rc) return rc;
+    if (!h->q8) return fail(h, DORY_EINVAL, "dory_kv_field: the cache is not q8_2f");
+    const bool frozen = h->seqs[seq].pos >= kWarmup + 1;
+    if (!frozen) return 0;
+    HIPCHECK(h, hipSetDevice(h->device));
+    HIPCHECK(h, hipDeviceSynchronize());
+    if (kcol) HIPCHECK(h, hipMemcpy(kcol, d->kcol, sizeof(float) * h->KV, hipMemcpyDeviceToHost));
+    if (vcol) HIPCHECK(h, hipMemcpy(vcol, d->vcol, sizeof(float) * h->KV, hipMemcpyDeviceToHost));
+    return 1;
+}
+
+int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t npos, int32_t n_slot,
+                 const float *k, const float *v) {
+    if (!h) return DORY_EINVAL;
+    if (seq < 0 || seq >= h->cfg.max_seqs) return fail(h, DORY_EINVAL, "dory_kv_load: seq out of range");
+    if (kv_mode != DORY_PER_LOOP && kv_mode != DORY_LAST_LOOP) return fail(h, DORY_EINVAL, "dory_kv_load: kv_mode");
+    if (loops < 1 || loops > DORY_MAX_LOOPS) return fail(h, DORY_EINVAL, "dory_kv_load: loops must be in 1..16");
+    if (!k || !v || npos < 0 || npos > h->cfg.max_ctx || n_slot < 1 || n_slot > kMaxLoops)
+        return fail(h, DORY_EINVAL, "dory_kv_load: bad rows");
+    if (n_slot < (kv_mode == DORY_PER_LOOP ? loops : 1))
+        return fail(h, DORY_EINVAL, "dory_kv_load: n_slot below the slots the mode uses");
+    if (h->seqs[seq].pos != 0) return fail(h, DORY_ESTATE, "dory_kv_load: the sequence is not fresh");
+    HIPCHECK(h, hipSetDevice(h->device));
+    int rc = ensure_slots(h, seq, kv_mode, loops);
+    if (rc) return rc;
+    HIPCHECK(h, hipDeviceSynchronize());
+    const int chunk = std::min(h->cfg.max_chunk, std::min(h->cap_s, h->cap_f));
+    const size_t row = h->KV;
+    for (const LayerInfo &l : h->L) {
+        if (!l.attn) continue;
+        const int ns = (kv_mode == DORY_PER_LOOP && l.rec) ? loops : 1;
+        for (int s = 0; s < ns; ++s) {
+            const float *kb = k + ((size_t)(l.ord * n_slot + s) * npos) * row;
+            const float *vb = v + ((size_t)(l.ord * n_slot + s) * npos) * row;
+            bool froze = false;
+            for (int64_t p0 = 0; p0 < npos; p0 += chunk) {
+                const int T = (int)std::min<int64_t>(chunk, npos - p0);
+                rc = put_record(h, seq, p0, T, nullptr, nullptr, nullptr);
+                if (rc) return rc;
+                HIPCHECK(h, hipMemcpy(h->ld_k, kb + p0 * row, sizeof(float) * T * row, hipMemcpyHostToDevice));
+                HIPCHECK(h, hipMemcpy(h->ld_v, vb + p0 * row, sizeof(float) * T * row, hipMemcpyHostToDevice));
+                if (!h->q8) {
+                    HIPCHECK(h, launch_kv_store(h->ld_k, h->ld_v, h->tab, h->n_ord, l.ord, s, h->nk, h->hd, T,
+                                                h->rec, nullptr));
+                } else {
+                    Q8WriteArgs wa{};
+                    wa.ksrc = h->ld_k; wa.kld = h->KV; wa.vsrc = h->ld_v; wa.vld = h->KV;
+                    wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = s; wa.nk = h->nk; wa.hd = h->hd;
+                    wa.rec = h->rec;
+                    const bool frozen = froze || p0 >= kWarmup + 1;
+                    if (frozen || p0 + T <= kWarmup) {
+                        wa.r0 = 0; wa.r1 = T; wa.field = frozen;
+                        HIPCHECK(h, launch_q8_write(wa, nullptr));
+                    } else {
+                        const int split = (int)(kWarmup - p0);
+                        wa.r0 = 0; wa.r1 = split; wa.field = 0;
+                        HIPCHECK(h, launch_q8_write(wa, nullptr));
+                        HIPCHECK(h, launch_q8_freeze(h->tab, h->n_ord, l.ord, s, h->nk, h->hd, h->rec, nullptr));
+                        wa.r0 = split; wa.r1 = T; wa.field = 1;
+                        HIPCHECK(h, launch_q8_write(wa, nullptr));
+                        froze = true;
+                    }
+                }
+                HIPCHECK(h, hipDeviceSynchronize());
+            }
+        }
+    }
+    SeqState &st = h->seqs[seq];
+    st.pos = npos;
+    st.mode = kv_mode;
+    st.loops = kv_mode == DORY_PER_LOOP ? loops : 0;
+    return DORY_OK;
+}
+
+int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t stream) {
+    if (!h) return DORY_EINVAL;
+    if (stage < 0 || stage > 5 || reps < 1) return fail(h, DORY_EINVAL, "dory_stage_bench: stage 0..5, reps >= 1");
+    if (h->last_loops == 0 || h->seqs[0].pos < 1)
+        return fail(h, DORY_ESTATE, "dory_stage_bench: needs a one-row call on sequence 0 first");
+    HIPCHECK(h, hipSetDevice(h->device));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    std::vector<const LayerInfo *> ls;
+    for (const LayerInfo &l : h->L)
+        if ((stage <= 2) == l.attn) ls.push_back(&l);
+    if (stage == 5) ls.assign(1, nullptr);
+    if (ls.empty()) return fail(h, DORY_EINVAL, "dory_stage_bench: no sub-layer has this stage");
+    const int ld = 2 * h->Q + 2 * h->KV;
+    for (int i = 0; i < reps; ++i) {
+        const LayerInfo *l = ls[i % ls.size()];
+        Resolve rs{};
+        rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 1; rs.loop_op = kLoopNone;
+        rs.inp = h->inp; rs.h_out = nullptr; rs.tap_pass = -1;
+        GemvArgs a{};
+        a.rec = h->rec; a.hidden = h->H; a.row = 0; a.rs = rs;
+        hipError_t e = hipSuccess;
+        if (stage == 0) {
+            a.w[0] = l->w.wq; a.w[1] = l->w.wk; a.w[2] = l->w.wv; a.w[3] = l->w.wg;
+            a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
+            a.nseg = 4; a.N = ld; a.K = h->H; a.y = h->qkvg;
+            e = launch_gemv(h->wt, kProResolve, kEpiStore, a, s);
+        } else if (stage == 1) {
+            AttnArgs aa{};
+            aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = l->w.sg; aa.z = h->z; aa.part = h->part; aa.cnt = h->cnt;
+            aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l->ord;
+            aa.slot = slot_of(h, *l, h->last_mode, h->last_loops - 1);
+            aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
+            aa.window = l->sliding ? h->win_s : h->win_f;
+            aa.split = h->split_dec; aa.max_split = h->ms_dec;
+            aa.q8 = h->q8; aa.field = h->q8 && h->seqs[0].pos >= kWarmup + 1; aa.rec = h->rec;
+            e = launch_attn(aa, 1, s);
+        } else if (stage == 2) {
+            a.w[0] = l->w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.src = h->z; a.y = h->o;
+            e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);
+        } else if (stage == 3) {
+            a.w[0] = l->w.wgate; a.w[1] = l->w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H;
+            a.y = h->ga; a.sg = l->w.sg; a.su = l->w.su;
+            e = launch_gemv(h->wt, kProResolve, kEpiPair, a, s);
+        } else if (stage == 4) {
+            a.w[0] = l->w.wdown; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->F; a.src = h->ga; a.y = h->o;
+            e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);
+        } else {
+            a.w[0] = h->w.head; a.seg_end[0] = h->V; a.nseg = 1; a.N = h->V; a.K = h->H;
+            a.logit_scale = h->w.logit_scale;
+            e = launch_gemv(h->wt, kProResolve, kEpiHead, a, s);
+        }
+        if (e != hipSuccess) return hip_fail(h, e, "dory_stage_bench");
+    }
+    return DORY_OK;
+}
+
+int dory_q8_encode_rows(const float *x, const float *col, int32_t rows, int32_t n, int32_t group, int8_t *codes,
+                        float *scales, dory_stream_t stream) {
+    if (!x || !codes || !scales || rows < 0 || n <= 0 || n > 256 || !(group == kKGroup || group >= n))
+        return fail(nullptr, DORY_EINVAL, "dory_q8_encode_rows: bad arguments (n <= 256, group 32 or >= n)");
+    hipError_t e = launch_q8_encode_rows(x, col, rows, n, group, codes, scales, reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(nullptr, e, "dory_q8_encode_rows");
+    return DORY_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,216 @@
+// gemv.hip -- weight-streaming matrix-vector products for one-row calls (decode).
+//
+// y = W x with W [N][K] row-major in bf16 or fp32 and x, y fp32 (dory.rs
+// `attn_layer` / `mlp_layer` / `head`, the one-row matvec branches).  The work is
+// HBM-bound: every weight byte is read once, so the kernel keeps many 16-byte
+// loads in flight and hides the prologue behind them.
+//
+// Workgroup: 256 threads = 4 waves, ROWS output rows.  The K axis is cut in
+// 512-element chunks (64 lanes x 8 elements = one 16-byte bf16 load per lane),
+// dealt round-robin to the 4 waves; a wave issues the loads of all its chunks
+// for all its rows before the prologue runs, then reduces each row over its 64
+// lanes, and the 4 wave partials are added through LDS.
+//
+// Prologues build x in LDS:
+//   kProResolve: the previous sub-layer's slerp and the loop mix (Resolve);
+//                workgroup 0 also stores the new residual, loop input and tap.
+//   kProNorm:    x = justnorm(src row) (the renorm over Q before O and over F
+//                before down, dory.rs `attn_layer` / `mlp_layer`).
+// Epilogues:
+//   kEpiStore:   y[n] = acc.
+//   kEpiPair:    rows n of Wgate and Wup together: y[n] = silu(a*sg)*(b*su)
+//                (dory.rs `silu_body`).
+//   kEpiHead:    logits[n] = acc * logit_scale[n] into the call record's
+//                pointer (dory.rs `head`); nothing when it is null.
+#include "device.h"
+
+namespace dk {
+
+namespace {
+
+constexpr int ROWS = 4;
+
+template <int WT>
+struct W8;
+
+template <>
+struct W8<kBF16> {
+    uint4 v;
+    __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void load(const void *base, size_t elem) {
+        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + elem);
+    }
+    __device__ __forceinline__ float dot(const float4 &a, const float4 &b) const {
+        float s = bf16lo(v.x) * a.x;
+        s = fmaf(bf16hi(v.x), a.y, s);
+        s = fmaf(bf16lo(v.y), a.z, s);
+        s = fmaf(bf16hi(v.y), a.w, s);
+        s = fmaf(bf16lo(v.z), b.x, s);
+        s = fmaf(bf16hi(v.z), b.y, s);
+        s = fmaf(bf16lo(v.w), b.z, s);
+        s = fmaf(bf16hi(v.w), b.w, s);
+        return s;
+    }
+};
+
+template <>
+struct W8<kF32> {
+    float4 a, b;
+    __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+    __device__ __forceinline__ void load(const void *base, size_t elem) {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
+        a = p[0];
+        b = p[1];
+    }
+    __device__ __forceinline__ float dot(const float4 &x, const float4 &y) const {
+        float s = a.x * x.x;
+        s = fmaf(a.y, x.y, s);
+        s = fmaf(a.z, x.z, s);
+        s = fmaf(a.w, x.w, s);
+        s = fmaf(b.x, y.x, s);
+        s = fmaf(b.y, y.y, s);
+        s = fmaf(b.z, y.z, s);
+        s = fmaf(b.w, y.w, s);
+        return s;
+    }
+};
+
+template <int WT, int PRO, int EPI, int MAXC>
+__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+    extern __shared__ float smem[];
+    constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
+    float *xs = smem;                 // [K]
+    float *red = smem + a.K;          // [8]
+    float *part = red + 8;            // [4][WR]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row0 = blockIdx.x * ROWS;
+    const int K = a.K, N = a.N;
+    const CallRec *rec = a.rec;
+
+    if (EPI == kEpiHead && rec->logits == nullptr) {
+        // No logits wanted: only the tap of the last pass, if any.
+        if (PRO != kProResolve || blockIdx.x != 0 || rec->tap == nullptr) return;
+        resolve_row(a.rs, a.row, K, xs, red, true, rec);
+        return;
+    }
+
+    // Weight rows of this workgroup.
+    const void *base[WR];
+    size_t roff[WR];
+    bool valid[WR];
+    int seg = 0;
+    while (seg + 1 < a.nseg && row0 >= a.seg_end[seg]) ++seg;
+    const int seg0 = seg ? a.seg_end[seg - 1] : 0;
+#pragma unroll
+    for (int j = 0; j < WR; ++j) {
+        const int n = row0 + (j % ROWS);
+        valid[j] = n < N;
+        if (EPI == kEpiPair) {
+            base[j] = a.w[j < ROWS ? 0 : 1];
+            roff[j] = (size_t)n * K;
+        } else {
+            base[j] = a.w[seg];
+            roff[j] = (size_t)(n - seg0) * K;
+        }
+    }
+
+    // Issue every weight load first; the prologue runs while they fly.
+    W8<WT> wv[WR][MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int k0 = (wave + 4 * c) * 512 + lane * 8;
+#pragma unroll
+        for (int j = 0; j < WR; ++j) {
+            if (k0 < K && valid[j]) wv[j][c].load(base[j], roff[j] + k0);
+            else wv[j][c].zero();
+        }
+    }
+
+    if (PRO == kProResolve) {
+        resolve_row(a.rs, a.row, K, xs, red, blockIdx.x == 0, rec);
+    } else {
+        const float *src = a.src + (size_t)a.row * K;
+        float s = 0.f;
+        for (int i = tid; i < K; i += 256) {
+            float v = src[i];
+            xs[i] = v;
+            s += v * v;
+        }
+        if (PRO == kProNorm) {
+            const float f = norm_factor(block_sum(s, red));
+            for (int i = tid; i < K; i += 256) xs[i] *= f;
+        }
+    }
+    __syncthreads();
+
+    float acc[WR];
+#pragma unroll
+    for (int j = 0; j < WR; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        const int k0 = (wave + 4 * c) * 512 + lane * 8;
+        if (k0 < K) {
+            const float4 x0 = *reinterpret_cast<const float4 *>(xs + k0);
+            const float4 x1 = *reinterpret_cast<const float4 *>(xs + k0 + 4);
+#pragma unroll
+            for (int j = 0; j < WR; ++j) acc[j] += wv[j][c].dot(x0, x1);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < WR; ++j) {
+        float v = wave_sum(acc[j]);
+        if (lane == 0) part[wave * WR + j] = v;
+    }
+    __syncthreads();
+    if (tid < ROWS) {
+        const int n = row0 + tid;
+        if (n < N) {
+            float v = part[tid] + part[WR + tid] + part[2 * WR + tid] + part[3 * WR + tid];
+            if (EPI == kEpiStore) {
+                a.y[n] = v;
+            } else if (EPI == kEpiPair) {
+                const int j = ROWS + tid;
+                float b = part[j] + part[WR + j] + part[2 * WR + j] + part[3 * WR + j];
+                float g = v * a.sg[n];
+                a.y[n] = g / (1.0f + expf(-g)) * (b * a.su[n]);
+            } else {
+                rec->logits[n] = v * a.logit_scale[n];
+            }
+        }
+    }
+}
+
+template <int WT, int PRO, int EPI>
+hipError_t launch_c(const GemvArgs &a, hipStream_t s) {
+    const int nch = (a.K + 511) / 512;
+    const int maxc = (nch + 3) / 4;
+    dim3 grid((a.N + ROWS - 1) / ROWS), block(256);
+    const size_t lds = sizeof(float) * (a.K + 8 + 4 * 2 * ROWS);
+    switch (maxc) {
+        case 1: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 1>), grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 2>), grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 3>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 4>), grid, block, lds, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int WT>
+hipError_t launch_w(int pro, int epi, const GemvArgs &a, hipStream_t s) {
+    if (pro == kProResolve && epi == kEpiStore) return launch_c<WT, kProResolve, kEpiStore>(a, s);
+    if (pro == kProNorm && epi == kEpiStore) return launch_c<WT, kProNorm, kEpiStore>(a, s);
+    if (pro == kProResolve && epi == kEpiPair) return launch_c<WT, kProResolve, kEpiPair>(a, s);
+    if (pro == kProResolve && epi == kEpiHead) return launch_c<WT, kProResolve, kEpiHead>(a, s);
+    if (pro == kProPlain && epi == kEpiHead) return launch_c<WT, kProPlain, kEpiHead>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemv(int wtype, int pro, int epi, const GemvArgs &a, hipStream_t s) {
+    if (a.K <= 0 || a.K > 8192 || a.K % 8 || a.N <= 0) return hipErrorInvalidValue;
+    return wtype == kBF16 ? launch_w<kBF16>(pro, epi, a, s) : launch_w<kF32>(pro, epi, a, s);
+}
+
+}  // namespace dk

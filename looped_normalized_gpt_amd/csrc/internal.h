@@ -1,0 +1,153 @@
+// internal.h -- types shared by the host runtime and the gfx950 kernels of
+// libdory.so.  Nothing here is part of the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dk {
+
+constexpr int kMaxLoops = 16;
+constexpr int kWarmup = 64;     // kv_cache.rs `KV_COL_WARMUP`: rows before the q8 field freezes
+constexpr int kKGroup = 32;     // kv_cache.rs `KV_K_GROUP`: K channels per q8 scale
+constexpr float kEps = 1e-6f;   // dory.rs `EPS`: justnorm's epsilon
+
+// The per-call record: written by the host into pinned memory and copied to the
+// device ahead of the call's kernels, so a captured graph replays unchanged.
+struct CallRec {
+    int64_t pos0;      // position of row 0
+    int32_t n;         // rows
+    int32_t seq;       // sequence index (selects the cache slots)
+    float *logits;     // device [vocab] or null
+    float *tap;        // device [passes][n][hidden] or null
+    int32_t tokens[1]; // [max_chunk]
+};
+inline size_t rec_bytes(int max_chunk) { return sizeof(CallRec) + sizeof(int32_t) * (max_chunk - 1); }
+
+// One cache slot (attention ordinal x loop slot) of one sequence.  Rings are
+// head-major: K, V [nk][cap][hd]; position p sits at ring row p % cap.
+struct SlotDesc {
+    float *k, *v;          // fp32 cache
+    int8_t *kc, *vc;       // q8 codes [nk][cap][hd]
+    float *ks;             // q8 K scales [nk][cap][ngk]
+    float *vs;             // q8 V scales [nk][cap]
+    float *kcol, *vcol;    // q8 fields [nk][hd]
+    int32_t cap;
+    int32_t pad;
+};
+
+// Slot table on the device: [max_seqs][n_ord][kMaxLoops].
+inline __host__ __device__ const SlotDesc &slot_at(const SlotDesc *tab, int seq, int n_ord, int ord, int slot) {
+    return tab[(seq * n_ord + ord) * kMaxLoops + slot];
+}
+
+// How the x fed to a sub-layer is obtained from the previous sub-layer's result.
+// e = slerp(h, o, alpha) (or e = h for the very first pass); then
+//   kLoopNone:  x = e
+//   kLoopEnter: input = e; state = e; x = norm(state + input)      (first loop)
+//   kLoopNext:  state = norm(e); x = norm(state + input)           (later loops)
+//   kLoopExit:  state = norm(e); x = state                          (after the loops)
+enum LoopOp { kLoopNone = 0, kLoopEnter = 1, kLoopNext = 2, kLoopExit = 3 };
+
+struct Resolve {
+    const float *h;      // residual before the previous sub-layer [T][H]
+    const float *o;      // previous sub-layer's output [T][H] (slerp only)
+    const float *alpha;  // previous sub-layer's |alpha| [H] (slerp only)
+    float *h_out;        // x for this sub-layer [T][H]
+    float *inp;          // the loop's input [T][H]
+    int32_t slerp;       // 1: e = slerp(h, o, alpha); 0: e = h
+    int32_t loop_op;
+    int32_t tap_pass;    // pass index of e for the tap, or -1
+    int32_t pad;
+};
+
+enum WType { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------- launchers
+// GEMV for one row (decode).  Prologue builds x in LDS, epilogue stores.
+enum GemvPro { kProPlain = 0, kProNorm = 1, kProResolve = 2 };
+enum GemvEpi { kEpiStore = 0, kEpiPair = 1, kEpiHead = 2 };
+
+struct GemvArgs {
+    // weight row pointers by segment: rows [seg_end[i-1], seg_end[i]) read w[i]
+    const void *w[4];
+    int32_t seg_end[4];
+    int32_t nseg;
+    int32_t N;           // output rows (pairs for kEpiPair)
+    int32_t K;
+    int32_t row;         // which row of the [T][K] source feeds x
+    const float *src;    // kProPlain / kProNorm: [T][K]
+    Resolve rs;          // kProResolve
+    float *y;            // output [N] at row offset (kEpiStore, kEpiPair)
+    const float *sg, *su;        // kEpiPair
+    const float *logit_scale;    // kEpiHead
+    const CallRec *rec;
+    int32_t hidden;      // tap row length
+};
+
+hipError_t launch_gemv(int wtype, int pro, int epi, const GemvArgs &a, hipStream_t s);
+
+// Prefill row kernels.
+hipError_t launch_embed(int wtype, const void *embed, int V, int H, const CallRec *rec, int T,
+                        float *h, hipStream_t s);
+hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s);
+hipError_t launch_rownorm(const float *src, int ld_src, float *dst, int N, int T, hipStream_t s);
+hipError_t launch_swiglu_norm(const float *a, const float *b, const float *sg, const float *su,
+                              float *dst, int F, int T, hipStream_t s);
+
+// C[T][ldc] (columns c0..c0+N) = A[T][K] . W[N][K]^T, fp32 accumulation.
+hipError_t launch_gemm(int wtype, const float *A, int lda, const void *W, int N, int K, float *C,
+                       int ldc, int T, hipStream_t s);
+
+// Attention.
+struct PrepArgs {
+    const float *qkvg;   // [T][Q + 2KV + Q]
+    float *qp;           // [T][Q] rotated, normed, scaled queries
+    float *kstage;       // [T][KV] rotated, normed keys (q8 cache) or null (fp32 cache: ring)
+    const float *inv;    // [hd/2] RoPE inverse frequencies of the layer's kind
+    const float *sq;     // [Q]
+    const SlotDesc *tab;
+    int32_t n_ord, ord, slot;
+    int32_t nh, nk, hd;
+    const CallRec *rec;
+};
+hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s);
+
+struct AttnArgs {
+    const float *qp;     // [T][Q]
+    const float *qkvg;   // gate g at column Q + 2KV
+    const float *sg;     // [Q]
+    float *z;            // [T][Q] gated attention output (before the renorm)
+    float *part;         // split partials
+    int32_t *cnt;        // [T][nk] arrival counters, zero between launches
+    const SlotDesc *tab;
+    int32_t n_ord, ord, slot;
+    int32_t nh, nk, hd;
+    int64_t window;      // keys p-window+1 ..= p (huge for full attention)
+    int32_t split;       // keys per workgroup
+    int32_t max_split;   // grid.x; partial stride
+    int32_t q8;          // cache encoding
+    int32_t field;       // q8: the field is frozen (apply kcol / vcol)
+    const CallRec *rec;
+};
+hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
+
+// q8_2f cache writes (kv_cache.rs `append` / `freeze_cols`).
+struct Q8WriteArgs {
+    const float *ksrc; int32_t kld;   // rotated normed keys [T][..], kv head kh at kh*hd
+    const float *vsrc; int32_t vld;   // values
+    const SlotDesc *tab;
+    int32_t n_ord, ord, slot, nk, hd;
+    int32_t r0, r1;                   // rows of the call to encode
+    int32_t field;                    // encode against the frozen field
+    const CallRec *rec;
+};
+hipError_t launch_q8_write(const Q8WriteArgs &a, hipStream_t s);
+hipError_t launch_q8_freeze(const SlotDesc *tab, int n_ord, int ord, int slot, int nk, int hd,
+                            const CallRec *rec, hipStream_t s);
+hipError_t launch_q8_encode_rows(const float *x, const float *col, int rows, int n, int group,
+                                 int8_t *codes, float *scales, hipStream_t s);
+// fp32 rows straight into a ring (cache set-up).
+hipError_t launch_kv_store(const float *k, const float *v, const SlotDesc *tab, int n_ord, int ord,
+                           int slot, int nk, int hd, int T, const CallRec *rec, hipStream_t s);
+
+}  // namespace dk

@@ -1,0 +1,87 @@
+// rows.hip -- per-row kernels of multi-row calls (prefill chunks): embedding
+// gather, the residual step between sub-layers, and the renorms before O and
+// down.  One 256-thread workgroup per row; these are launch-latency work.
+#include "device.h"
+
+namespace dk {
+
+namespace {
+
+// dory.rs `forward_host`: h[r] = E[token r]; an id past the table is a zero row.
+template <int WT>
+__global__ __launch_bounds__(256) void k_embed(const void *E, int V, int H, const CallRec *rec, float *h) {
+    const int r = blockIdx.x;
+    const uint32_t id = (uint32_t)rec->tokens[r];
+    float *out = h + (size_t)r * H;
+    if (id >= (uint32_t)V) {
+        for (int i = threadIdx.x; i < H; i += 256) out[i] = 0.f;
+        return;
+    }
+    if (WT == kBF16) {
+        const uint16_t *e = reinterpret_cast<const uint16_t *>(E) + (size_t)id * H;
+        for (int i = threadIdx.x; i < H; i += 256) out[i] = bf16f(e[i]);
+    } else {
+        const float *e = reinterpret_cast<const float *>(E) + (size_t)id * H;
+        for (int i = threadIdx.x; i < H; i += 256) out[i] = e[i];
+    }
+}
+
+__global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const CallRec *rec) {
+    extern __shared__ float smem[];
+    resolve_row(rs, blockIdx.x, H, smem + 8, smem, true, rec);
+}
+
+// dst[r] = justnorm(src[r]) over N values.
+__global__ __launch_bounds__(256) void k_rownorm(const float *src, int ld, float *dst, int N) {
+    __shared__ float red[8];
+    const float *x = src + (size_t)blockIdx.x * ld;
+    float *y = dst + (size_t)blockIdx.x * N;
+    float s = 0.f;
+    for (int i = threadIdx.x; i < N; i += 256) s += x[i] * x[i];
+    const float f = norm_factor(block_sum(s, red));
+    for (int i = threadIdx.x; i < N; i += 256) y[i] = x[i] * f;
+}
+
+// dory.rs `mlp_layer`: z = silu(a*sg) * (b*su), then justnorm over F.
+__global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float *b, const float *sg,
+                                                     const float *su, float *dst, int F) {
+    extern __shared__ float smem[];
+    float *red = smem, *z = smem + 8;
+    const size_t off = (size_t)blockIdx.x * F;
+    float s = 0.f;
+    for (int i = threadIdx.x; i < F; i += 256) {
+        float g = a[off + i] * sg[i];
+        float v = g / (1.0f + expf(-g)) * (b[off + i] * su[i]);
+        z[i] = v;
+        s += v * v;
+    }
+    const float f = norm_factor(block_sum(s, red));
+    for (int i = threadIdx.x; i < F; i += 256) dst[off + i] = z[i] * f;
+}
+
+}  // namespace
+
+hipError_t launch_embed(int wtype, const void *E, int V, int H, const CallRec *rec, int T, float *h,
+                        hipStream_t s) {
+    if (wtype == kBF16) hipLaunchKernelGGL((k_embed<kBF16>), dim3(T), dim3(256), 0, s, E, V, H, rec, h);
+    else hipLaunchKernelGGL((k_embed<kF32>), dim3(T), dim3(256), 0, s, E, V, H, rec, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s) {
+    hipLaunchKernelGGL(k_resolve_rows, dim3(T), dim3(256), sizeof(float) * (H + 8), s, rs, H, rec);
+    return hipGetLastError();
+}
+
+hipError_t launch_rownorm(const float *src, int ld, float *dst, int N, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_rownorm, dim3(T), dim3(256), 0, s, src, ld, dst, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_norm(const float *a, const float *b, const float *sg, const float *su, float *dst,
+                              int F, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_swiglu_norm, dim3(T), dim3(256), sizeof(float) * (F + 8), s, a, b, sg, su, dst, F);
+    return hipGetLastError();
+}
+
+}  // namespace dk
