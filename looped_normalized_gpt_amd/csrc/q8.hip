@@ -3,9 +3,11 @@
 //
 // The codes, scales and fields must equal, bit for bit, what the page's fp32
 // steps give for the same fp32 rows.  So this file is built with fp contraction
-// off, and every step that rounds is written with an explicitly rounded
-// operation: IEEE division (x/col, absmax/127, r/scale, sum/n), the square root,
-// and the product and sum of the field's sum of squares, taken in row order.
+// off, and every step that rounds is an IEEE correctly rounded operation: the
+// divisions (x/col, absmax/127, r/scale, sum/n), the square root (the compiler's
+// default correctly rounded sqrt; HIP's __fsqrt_rn is the approximate native
+// one unless the OCML rounded operations are enabled), and the product and sum
+// of the field's sum of squares, taken in row order.
 #include "device.h"
 
 namespace dk {
@@ -96,8 +98,8 @@ __global__ __launch_bounds__(256) void k_q8_freeze(const SlotDesc *tab, int n_or
             ck = __fadd_rn(ck, __fmul_rn(dk, dk));
             cv = __fadd_rn(cv, __fmul_rn(dv, dv));
         }
-        ck = fmaxf(__fsqrt_rn(__fdiv_rn(ck, (float)n)), 1e-6f);
-        cv = fmaxf(__fsqrt_rn(__fdiv_rn(cv, (float)n)), 1e-6f);
+        ck = fmaxf(__builtin_sqrtf(__fdiv_rn(ck, (float)n)), 1e-6f);
+        cv = fmaxf(__builtin_sqrtf(__fdiv_rn(cv, (float)n)), 1e-6f);
         kcol[d] = ck;
         vcol[d] = cv;
         sd.kcol[kh * hd + d] = ck;
