@@ -50,13 +50,13 @@ struct dory {
     int n_ord = 0;
     int H = 0, F = 0, V = 0, Q = 0, KV = 0, nh = 0, nk = 0, hd = 0, ngk = 0, wt = 0, q8 = 0;
     int cap_s = 0, cap_f = 0;
-    int split_dec = 64, split_pf = 256, ms_dec = 1, ms_pf = 1;
+    int split_pf = 256, ms_dec = 1, ms_pf = 1;
+    int split_ds = 64, split_df = 64, ms_ds = 1, ms_df = 1;  // one-row calls: sliding, full layers
     int64_t win_s = 0, win_f = 0;
     // device scratch
     float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
     float *z = nullptr, *zn = nullptr, *ga = nullptr, *gb = nullptr, *un = nullptr, *kstage = nullptr;
     float *part = nullptr, *inv_s = nullptr, *inv_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
-    int32_t *cnt = nullptr;
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
     std::vector<SlotDesc> tab_host;
@@ -232,48 +232,60 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         LAUNCH(launch_gemm(h->wt, x, h->H, w.wv, h->KV, h->H, h->qkvg + h->Q + h->KV, ld, T, q.s));
         LAUNCH(launch_gemm(h->wt, x, h->H, w.wg, h->Q, h->H, h->qkvg + h->Q + 2 * h->KV, ld, T, q.s));
     }
-    PrepArgs pa{};
-    pa.qkvg = h->qkvg; pa.qp = h->qp; pa.kstage = h->q8 ? h->kstage : nullptr;
-    pa.inv = l.sliding ? h->inv_s : h->inv_f; pa.sq = w.sq; pa.tab = h->tab;
-    pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = h->rec;
-    LAUNCH(launch_prep(pa, T, q.s));
-    bool field = false;
-    if (h->q8) {
-        // kv_cache.rs `append`: the field freezes when the 65th row (position 64)
-        // is appended; rows before it were encoded without a field, rows after
-        // against it.  A later loop's rewrite of the same rows finds it frozen.
-        uint8_t &froze = q.froze[l.ord * kMaxLoops + slot];
-        const bool frozen = q.pos0 >= kWarmup + 1 || froze;
-        Q8WriteArgs wa{};
-        wa.ksrc = h->kstage; wa.kld = h->KV; wa.vsrc = h->qkvg + h->Q + h->KV; wa.vld = ld;
-        wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = slot; wa.nk = h->nk; wa.hd = h->hd;
-        wa.rec = h->rec;
-        if (frozen) {
-            wa.r0 = 0; wa.r1 = T; wa.field = 1;
-            LAUNCH(launch_q8_write(wa, q.s));
-        } else if (q.pos0 + T <= kWarmup) {
-            wa.r0 = 0; wa.r1 = T; wa.field = 0;
-            LAUNCH(launch_q8_write(wa, q.s));
-        } else {
-            const int split = (int)(kWarmup - q.pos0);
-            wa.r0 = 0; wa.r1 = split; wa.field = 0;
-            LAUNCH(launch_q8_write(wa, q.s));
-            LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, q.s));
-            wa.r0 = split; wa.r1 = T; wa.field = 1;
-            LAUNCH(launch_q8_write(wa, q.s));
-            froze = 1;
-        }
-        field = q.pos0 >= kWarmup + 1 || froze;
-    }
+    const bool freeze_now = h->q8 && q.pos0 <= kWarmup && q.pos0 + T > kWarmup;
     AttnArgs aa{};
-    aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part; aa.cnt = h->cnt;
+    aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part;
     aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l.ord; aa.slot = slot;
     aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
     aa.window = l.sliding ? h->win_s : h->win_f;
-    aa.split = T == 1 ? h->split_dec : h->split_pf;
-    aa.max_split = T == 1 ? h->ms_dec : h->ms_pf;
-    aa.q8 = h->q8; aa.field = field; aa.rec = h->rec;
-    LAUNCH(launch_attn(aa, T, q.s));
+    aa.q8 = h->q8; aa.rec = h->rec;
+    aa.inv = l.sliding ? h->inv_s : h->inv_f; aa.sq = w.sq;
+    if (T == 1 && !freeze_now) {
+        // one row: prep and the cache write are fused into the attention kernel
+        aa.split = l.sliding ? h->split_ds : h->split_df;
+        aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
+        aa.field = h->q8 && q.pos0 >= kWarmup + 1;
+        LAUNCH(launch_attn_dec(aa, q.s));
+    } else {
+        PrepArgs pa{};
+        pa.qkvg = h->qkvg; pa.qp = h->qp; pa.kstage = h->q8 ? h->kstage : nullptr;
+        pa.inv = l.sliding ? h->inv_s : h->inv_f; pa.sq = w.sq; pa.tab = h->tab;
+        pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = h->rec;
+        LAUNCH(launch_prep(pa, T, q.s));
+        bool field = false;
+        if (h->q8) {
+            // kv_cache.rs `append`: the field freezes when the 65th row (position 64)
+            // is appended; rows before it were encoded without a field, rows after
+            // against it.  A later loop's rewrite of the same rows finds it frozen.
+            uint8_t &froze = q.froze[l.ord * kMaxLoops + slot];
+            const bool frozen = q.pos0 >= kWarmup + 1 || froze;
+            Q8WriteArgs wa{};
+            wa.ksrc = h->kstage; wa.kld = h->KV; wa.vsrc = h->qkvg + h->Q + h->KV; wa.vld = ld;
+            wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = slot; wa.nk = h->nk; wa.hd = h->hd;
+            wa.rec = h->rec;
+            if (frozen) {
+                wa.r0 = 0; wa.r1 = T; wa.field = 1;
+                LAUNCH(launch_q8_write(wa, q.s));
+            } else if (q.pos0 + T <= kWarmup) {
+                wa.r0 = 0; wa.r1 = T; wa.field = 0;
+                LAUNCH(launch_q8_write(wa, q.s));
+            } else {
+                const int split = (int)(kWarmup - q.pos0);
+                wa.r0 = 0; wa.r1 = split; wa.field = 0;
+                LAUNCH(launch_q8_write(wa, q.s));
+                LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, q.s));
+                wa.r0 = split; wa.r1 = T; wa.field = 1;
+                LAUNCH(launch_q8_write(wa, q.s));
+                froze = 1;
+            }
+            field = q.pos0 >= kWarmup + 1 || froze;
+        }
+        aa.split = h->split_pf;
+        aa.max_split = h->ms_pf;
+        aa.field = field;
+        LAUNCH(launch_attn(aa, T, q.s));
+
+    }
     if (T == 1) {
         GemvArgs a{};
         a.w[0] = w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.row = 0;
@@ -338,7 +350,10 @@ int enqueue(Enq &q) {
         rs.inp = h->inp;
         rs.loop_op = op;
         if (k == 0) {
-            rs.h = h->hb[0]; rs.slerp = 0; rs.h_out = nullptr; rs.tap_pass = -1;
+            // the first pass takes the embedding as it is; o and alpha only need
+            // to be valid addresses (the GEMV prologue loads them unconditionally)
+            rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0; rs.h_out = nullptr;
+            rs.tap_pass = -1;
         } else {
             rs.h = h->hb[(k - 1) % 2]; rs.o = h->o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
             rs.h_out = h->hb[k % 2]; rs.tap_pass = k - 1;
@@ -433,10 +448,21 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
                    : cfg->max_ctx;
     const int64_t wmax = std::min<int64_t>(std::max<int64_t>(h->win_s, std::min<int64_t>(h->win_f, cfg->max_ctx)),
                                            cfg->max_ctx);
-    h->split_dec = 64;
-    while ((wmax + h->split_dec - 1) / h->split_dec > 1024 && h->split_dec < 256) h->split_dec *= 2;
+    // One-row calls: about 64 workgroups per kv head at the longest window, each
+    // taking a multiple of the keys a workgroup covers per step.
+    const int dmax = attn_dec_max_split(h->hd), kb = 256 / (h->hd / 4);
+    auto pick = [&](int64_t W) {
+        int sp = (int)std::min<int64_t>((W + 63) / 64, dmax);
+        sp = std::max(kb, (sp + kb - 1) / kb * kb);
+        return std::min(sp, dmax);
+    };
+    const int64_t wf = std::min<int64_t>(h->win_f, cfg->max_ctx), ws = std::min<int64_t>(h->win_s, cfg->max_ctx);
+    h->split_ds = pick(ws);
+    h->split_df = pick(wf);
+    h->ms_ds = (int)((ws + h->split_ds - 1) / h->split_ds);
+    h->ms_df = (int)((wf + h->split_df - 1) / h->split_df);
+    h->ms_dec = std::max(h->ms_ds, h->ms_df);
     h->split_pf = 256;
-    h->ms_dec = (int)((wmax + h->split_dec - 1) / h->split_dec);
     h->ms_pf = (int)((wmax + h->split_pf - 1) / h->split_pf);
     if (h->ms_dec > 1024 || h->ms_pf > 1024) {
         delete h;
@@ -476,8 +502,6 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     const size_t rep = h->nh / h->nk;
     const size_t part = std::max((size_t)h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2);
     CREATE_CHECK(dmalloc(h, &h->part, part));
-    CREATE_CHECK(dmalloc(h, &h->cnt, (size_t)chunk * h->nk));
-    CREATE_CHECK(hipMemset(h->cnt, 0, sizeof(int32_t) * chunk * h->nk));
     CREATE_CHECK(dmalloc(h, &h->tab, h->tab_host.size()));
     CREATE_CHECK(hipMemset(h->tab, 0, sizeof(SlotDesc) * h->tab_host.size()));
     char *recp = nullptr;
@@ -743,14 +767,16 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_gemv(h->wt, kProResolve, kEpiStore, a, s);
         } else if (stage == 1) {
             AttnArgs aa{};
-            aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = l->w.sg; aa.z = h->z; aa.part = h->part; aa.cnt = h->cnt;
+            aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = l->w.sg; aa.z = h->z; aa.part = h->part;
             aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l->ord;
             aa.slot = slot_of(h, *l, h->last_mode, h->last_loops - 1);
             aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
             aa.window = l->sliding ? h->win_s : h->win_f;
-            aa.split = h->split_dec; aa.max_split = h->ms_dec;
+            aa.split = l->sliding ? h->split_ds : h->split_df;
+            aa.max_split = l->sliding ? h->ms_ds : h->ms_df;
+            aa.inv = l->sliding ? h->inv_s : h->inv_f; aa.sq = l->w.sq; aa.no_write = 1;
             aa.q8 = h->q8; aa.field = h->q8 && h->seqs[0].pos >= kWarmup + 1; aa.rec = h->rec;
-            e = launch_attn(aa, 1, s);
+            e = launch_attn_dec(aa, s);
         } else if (stage == 2) {
             a.w[0] = l->w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.src = h->z; a.y = h->o;
             e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);

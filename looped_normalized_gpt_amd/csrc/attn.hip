@@ -76,8 +76,46 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
     for (int j = lane; j < hd; j += 64) vd[j] = v[j];
 }
 
-__device__ __forceinline__ float load_agent(const float *p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+// Merges the split partials of (row r, q head h) in log-sum-exp form, scales by
+// the V field (q8), applies the sigmoid gate (dory.rs `gate_body`) and writes z.
+// Grid (T, nh, ceil(hd/64)), 64 threads: thread d of the block owns one channel
+// and reads that channel of every split (coalesced across the block).  A kernel
+// of its own: the partials come from workgroups on other XCDs, whose L2s are
+// only coherent with this one at kernel boundaries.
+template <int Q8>
+__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
+    const int r = blockIdx.x, hq = blockIdx.y, d = blockIdx.z * 64 + threadIdx.x;
+    const int hd = a.hd, rep = a.nh / a.nk, kh = hq / rep, h = hq % rep;
+    const int64_t p = a.rec->pos0 + r;
+    const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+    const int nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
+    const size_t pstride = (size_t)rep * (hd + 2);
+    const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride + (size_t)h * (hd + 2);
+    float M = -INFINITY;
+    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, all[j * pstride]);
+    if (d >= hd) return;
+    float L = 0.f, y0 = 0.f, y1 = 0.f;
+    int j = 0;
+    for (; j + 2 <= nsplit; j += 2) {
+        const float w0 = expf(all[j * pstride] - M), w1 = expf(all[(j + 1) * pstride] - M);
+        L += w0 * all[j * pstride + 1] + w1 * all[(j + 1) * pstride + 1];
+        y0 += w0 * all[j * pstride + 2 + d];
+        y1 += w1 * all[(j + 1) * pstride + 2 + d];
+    }
+    for (; j < nsplit; ++j) {
+        const float w0 = expf(all[j * pstride] - M);
+        L += w0 * all[j * pstride + 1];
+        y0 += w0 * all[j * pstride + 2 + d];
+    }
+    float y = (y0 + y1) / L;
+    if (Q8 && a.field) {
+        const SlotDesc &sd = slot_at(a.tab, a.rec->seq, a.n_ord, a.ord, a.slot);
+        y *= sd.vcol[kh * hd + d];
+    }
+    const int Q = a.nh * hd, ld = 2 * Q + 2 * a.nk * hd;
+    const float g = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + d];
+    a.z[(size_t)r * Q + hq * hd + d] = y / (1.0f + expf(-(g * a.sg[hq * hd + d])));
 }
 
 // Grouped-query attention of one row over keys max(p+1-window, 0) ..= p for the
@@ -88,8 +126,7 @@ __device__ __forceinline__ float load_agent(const float *p) {
 // row r.  It reads each K row once for its REP heads (HD/4 lanes per key, one
 // 16-byte load each), keeps the scores in LDS, takes per-head maxima and sums,
 // then reads each V row once.  It leaves (max, sum, unnormalised sum of
-// p*v) per head; the last workgroup of (r, kh) to arrive merges the splits in
-// log-sum-exp form and applies the sigmoid gate (dory.rs `gate_body`).
+// p*v) per head for k_attn_merge.
 template <int HD, int REP, int Q8>
 __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     constexpr int LPK = HD / 4;       // lanes per key
@@ -100,7 +137,6 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     __shared__ float sc[REP][SLMAX];
     __shared__ float red[G * REP * HD];
     __shared__ float stat[2][REP];
-    __shared__ int last;
     const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const CallRec *rec = a.rec;
@@ -219,47 +255,242 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
         mine[tid * (HD + 2) + 1] = stat[1][tid];
     }
 
-    // ---- the last workgroup of (r, kh) merges the splits
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) last = atomicAdd(&a.cnt[r * a.nk + kh], 1) == nsplit - 1;
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride;
-    float *wts = red;  // [nsplit][REP]
-    if (tid < REP) {
-        float M = -INFINITY;
-        for (int j = 0; j < nsplit; ++j) M = fmaxf(M, load_agent(all + j * pstride + tid * (HD + 2)));
-        float L = 0.f;
-        for (int j = 0; j < nsplit; ++j) {
-            const float w = expf(load_agent(all + j * pstride + tid * (HD + 2)) - M);
-            wts[j * REP + tid] = w;
-            L += w * load_agent(all + j * pstride + tid * (HD + 2) + 1);
+}
+
+
+// Decode attention: one row at position p (the call's only row), kv head kh,
+// keys max(p+1-window, 0) ..= p split across workgroups (dory.rs
+// `attn_layer`; kv_cache.rs `attend_group_upto` for q8_2f rows).  The
+// projections arrive raw: every workgroup rotates and normalises its group's
+// REP query heads itself (cheap, and it saves a kernel per sub-layer), and the
+// workgroup whose split ends at p also rotates and normalises the new key,
+// writes the new row to the cache (encoding it under q8_2f) and uses it from
+// LDS in place of the ring row it prefetched.
+//
+// Each thread owns key slot g = tid / (HD/4) and the 4 channels dq*4.. of it;
+// the workgroup takes KB = 256/(HD/4) keys per step and IT = 8 steps, and every
+// K and V load of the split is issued before any arithmetic.
+template <int HD, int REP, int Q8>
+__global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
+    constexpr int LPK = HD / 4, KB = 256 / LPK, IT = 8;
+    constexpr int SMAX = IT * KB < 256 ? IT * KB : 256;
+    constexpr int NGK = (HD + kKGroup - 1) / kKGroup;
+    constexpr int HALF = HD / 2;
+    __shared__ float sc[REP][SMAX];
+    __shared__ float red[KB * REP * HD];
+    __shared__ float qs[REP + 1][HD];  // the group's query heads, then the new key
+    __shared__ float vn[HD];
+    __shared__ float rot[2][HALF];
+    __shared__ int8_t kcn[HD], vcn[HD];
+    __shared__ float ksn[NGK], vsn[1];
+    __shared__ float stat[2][REP];
+    const int s = blockIdx.x, kh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const CallRec *rec = a.rec;
+    const int64_t p = rec->pos0;
+    const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+    const int64_t nkeys = p - lo + 1;
+    const int nsplit = (int)((nkeys + a.split - 1) / a.split);
+    if (s >= nsplit) return;
+    const int64_t e0 = lo + (int64_t)s * a.split;
+    const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
+    const bool tail = s == nsplit - 1;
+    const SlotDesc &sd = slot_at(a.tab, rec->seq, a.n_ord, a.ord, a.slot);
+    const int cap = sd.cap;
+    const int Q = a.nh * HD, KV = a.nk * HD;
+    const int g = tid / LPK, dq = tid % LPK;
+    const float scale = 1.0f / sqrtf((float)HD);
+
+    // ---- 1. every K and V row of the split, in flight at once
+    const int rbase = (int)(e0 % cap);
+    float4 kr[IT], vr[IT];
+    float ksr[IT], vsr[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = g + KB * it;
+        int rr = rbase + (e < len ? e : 0);
+        if (rr >= cap) rr -= cap;
+        const size_t row = (size_t)kh * cap + rr;
+        if (Q8) {
+            const char4 kc = *reinterpret_cast<const char4 *>(sd.kc + row * HD + dq * 4);
+            const char4 vc = *reinterpret_cast<const char4 *>(sd.vc + row * HD + dq * 4);
+            kr[it] = make_float4((float)kc.x, (float)kc.y, (float)kc.z, (float)kc.w);
+            vr[it] = make_float4((float)vc.x, (float)vc.y, (float)vc.z, (float)vc.w);
+            ksr[it] = sd.ks[row * NGK + (dq * 4) / kKGroup];
+            vsr[it] = sd.vs[row];
+        } else {
+            kr[it] = *reinterpret_cast<const float4 *>(sd.k + row * HD + dq * 4);
+            vr[it] = *reinterpret_cast<const float4 *>(sd.v + row * HD + dq * 4);
         }
-        const float inv = 1.0f / L;
-        for (int j = 0; j < nsplit; ++j) wts[j * REP + tid] *= inv;
+    }
+
+    // ---- 2. RoPE (angles in f64, dory.rs `stack`), unit norms, q times sq
+    if (tid < HALF) {
+        const double ang = (double)p * (double)a.inv[tid];
+        rot[0][tid] = (float)cos(ang);
+        rot[1][tid] = (float)sin(ang);
     }
     __syncthreads();
-    const int ld = Q + 2 * a.nk * HD + Q;
+    const int nvec = REP + (tail ? 1 : 0);
+    for (int idx = tid; idx < nvec * HALF; idx += 256) {
+        const int v = idx / HALF, j = idx % HALF;
+        const float *src = v < REP ? a.qkvg + (size_t)(kh * REP + v) * HD : a.qkvg + Q + (size_t)kh * HD;
+        const float x = src[j], y = src[j + HALF], cs = rot[0][j], sn = rot[1][j];
+        qs[v][j] = x * cs - y * sn;
+        qs[v][j + HALF] = y * cs + x * sn;
+    }
+    if (tail)
+        for (int d = tid; d < HD; d += 256) vn[d] = a.qkvg[Q + KV + (size_t)kh * HD + d];
+    __syncthreads();
+    for (int v = wave; v < nvec; v += 4) {
+        float ss = 0.f;
+        for (int d = lane; d < HD; d += 64) ss += qs[v][d] * qs[v][d];
+        const float f = norm_factor(wave_sum(ss));
+        for (int d = lane; d < HD; d += 64)
+            qs[v][d] *= v < REP ? f * a.sq[(kh * REP + v) * HD + d] : f;
+    }
+    __syncthreads();
+
+    // ---- 3. the new row: into the cache, and in place of its prefetched copy
+    if (tail) {
+        const size_t row = (size_t)kh * cap + (size_t)(p % cap);
+        if (Q8) {
+            if (wave == 0) encode_row(qs[REP], a.field ? sd.kcol + kh * HD : nullptr, HD, kKGroup, kcn, ksn);
+            if (wave == 1) encode_row(vn, a.field ? sd.vcol + kh * HD : nullptr, HD, HD, vcn, vsn);
+            __syncthreads();
+            if (!a.no_write) {
+            for (int d = tid; d < HD; d += 256) {
+                sd.kc[row * HD + d] = kcn[d];
+                sd.vc[row * HD + d] = vcn[d];
+            }
+            if (tid < NGK) sd.ks[row * NGK + tid] = ksn[tid];
+            if (tid == 0) sd.vs[row] = vsn[0];
+            }
+        } else if (!a.no_write) {
+            for (int d = tid; d < HD; d += 256) {
+                sd.k[row * HD + d] = qs[REP][d];
+                sd.v[row * HD + d] = vn[d];
+            }
+        }
+        const int el = len - 1;
+        if (g == el % KB) {
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                if (it != el / KB) continue;
+                if (Q8) {
+                    const char4 kc = *reinterpret_cast<const char4 *>(kcn + dq * 4);
+                    const char4 vc = *reinterpret_cast<const char4 *>(vcn + dq * 4);
+                    kr[it] = make_float4((float)kc.x, (float)kc.y, (float)kc.z, (float)kc.w);
+                    vr[it] = make_float4((float)vc.x, (float)vc.y, (float)vc.z, (float)vc.w);
+                    ksr[it] = ksn[(dq * 4) / kKGroup];
+                    vsr[it] = vsn[0];
+                } else {
+                    kr[it] = *reinterpret_cast<const float4 *>(&qs[REP][dq * 4]);
+                    vr[it] = *reinterpret_cast<const float4 *>(&vn[dq * 4]);
+                }
+            }
+        }
+    }
+
+    // ---- 4. scores s_e = q . k_e / sqrt(hd)
+    {
+        float4 q[REP];
+#pragma unroll
+        for (int h = 0; h < REP; ++h) q[h] = *reinterpret_cast<const float4 *>(&qs[h][dq * 4]);
+        if (Q8 && a.field) {
+            const float4 c = *reinterpret_cast<const float4 *>(sd.kcol + kh * HD + dq * 4);
+#pragma unroll
+            for (int h = 0; h < REP; ++h) {
+                q[h].x *= c.x; q[h].y *= c.y; q[h].z *= c.z; q[h].w *= c.w;
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = g + KB * it;
+#pragma unroll
+            for (int h = 0; h < REP; ++h) {
+                float d = q[h].x * kr[it].x + q[h].y * kr[it].y + q[h].z * kr[it].z + q[h].w * kr[it].w;
+                if (Q8) d *= ksr[it];
+                d = group_sum<LPK>(d);
+                if (e < len && dq == 0) sc[h][e] = d * scale;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- 5. per-head max and sum of exp (dory.rs `soft_body`)
+    for (int h = wave; h < REP; h += 4) {
+        float m = -INFINITY;
+        for (int e = lane; e < len; e += 64) m = fmaxf(m, sc[h][e]);
+        m = wave_max(m);
+        float l = 0.f;
+        for (int e = lane; e < len; e += 64) {
+            const float pv = expf(sc[h][e] - m);
+            sc[h][e] = pv;
+            l += pv;
+        }
+        l = wave_sum(l);
+        if (lane == 0) {
+            stat[0][h] = m;
+            stat[1][h] = l;
+        }
+    }
+    __syncthreads();
+
+    // ---- 6. values: acc_h = sum_e p_e v_e
+    {
+        float4 acc[REP];
+#pragma unroll
+        for (int h = 0; h < REP; ++h) acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = g + KB * it;
+            if (e < len) {
+#pragma unroll
+                for (int h = 0; h < REP; ++h) {
+                    const float w = Q8 ? sc[h][e] * vsr[it] : sc[h][e];
+                    acc[h].x += w * vr[it].x;
+                    acc[h].y += w * vr[it].y;
+                    acc[h].z += w * vr[it].z;
+                    acc[h].w += w * vr[it].w;
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < REP; ++h) *reinterpret_cast<float4 *>(&red[(g * REP + h) * HD + dq * 4]) = acc[h];
+    }
+    __syncthreads();
+    const size_t pstride = (size_t)REP * (HD + 2);
+    float *mine = a.part + ((size_t)kh * a.max_split + s) * pstride;
     for (int idx = tid; idx < REP * HD; idx += 256) {
         const int h = idx / HD, d = idx % HD;
-        float y = 0.f;
-        for (int j = 0; j < nsplit; ++j) y += wts[j * REP + h] * load_agent(all + j * pstride + h * (HD + 2) + 2 + d);
-        if (Q8 && a.field) y *= sd.vcol[kh * HD + d];
-        const int hq = kh * REP + h;
-        const float g = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * HD + hq * HD + d];
-        y = y / (1.0f + expf(-(g * a.sg[hq * HD + d])));
-        a.z[(size_t)r * Q + hq * HD + d] = y;
+        float v = 0.f;
+#pragma unroll 8
+        for (int gg = 0; gg < KB; ++gg) v += red[(gg * REP + h) * HD + d];
+        mine[h * (HD + 2) + 2 + d] = v;
     }
-    if (tid == 0) a.cnt[r * a.nk + kh] = 0;
+    if (tid < REP) {
+        mine[tid * (HD + 2)] = stat[0][tid];
+        mine[tid * (HD + 2) + 1] = stat[1][tid];
+    }
 }
 
 template <int HD, int REP>
 hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
-    dim3 grid(a.max_split, a.nk, T), block(256);
-    if (a.q8) hipLaunchKernelGGL((k_attn<HD, REP, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_attn<HD, REP, 0>), grid, block, 0, s, a);
+    if (T == 0) {  // one-row decode kernel
+        dim3 grid(a.max_split, a.nk), block(256);
+        if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0>), grid, block, 0, s, a);
+    } else {
+        dim3 grid(a.max_split, a.nk, T), block(256);
+        if (a.q8) hipLaunchKernelGGL((k_attn<HD, REP, 1>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((k_attn<HD, REP, 0>), grid, block, 0, s, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 mgrid(T ? T : 1, a.nh, (HD + 63) / 64);
+    if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(64), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
@@ -274,15 +505,7 @@ hipError_t launch_h(const AttnArgs &a, int T, hipStream_t s) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_prep, dim3(T, a.nh + a.nk), dim3(64), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
-    if (a.split <= 0 || a.split > 256) return hipErrorInvalidValue;
+hipError_t launch_hd(const AttnArgs &a, int T, hipStream_t s) {
     switch (a.hd) {
         case 8: return launch_h<8>(a, T, s);
         case 16: return launch_h<16>(a, T, s);
@@ -292,6 +515,28 @@ hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
         case 256: return launch_h<256>(a, T, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
+    hipLaunchKernelGGL(k_prep, dim3(T, a.nh + a.nk), dim3(64), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
+    if (a.split <= 0 || a.split > 256 || T <= 0) return hipErrorInvalidValue;
+    return launch_hd(a, T, s);
+}
+
+int attn_dec_max_split(int hd) {
+    const int kb = 256 / (hd / 4);
+    return 8 * kb < 256 ? 8 * kb : 256;
+}
+
+hipError_t launch_attn_dec(const AttnArgs &a, hipStream_t s) {
+    if (a.split <= 0 || a.split > attn_dec_max_split(a.hd)) return hipErrorInvalidValue;
+    return launch_hd(a, 0, s);
 }
 
 }  // namespace dk

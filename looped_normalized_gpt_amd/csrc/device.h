@@ -11,25 +11,44 @@ __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u <
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+// Cross-lane steps on wave64 without LDS traffic: DPP quad permutes and row
+// mirrors inside 16-lane rows, a swizzle across the two rows of a 32-lane half,
+// and a bpermute across the halves.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+__device__ __forceinline__ float swap16(float v) {  // lane i <-> lane i ^ 16 (within 32)
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
 }
+__device__ __forceinline__ float swap32(float v) { return __shfl_xor(v, 32, 64); }
 
-// Sum over aligned groups of G lanes (G a power of two, <= 64).
+// Sum over aligned groups of G lanes (G a power of two, <= 64); every lane of
+// a group gets the group's sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int o = G / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    if (G >= 2) v += dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if (G >= 4) v += dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if (G >= 8) v += dpp<0x141>(v);   // row_half_mirror: the other quad of 8
+    if (G >= 16) v += dpp<0x140>(v);  // row_mirror: the other 8 of 16
+    if (G >= 32) v += swap16(v);
+    if (G >= 64) v += swap32(v);
     return v;
 }
+
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+    if (G >= 2) v = fmaxf(v, dpp<0xB1>(v));
+    if (G >= 4) v = fmaxf(v, dpp<0x4E>(v));
+    if (G >= 8) v = fmaxf(v, dpp<0x141>(v));
+    if (G >= 16) v = fmaxf(v, dpp<0x140>(v));
+    if (G >= 32) v = fmaxf(v, swap16(v));
+    if (G >= 64) v = fmaxf(v, swap32(v));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
+__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
 // Sums of two values over a 256-thread workgroup; red holds >= 8 floats.
 // Every thread gets both results.
@@ -126,6 +145,138 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
     if (writer && rs.h_out) {
         float *ho = rs.h_out + (size_t)r * H;
         for (int i = tid; i < H; i += 256) ho[i] = xs[i];
+    }
+}
+
+// The same step with the inputs already in registers.  Thread tid holds the
+// float4 groups at 4*tid + 1024*jj (jj < EPT/4) of the row in slots
+// 4*jj .. 4*jj+3 (zeros past H).  h, o, al, in: the residual, the sub-layer
+// output, |alpha| and the loop input.  No global loads, so it can run while a
+// caller's earlier loads are still in flight.
+__device__ __forceinline__ int reg_index(int j) { return 4 * (int)threadIdx.x + 1024 * (j >> 2) + (j & 3); }
+
+template <int EPT>
+__device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float (&h)[EPT], const float (&o)[EPT],
+                                    const float (&al)[EPT], const float (&in)[EPT], float *xs, float *red,
+                                    bool writer, const CallRec *rec) {
+    float e[EPT];
+    if (!rs.slerp) {
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) e[j] = h[j];
+    } else {
+        float sx = 0.f, so = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            sx += h[j] * h[j];
+            so += o[j] * o[j];
+        }
+        block_sum2(sx, so, red);
+        const float rx = norm_factor(sx), ro = norm_factor(so);
+        float se = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const float xh = h[j] * rx, oh = o[j] * ro;
+            e[j] = xh + al[j] * (oh - xh);
+            se += e[j] * e[j];
+        }
+        const float re = norm_factor(block_sum(se, red));
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) e[j] *= re;
+    }
+    if (writer && rec->tap && rs.tap_pass >= 0) {
+        float *t = rec->tap + ((size_t)rs.tap_pass * rec->n + r) * H;
+#pragma unroll
+        for (int j = 0; j < EPT; j += 4)
+            if (reg_index(j) < H) *reinterpret_cast<float4 *>(t + reg_index(j)) = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
+    }
+    if (rs.loop_op == kLoopEnter) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPT; j += 4) {
+            if (writer && reg_index(j) < H)
+                *reinterpret_cast<float4 *>(rs.inp + (size_t)r * H + reg_index(j)) =
+                    make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
+        }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            e[j] = e[j] + e[j];
+            s += e[j] * e[j];
+        }
+        const float f = norm_factor(block_sum(s, red));
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) e[j] *= f;
+    } else if (rs.loop_op != kLoopNone) {
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) s += e[j] * e[j];
+        const float fs = norm_factor(block_sum(s, red));
+        if (rs.loop_op == kLoopExit) {
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) e[j] *= fs;
+        } else {
+            float s2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) {
+                e[j] = e[j] * fs + in[j];
+                s2 += e[j] * e[j];
+            }
+            const float f = norm_factor(block_sum(s2, red));
+#pragma unroll
+            for (int j = 0; j < EPT; ++j) e[j] *= f;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < EPT; j += 4) {
+        const int i = reg_index(j);
+        if (i < H) {
+            const float4 v = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
+            *reinterpret_cast<float4 *>(xs + i) = v;
+            if (writer && rs.h_out) *reinterpret_cast<float4 *>(rs.h_out + (size_t)r * H + i) = v;
+        }
+    }
+}
+
+// kv_cache.rs `quant_row` for one row of n <= 256 values, one wave: r = x/col
+// (x when col is null); per group of `group` channels (32, or one group when
+// group >= n) scale = max(absmax/127, 1e-12) and code = clamp(round(r/scale),
+// -127, 127), rounding half away from zero.  Only IEEE correctly rounded
+// divisions and exact max/abs/round: no step a compiler could contract, so the
+// codes and scales equal the fp32 definition bit for bit.
+__device__ inline void encode_row(const float *x, const float *col, int n, int group, int8_t *codes,
+                                  float *scales) {
+    const int lane = threadIdx.x & 63;
+    float r[4];
+    float m[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        r[i] = 0.f;
+        if (d < n) r[i] = col ? __fdiv_rn(x[d], col[d]) : x[d];
+        m[i] = fabsf(r[i]);
+    }
+    if (group >= n) {
+        float mm = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+        mm = wave_max(mm);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m[i] = mm;
+    } else {
+        // group == 32: channel lane + 64i is in group (lane >> 5) + 2i, one half-wave
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m[i] = group_max<32>(m[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        if (d >= n) continue;
+        const float s = fmaxf(__fdiv_rn(m[i], 127.0f), 1e-12f);
+        float c = roundf(__fdiv_rn(r[i], s));
+        c = fminf(fmaxf(c, -127.0f), 127.0f);
+        codes[d] = (int8_t)c;
+        if (group >= n) {
+            if (d == 0) scales[0] = s;
+        } else if (d % group == 0) {
+            scales[d / group] = s;
+        }
     }
 }
 

@@ -79,22 +79,49 @@ template <int WT, int PRO, int EPI, int MAXC>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     extern __shared__ float smem[];
     constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
-    float *xs = smem;                 // [K]
-    float *red = smem + a.K;          // [8]
-    float *part = red + 8;            // [4][WR]
+    constexpr int EPT = 8 * MAXC;  // prologue elements per thread: K <= 2048 * MAXC
+    float *xs = smem;              // [K]
+    float *red = smem + a.K;       // [8]
+    float *part = red + 8;         // [4][WR]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row0 = blockIdx.x * ROWS;
     const int K = a.K, N = a.N;
     const CallRec *rec = a.rec;
+    const Resolve &rs = a.rs;
 
     if (EPI == kEpiHead && rec->logits == nullptr) {
         // No logits wanted: only the tap of the last pass, if any.
         if (PRO != kProResolve || blockIdx.x != 0 || rec->tap == nullptr) return;
-        resolve_row(a.rs, a.row, K, xs, red, true, rec);
+        resolve_row(rs, a.row, K, xs, red, true, rec);
         return;
     }
 
-    // Weight rows of this workgroup.
+    // 1. The prologue's inputs, as float4 groups at 4*tid + 1024*jj.  Every load
+    // is unconditional (out-of-range groups re-read group 0 and are zeroed), so
+    // the compiler can count them and wait for exactly these below.
+    float ph[EPT], po[EPT], pa[EPT], pi[EPT];
+    {
+        const float *src = (PRO == kProResolve ? rs.h : a.src) + (size_t)a.row * K;
+#pragma unroll
+        for (int jj = 0; jj < EPT / 4; ++jj) {
+            const int i = 4 * tid + 1024 * jj;
+            const int ic = i < K ? i : 0;
+            const float4 v = *reinterpret_cast<const float4 *>(src + ic);
+            ph[4 * jj] = v.x; ph[4 * jj + 1] = v.y; ph[4 * jj + 2] = v.z; ph[4 * jj + 3] = v.w;
+            if (PRO == kProResolve) {
+                const float4 vo = *reinterpret_cast<const float4 *>(rs.o + (size_t)a.row * K + ic);
+                const float4 va = *reinterpret_cast<const float4 *>(rs.alpha + ic);
+                const float4 vi = *reinterpret_cast<const float4 *>(rs.inp + (size_t)a.row * K + ic);
+                po[4 * jj] = vo.x; po[4 * jj + 1] = vo.y; po[4 * jj + 2] = vo.z; po[4 * jj + 3] = vo.w;
+                pa[4 * jj] = va.x; pa[4 * jj + 1] = va.y; pa[4 * jj + 2] = va.z; pa[4 * jj + 3] = va.w;
+                pi[4 * jj] = vi.x; pi[4 * jj + 1] = vi.y; pi[4 * jj + 2] = vi.z; pi[4 * jj + 3] = vi.w;
+            }
+        }
+    }
+
+    // 2. Weight rows of this workgroup, every load issued now (the prologue runs
+    // while they fly).  Rows past N and chunks past K re-read a valid address
+    // and are masked at use.
     const void *base[WR];
     size_t roff[WR];
     bool valid[WR];
@@ -105,44 +132,52 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int j = 0; j < WR; ++j) {
         const int n = row0 + (j % ROWS);
         valid[j] = n < N;
+        const int nn = valid[j] ? n : row0;
         if (EPI == kEpiPair) {
             base[j] = a.w[j < ROWS ? 0 : 1];
-            roff[j] = (size_t)n * K;
+            roff[j] = (size_t)nn * K;
         } else {
             base[j] = a.w[seg];
-            roff[j] = (size_t)(n - seg0) * K;
+            roff[j] = (size_t)(nn - seg0) * K;
         }
     }
-
-    // Issue every weight load first; the prologue runs while they fly.
     W8<WT> wv[WR][MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
         const int k0 = (wave + 4 * c) * 512 + lane * 8;
+        const int kc = k0 < K ? k0 : 0;
 #pragma unroll
-        for (int j = 0; j < WR; ++j) {
-            if (k0 < K && valid[j]) wv[j][c].load(base[j], roff[j] + k0);
-            else wv[j][c].zero();
-        }
+        for (int j = 0; j < WR; ++j) wv[j][c].load(base[j], roff[j] + kc);
     }
 
+    // 3. x in LDS.
     if (PRO == kProResolve) {
-        resolve_row(a.rs, a.row, K, xs, red, blockIdx.x == 0, rec);
+#pragma unroll
+        for (int jj = 0; jj < EPT / 4; ++jj)
+            if (4 * tid + 1024 * jj >= K)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) ph[4 * jj + c] = po[4 * jj + c] = pa[4 * jj + c] = pi[4 * jj + c] = 0.f;
+        resolve_regs<EPT>(rs, a.row, K, ph, po, pa, pi, xs, red, blockIdx.x == 0, rec);
     } else {
-        const float *src = a.src + (size_t)a.row * K;
-        float s = 0.f;
-        for (int i = tid; i < K; i += 256) {
-            float v = src[i];
-            xs[i] = v;
-            s += v * v;
-        }
+        float f = 1.f;
         if (PRO == kProNorm) {
-            const float f = norm_factor(block_sum(s, red));
-            for (int i = tid; i < K; i += 256) xs[i] *= f;
+            float s = 0.f;
+#pragma unroll
+            for (int j = 0; j < EPT; ++j)
+                if (reg_index(j) < K) s += ph[j] * ph[j];
+            f = norm_factor(block_sum(s, red));
+        }
+#pragma unroll
+        for (int jj = 0; jj < EPT / 4; ++jj) {
+            const int i = 4 * tid + 1024 * jj;
+            if (i < K)
+                *reinterpret_cast<float4 *>(xs + i) =
+                    make_float4(ph[4 * jj] * f, ph[4 * jj + 1] * f, ph[4 * jj + 2] * f, ph[4 * jj + 3] * f);
         }
     }
     __syncthreads();
 
+    // 4. Dot products, wave reductions, the 4 wave partials through LDS.
     float acc[WR];
 #pragma unroll
     for (int j = 0; j < WR; ++j) acc[j] = 0.f;
@@ -159,7 +194,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
     for (int j = 0; j < WR; ++j) {
         float v = wave_sum(acc[j]);
-        if (lane == 0) part[wave * WR + j] = v;
+        if (lane == 0) part[wave * WR + j] = valid[j] ? v : 0.f;
     }
     __syncthreads();
     if (tid < ROWS) {

@@ -117,8 +117,7 @@ struct AttnArgs {
     const float *qkvg;   // gate g at column Q + 2KV
     const float *sg;     // [Q]
     float *z;            // [T][Q] gated attention output (before the renorm)
-    float *part;         // split partials
-    int32_t *cnt;        // [T][nk] arrival counters, zero between launches
+    float *part;         // split partials [T][nk][max_split][rep][2 + hd]: max, sum, sum of p*v
     const SlotDesc *tab;
     int32_t n_ord, ord, slot;
     int32_t nh, nk, hd;
@@ -128,8 +127,17 @@ struct AttnArgs {
     int32_t q8;          // cache encoding
     int32_t field;       // q8: the field is frozen (apply kcol / vcol)
     const CallRec *rec;
+    // one-row calls: the RoPE, norms and cache write of the new row are fused in
+    const float *inv;    // [hd/2] RoPE inverse frequencies of the layer's kind
+    const float *sq;     // [Q]
+    int32_t no_write;    // benchmark only: leave the cache row of p untouched
 };
+// Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
+// One-row calls from the raw projections: grid (max_split, nk), then the merge.
+hipError_t launch_attn_dec(const AttnArgs &a, hipStream_t s);
+// Keys a one-row workgroup takes at most for head dim hd.
+int attn_dec_max_split(int hd);
 
 // q8_2f cache writes (kv_cache.rs `append` / `freeze_cols`).
 struct Q8WriteArgs {

@@ -14,52 +14,6 @@ namespace dk {
 
 namespace {
 
-// Encodes one row of n <= 256 values with one wave: r = x/col (x when col is
-// null), per group of `group` channels (32, or one group when group >= n)
-// scale = max(absmax/127, 1e-12) and code = clamp(round(r/scale), -127, 127),
-// rounding half away from zero.
-__device__ void encode_row(const float *x, const float *col, int n, int group, int8_t *codes,
-                           float *scales) {
-    const int lane = threadIdx.x & 63;
-    float r[4];
-    float m[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int d = lane + 64 * i;
-        r[i] = 0.f;
-        if (d < n) r[i] = col ? __fdiv_rn(x[d], col[d]) : x[d];
-        m[i] = fabsf(r[i]);
-    }
-    if (group >= n) {
-        float mm = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
-        mm = wave_max(mm);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m[i] = mm;
-    } else {
-        // group == 32: channel lane + 64i is in group (lane >> 5) + 2i, one half-wave
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int o = 16; o > 0; o >>= 1) m[i] = fmaxf(m[i], __shfl_xor(m[i], o, 64));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int d = lane + 64 * i;
-        if (d >= n) continue;
-        const float s = fmaxf(__fdiv_rn(m[i], 127.0f), 1e-12f);
-        float c = roundf(__fdiv_rn(r[i], s));
-        c = fminf(fmaxf(c, -127.0f), 127.0f);
-        codes[d] = (int8_t)c;
-        if (d % group == 0 || group >= n) {
-            if (group >= n) {
-                if (d == 0) scales[0] = s;
-            } else {
-                scales[d / group] = s;
-            }
-        }
-    }
-}
-
 // One wave per (row of the call, kv head): the row's K (groups of 32) and V (one
 // group of hd) into ring row p % cap, against the field when it is frozen.
 __global__ __launch_bounds__(64) void k_q8_write(Q8WriteArgs a) {
