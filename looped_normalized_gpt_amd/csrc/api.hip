@@ -56,7 +56,7 @@ struct dory {
     // device scratch
     float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
     float *z = nullptr, *zn = nullptr, *ga = nullptr, *gb = nullptr, *un = nullptr, *kstage = nullptr;
-    float *part = nullptr, *inv_s = nullptr, *inv_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
+    float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
     std::vector<SlotDesc> tab_host;
@@ -239,7 +239,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
     aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
     aa.window = l.sliding ? h->win_s : h->win_f;
     aa.q8 = h->q8; aa.rec = h->rec;
-    aa.inv = l.sliding ? h->inv_s : h->inv_f; aa.sq = w.sq;
+    aa.rope = l.sliding ? h->rope_s : h->rope_f; aa.sq = w.sq;
     if (T == 1 && !freeze_now) {
         // one row: prep and the cache write are fused into the attention kernel
         aa.split = l.sliding ? h->split_ds : h->split_df;
@@ -249,7 +249,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
     } else {
         PrepArgs pa{};
         pa.qkvg = h->qkvg; pa.qp = h->qp; pa.kstage = h->q8 ? h->kstage : nullptr;
-        pa.inv = l.sliding ? h->inv_s : h->inv_f; pa.sq = w.sq; pa.tab = h->tab;
+        pa.rope = l.sliding ? h->rope_s : h->rope_f; pa.sq = w.sq; pa.tab = h->tab;
         pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = h->rec;
         LAUNCH(launch_prep(pa, T, q.s));
         bool field = false;
@@ -507,14 +507,26 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     char *recp = nullptr;
     CREATE_CHECK(dmalloc(h, &recp, h->rec_sz));
     h->rec = reinterpret_cast<CallRec *>(recp);
-    // RoPE inverse frequencies theta^(-2j/hd), computed in double, kept as fp32.
-    std::vector<float> inv(h->hd / 2);
-    CREATE_CHECK(dmalloc(h, &h->inv_s, inv.size()));
-    CREATE_CHECK(dmalloc(h, &h->inv_f, inv.size()));
-    for (int j = 0; j < h->hd / 2; ++j) inv[j] = (float)std::pow(cfg->rope_theta_sliding, -2.0 * j / h->hd);
-    CREATE_CHECK(hipMemcpy(h->inv_s, inv.data(), sizeof(float) * inv.size(), hipMemcpyHostToDevice));
-    for (int j = 0; j < h->hd / 2; ++j) inv[j] = (float)std::pow(cfg->rope_theta_full, -2.0 * j / h->hd);
-    CREATE_CHECK(hipMemcpy(h->inv_f, inv.data(), sizeof(float) * inv.size(), hipMemcpyHostToDevice));
+    // RoPE tables for every position (dory.rs `stack`): inverse frequencies
+    // theta^(-2j/hd) rounded to fp32, angle p * inv in f64, cos and sin rounded
+    // to fp32; row p is [cos half | sin half].
+    {
+        const int hd = h->hd, half = hd / 2;
+        std::vector<float> tab((size_t)cfg->max_ctx * hd), inv(half);
+        for (int kind = 0; kind < 2; ++kind) {
+            const double theta = kind == 0 ? cfg->rope_theta_sliding : cfg->rope_theta_full;
+            for (int j = 0; j < half; ++j) inv[j] = (float)std::pow(theta, -2.0 * j / hd);
+            for (int64_t p = 0; p < cfg->max_ctx; ++p)
+                for (int j = 0; j < half; ++j) {
+                    const double ang = (double)p * (double)inv[j];
+                    tab[p * hd + j] = (float)std::cos(ang);
+                    tab[p * hd + half + j] = (float)std::sin(ang);
+                }
+            float *&dst = kind == 0 ? h->rope_s : h->rope_f;
+            CREATE_CHECK(dmalloc(h, &dst, tab.size()));
+            CREATE_CHECK(hipMemcpy(dst, tab.data(), sizeof(float) * tab.size(), hipMemcpyHostToDevice));
+        }
+    }
     CREATE_CHECK(hipHostMalloc((void **)&h->stage, h->rec_sz * kStages, hipHostMallocDefault));
     for (int i = 0; i < kStages; ++i) CREATE_CHECK(hipEventCreateWithFlags(&h->stage_ev[i], hipEventDisableTiming));
     CREATE_CHECK(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
@@ -774,7 +786,7 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             aa.window = l->sliding ? h->win_s : h->win_f;
             aa.split = l->sliding ? h->split_ds : h->split_df;
             aa.max_split = l->sliding ? h->ms_ds : h->ms_df;
-            aa.inv = l->sliding ? h->inv_s : h->inv_f; aa.sq = l->w.sq; aa.no_write = 1;
+            aa.rope = l->sliding ? h->rope_s : h->rope_f; aa.sq = l->w.sq; aa.no_write = 1;
             aa.q8 = h->q8; aa.field = h->q8 && h->seqs[0].pos >= kWarmup + 1; aa.rec = h->rec;
             e = launch_attn_dec(aa, s);
         } else if (stage == 2) {

@@ -7,10 +7,9 @@ namespace dk {
 
 namespace {
 
-// dory.rs `attn_layer` (rotate, justnorm per head, q times sq) and `stack` (the
-// RoPE tables: angle = position * inverse frequency in f64, cos/sin rounded to
-// f32).  One wave per (row, head); lane j owns the pairs (j, j + hd/2),
-// (j + 64, j + 64 + hd/2), ...
+// dory.rs `attn_layer` (rotate, justnorm per head, q times sq), with the RoPE
+// table row of the position (dory.rs `stack`: cos half, sin half).  One wave
+// per (row, head); lane j owns the pairs (j, j + hd/2), (j + 64, j + 64 + hd/2).
 __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
     const int r = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
     const int hd = a.hd, half = hd / 2, Q = a.nh * hd, KV = a.nk * hd;
@@ -26,8 +25,7 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
         const int j = lane + 64 * i;
         nx[i] = ny[i] = 0.f;
         if (j < half) {
-            const double ang = (double)p * (double)a.inv[j];
-            const float cs = (float)cos(ang), sn = (float)sin(ang);
+            const float cs = a.rope[(size_t)p * hd + j], sn = a.rope[(size_t)p * hd + half + j];
             const float x = src[j], y = src[j + half];
             nx[i] = x * cs - y * sn;
             ny[i] = y * cs + x * sn;
@@ -79,36 +77,52 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
 
 // Merges the split partials of (row r, q head h) in log-sum-exp form, scales by
 // the V field (q8), applies the sigmoid gate (dory.rs `gate_body`) and writes z.
-// Grid (T, nh, ceil(hd/64)), 64 threads: thread d of the block owns one channel
-// and reads that channel of every split (coalesced across the block).  A kernel
-// of its own: the partials come from workgroups on other XCDs, whose L2s are
-// only coherent with this one at kernel boundaries.
+// Grid (T, nh, ceil(hd/64)); lane d of every wave owns one channel, wave w takes
+// splits w, w + waves, ... with a running (max, sum, acc) merge, then wave 0
+// merges the waves' results.  A kernel of its own: the partials come from
+// workgroups on other XCDs, whose L2s are only coherent with this one at kernel
+// boundaries.
 template <int Q8>
-__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
-    const int r = blockIdx.x, hq = blockIdx.y, d = blockIdx.z * 64 + threadIdx.x;
+__global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
+    __shared__ float sm[16][66];
+    const int r = blockIdx.x, hq = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6;
+    const int d = blockIdx.z * 64 + lane;
     const int hd = a.hd, rep = a.nh / a.nk, kh = hq / rep, h = hq % rep;
     const int64_t p = a.rec->pos0 + r;
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
     const size_t pstride = (size_t)rep * (hd + 2);
     const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride + (size_t)h * (hd + 2);
-    float M = -INFINITY;
-    for (int j = 0; j < nsplit; ++j) M = fmaxf(M, all[j * pstride]);
-    if (d >= hd) return;
-    float L = 0.f, y0 = 0.f, y1 = 0.f;
-    int j = 0;
-    for (; j + 2 <= nsplit; j += 2) {
-        const float w0 = expf(all[j * pstride] - M), w1 = expf(all[(j + 1) * pstride] - M);
-        L += w0 * all[j * pstride + 1] + w1 * all[(j + 1) * pstride + 1];
-        y0 += w0 * all[j * pstride + 2 + d];
-        y1 += w1 * all[(j + 1) * pstride + 2 + d];
+    const int dc = d < hd ? d : 0;
+    float M = -INFINITY, L = 0.f, acc = 0.f;
+#pragma unroll 4
+    for (int j = wave; j < nsplit; j += nw) {
+        const float *pj = all + j * pstride;
+        const float m = pj[0], l = pj[1], v = pj[2 + dc];
+        const float Mn = fmaxf(M, m);
+        const float c0 = expf(M - Mn), c1 = expf(m - Mn);
+        L = L * c0 + l * c1;
+        acc = acc * c0 + v * c1;
+        M = Mn;
     }
-    for (; j < nsplit; ++j) {
-        const float w0 = expf(all[j * pstride] - M);
-        L += w0 * all[j * pstride + 1];
-        y0 += w0 * all[j * pstride + 2 + d];
+    sm[wave][2 + lane] = acc;
+    if (lane == 0) {
+        sm[wave][0] = M;
+        sm[wave][1] = L;
     }
-    float y = (y0 + y1) / L;
+    __syncthreads();
+    if (wave != 0 || d >= hd) return;
+    float Mt = -INFINITY;
+    for (int w = 0; w < nw; ++w) Mt = fmaxf(Mt, sm[w][0]);
+    float Lt = 0.f, y = 0.f;
+    for (int w = 0; w < nw; ++w) {
+        if (sm[w][0] == -INFINITY) continue;  // a wave with no split
+        const float c = expf(sm[w][0] - Mt);
+        Lt += sm[w][1] * c;
+        y += sm[w][2 + lane] * c;
+    }
+    y /= Lt;
     if (Q8 && a.field) {
         const SlotDesc &sd = slot_at(a.tab, a.rec->seq, a.n_ord, a.ord, a.slot);
         y *= sd.vcol[kh * hd + d];
@@ -268,19 +282,23 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 // LDS in place of the ring row it prefetched.
 //
 // Each thread owns key slot g = tid / (HD/4) and the 4 channels dq*4.. of it;
-// the workgroup takes KB = 256/(HD/4) keys per step and IT = 8 steps, and every
-// K and V load of the split is issued before any arithmetic.
+// the workgroup takes KB = 256/(HD/4) keys per step and IT = 8 steps.  Load
+// order: the projections, sq and the RoPE row first, then every K and V load
+// of the split; the prep waits only for the first group while the cache rows
+// are in flight.
 template <int HD, int REP, int Q8>
 __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     constexpr int LPK = HD / 4, KB = 256 / LPK, IT = 8;
     constexpr int SMAX = IT * KB < 256 ? IT * KB : 256;
     constexpr int NGK = (HD + kKGroup - 1) / kKGroup;
     constexpr int HALF = HD / 2;
+    constexpr int QPT = (REP * HD + 255) / 256;  // query values per thread
     __shared__ float sc[REP][SMAX];
     __shared__ float red[KB * REP * HD];
     __shared__ float qs[REP + 1][HD];  // the group's query heads, then the new key
+    __shared__ float sqs[REP][HD];
     __shared__ float vn[HD];
-    __shared__ float rot[2][HALF];
+    __shared__ float rot[HD];          // cos half, sin half
     __shared__ int8_t kcn[HD], vcn[HD];
     __shared__ float ksn[NGK], vsn[1];
     __shared__ float stat[2][REP];
@@ -300,6 +318,19 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     const int Q = a.nh * HD, KV = a.nk * HD;
     const int g = tid / LPK, dq = tid % LPK;
     const float scale = 1.0f / sqrtf((float)HD);
+
+    // ---- 0. the prep's inputs (unconditional loads at clamped indices)
+    float qv[QPT], sv[QPT];
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int idx = tid + 256 * i < REP * HD ? tid + 256 * i : 0;
+        qv[i] = a.qkvg[(size_t)kh * REP * HD + idx];
+        sv[i] = a.sq[(size_t)kh * REP * HD + idx];
+    }
+    const int td = tid < HD ? tid : 0;
+    const float kraw = a.qkvg[Q + (size_t)kh * HD + td];
+    const float vraw = a.qkvg[Q + KV + (size_t)kh * HD + td];
+    const float rv = a.rope[(size_t)p * HD + td];
 
     // ---- 1. every K and V row of the split, in flight at once
     const int rbase = (int)(e0 % cap);
@@ -324,33 +355,36 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
         }
     }
 
-    // ---- 2. RoPE (angles in f64, dory.rs `stack`), unit norms, q times sq
-    if (tid < HALF) {
-        const double ang = (double)p * (double)a.inv[tid];
-        rot[0][tid] = (float)cos(ang);
-        rot[1][tid] = (float)sin(ang);
+    // ---- 2. RoPE, unit norms, q times sq
+#pragma unroll
+    for (int i = 0; i < QPT; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < REP * HD) {
+            qs[idx / HD][idx % HD] = qv[i];
+            sqs[idx / HD][idx % HD] = sv[i];
+        }
+    }
+    if (tid < HD) {
+        qs[REP][tid] = kraw;
+        vn[tid] = vraw;
+        rot[tid] = rv;
     }
     __syncthreads();
     const int nvec = REP + (tail ? 1 : 0);
     for (int idx = tid; idx < nvec * HALF; idx += 256) {
         const int v = idx / HALF, j = idx % HALF;
-        const float *src = v < REP ? a.qkvg + (size_t)(kh * REP + v) * HD : a.qkvg + Q + (size_t)kh * HD;
-        const float x = src[j], y = src[j + HALF], cs = rot[0][j], sn = rot[1][j];
+        const float x = qs[v][j], y = qs[v][j + HALF], cs = rot[j], sn = rot[HALF + j];
         qs[v][j] = x * cs - y * sn;
         qs[v][j + HALF] = y * cs + x * sn;
     }
-    if (tail)
-        for (int d = tid; d < HD; d += 256) vn[d] = a.qkvg[Q + KV + (size_t)kh * HD + d];
     __syncthreads();
     for (int v = wave; v < nvec; v += 4) {
         float ss = 0.f;
         for (int d = lane; d < HD; d += 64) ss += qs[v][d] * qs[v][d];
         const float f = norm_factor(wave_sum(ss));
-        for (int d = lane; d < HD; d += 64)
-            qs[v][d] *= v < REP ? f * a.sq[(kh * REP + v) * HD + d] : f;
+        for (int d = lane; d < HD; d += 64) qs[v][d] *= v < REP ? f * sqs[v][d] : f;
     }
     __syncthreads();
-
     // ---- 3. the new row: into the cache, and in place of its prefetched copy
     if (tail) {
         const size_t row = (size_t)kh * cap + (size_t)(p % cap);
@@ -488,9 +522,12 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // one-row calls: 16 waves per head channel block; multi-row calls have
+    // fewer, longer splits and many more rows, so 4
     dim3 mgrid(T ? T : 1, a.nh, (HD + 63) / 64);
-    if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(64), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(64), 0, s, a);
+    const int waves = T ? 4 : 16;
+    if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(64 * waves), 0, s, a);
+    else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(64 * waves), 0, s, a);
     return hipGetLastError();
 }
 

@@ -103,7 +103,7 @@ struct PrepArgs {
     const float *qkvg;   // [T][Q + 2KV + Q]
     float *qp;           // [T][Q] rotated, normed, scaled queries
     float *kstage;       // [T][KV] rotated, normed keys (q8 cache) or null (fp32 cache: ring)
-    const float *inv;    // [hd/2] RoPE inverse frequencies of the layer's kind
+    const float *rope;   // [max_ctx][hd] RoPE table of the layer's kind: cos half, sin half
     const float *sq;     // [Q]
     const SlotDesc *tab;
     int32_t n_ord, ord, slot;
@@ -128,7 +128,7 @@ struct AttnArgs {
     int32_t field;       // q8: the field is frozen (apply kcol / vcol)
     const CallRec *rec;
     // one-row calls: the RoPE, norms and cache write of the new row are fused in
-    const float *inv;    // [hd/2] RoPE inverse frequencies of the layer's kind
+    const float *rope;   // [max_ctx][hd] RoPE table of the layer's kind: cos half, sin half
     const float *sq;     // [Q]
     int32_t no_write;    // benchmark only: leave the cache row of p untouched
 };
