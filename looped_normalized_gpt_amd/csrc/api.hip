@@ -225,7 +225,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         a.w[0] = w.wq; a.w[1] = w.wk; a.w[2] = w.wv; a.w[3] = w.wg;
         a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
         a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
-        LAUNCH(launch_gemv(h->wt, kProResolve, kEpiStore, a, q.s));
+        LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiStore, a, q.s));
     } else {
         LAUNCH(launch_gemm(h->wt, x, h->H, w.wq, h->Q, h->H, h->qkvg, ld, T, q.s));
         LAUNCH(launch_gemm(h->wt, x, h->H, w.wk, h->KV, h->H, h->qkvg + h->Q, ld, T, q.s));
@@ -306,7 +306,7 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x) {
         GemvArgs a{};
         a.w[0] = w.wgate; a.w[1] = w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H; a.row = 0;
         a.rs = rs; a.y = h->ga; a.sg = w.sg; a.su = w.su; a.rec = h->rec; a.hidden = h->H;
-        LAUNCH(launch_gemv(h->wt, kProResolve, kEpiPair, a, q.s));
+        LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiPair, a, q.s));
         GemvArgs d{};
         d.w[0] = w.wdown; d.seg_end[0] = h->H; d.nseg = 1; d.N = h->H; d.K = h->F; d.row = 0;
         d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;

@@ -84,27 +84,44 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
 // boundaries.
 template <int Q8>
 __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
+    constexpr int U = 8;  // splits a wave holds in flight
     __shared__ float sm[16][66];
     const int r = blockIdx.x, hq = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nw = blockDim.x >> 6;
     const int d = blockIdx.z * 64 + lane;
     const int hd = a.hd, rep = a.nh / a.nk, kh = hq / rep, h = hq % rep;
+    const int Q = a.nh * hd, ld = 2 * Q + 2 * a.nk * hd;
+    const int dc = d < hd ? d : 0;
+    // what does not depend on the partials first
+    const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + dc];
+    const float sgv = a.sg[hq * hd + dc];
+    float vcol = 1.f;
+    if (Q8 && a.field) vcol = slot_at(a.tab, a.rec->seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + dc];
     const int64_t p = a.rec->pos0 + r;
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
     const size_t pstride = (size_t)rep * (hd + 2);
     const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride + (size_t)h * (hd + 2);
-    const int dc = d < hd ? d : 0;
     float M = -INFINITY, L = 0.f, acc = 0.f;
-#pragma unroll 4
-    for (int j = wave; j < nsplit; j += nw) {
-        const float *pj = all + j * pstride;
-        const float m = pj[0], l = pj[1], v = pj[2 + dc];
-        const float Mn = fmaxf(M, m);
-        const float c0 = expf(M - Mn), c1 = expf(m - Mn);
-        L = L * c0 + l * c1;
-        acc = acc * c0 + v * c1;
-        M = Mn;
+    for (int base = wave; base < nsplit; base += nw * U) {
+        float m[U], l[U], v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + nw * u;
+            const float *pj = all + (size_t)(j < nsplit ? j : base) * pstride;
+            m[u] = pj[0];
+            l[u] = pj[1];
+            v[u] = pj[2 + dc];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (base + nw * u >= nsplit) break;
+            const float Mn = fmaxf(M, m[u]);
+            const float c0 = expf(M - Mn), c1 = expf(m[u] - Mn);
+            L = L * c0 + l[u] * c1;
+            acc = acc * c0 + v[u] * c1;
+            M = Mn;
+        }
     }
     sm[wave][2 + lane] = acc;
     if (lane == 0) {
@@ -122,14 +139,8 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
         Lt += sm[w][1] * c;
         y += sm[w][2 + lane] * c;
     }
-    y /= Lt;
-    if (Q8 && a.field) {
-        const SlotDesc &sd = slot_at(a.tab, a.rec->seq, a.n_ord, a.ord, a.slot);
-        y *= sd.vcol[kh * hd + d];
-    }
-    const int Q = a.nh * hd, ld = 2 * Q + 2 * a.nk * hd;
-    const float g = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + d];
-    a.z[(size_t)r * Q + hq * hd + d] = y / (1.0f + expf(-(g * a.sg[hq * hd + d])));
+    y = y / Lt * vcol;
+    a.z[(size_t)r * Q + hq * hd + d] = y / (1.0f + expf(-(gate * sgv)));
 }
 
 // Grouped-query attention of one row over keys max(p+1-window, 0) ..= p for the

@@ -5,7 +5,8 @@
 // HBM-bound: every weight byte is read once, so the kernel keeps many 16-byte
 // loads in flight and hides the prologue behind them.
 //
-// Workgroup: 256 threads = 4 waves, ROWS output rows.  The K axis is cut in
+// Workgroup: 256 threads = 4 waves, ROWS output rows (4, 8 or 16: more rows per
+// workgroup for the larger matrices, so fewer workgroups repeat the prologue).  The K axis is cut in
 // 512-element chunks (64 lanes x 8 elements = one 16-byte bf16 load per lane),
 // dealt round-robin to the 4 waves; a wave issues the loads of all its chunks
 // for all its rows before the prologue runs, then reduces each row over its 64
@@ -28,17 +29,22 @@ namespace dk {
 
 namespace {
 
-constexpr int ROWS = 4;
-
 template <int WT>
 struct W8;
+
+// Weights are read once per token: streaming (nontemporal) loads keep them from
+// displacing what the caches hold for the next kernels.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <>
 struct W8<kBF16> {
     uint4 v;
     __device__ __forceinline__ void zero() { v = make_uint4(0, 0, 0, 0); }
     __device__ __forceinline__ void load(const void *base, size_t elem) {
-        v = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(base) + elem);
+        const u32x4 t = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(base) + elem));
+        v = make_uint4(t.x, t.y, t.z, t.w);
     }
     __device__ __forceinline__ float dot(const float4 &a, const float4 &b) const {
         float s = bf16lo(v.x) * a.x;
@@ -58,9 +64,10 @@ struct W8<kF32> {
     float4 a, b;
     __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
     __device__ __forceinline__ void load(const void *base, size_t elem) {
-        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(base) + elem);
-        a = p[0];
-        b = p[1];
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(reinterpret_cast<const float *>(base) + elem);
+        const f32x4 x = __builtin_nontemporal_load(p), y = __builtin_nontemporal_load(p + 1);
+        a = make_float4(x.x, x.y, x.z, x.w);
+        b = make_float4(y.x, y.y, y.z, y.w);
     }
     __device__ __forceinline__ float dot(const float4 &x, const float4 &y) const {
         float s = a.x * x.x;
@@ -75,8 +82,9 @@ struct W8<kF32> {
     }
 };
 
-template <int WT, int PRO, int EPI, int MAXC>
+template <int WT, int PRO, int EPI, int MAXC, int ROWS>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
+    constexpr bool RES = PRO == kProResolve || PRO == kProResolveInp;
     extern __shared__ float smem[];
     constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
     constexpr int EPT = 8 * MAXC;  // prologue elements per thread: K <= 2048 * MAXC
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 
     if (EPI == kEpiHead && rec->logits == nullptr) {
         // No logits wanted: only the tap of the last pass, if any.
-        if (PRO != kProResolve || blockIdx.x != 0 || rec->tap == nullptr) return;
+        if (!RES || blockIdx.x != 0 || rec->tap == nullptr) return;
         resolve_row(rs, a.row, K, xs, red, true, rec);
         return;
     }
@@ -101,20 +109,24 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     // the compiler can count them and wait for exactly these below.
     float ph[EPT], po[EPT], pa[EPT], pi[EPT];
     {
-        const float *src = (PRO == kProResolve ? rs.h : a.src) + (size_t)a.row * K;
+        const float *src = (RES ? rs.h : a.src) + (size_t)a.row * K;
 #pragma unroll
         for (int jj = 0; jj < EPT / 4; ++jj) {
             const int i = 4 * tid + 1024 * jj;
             const int ic = i < K ? i : 0;
             const float4 v = *reinterpret_cast<const float4 *>(src + ic);
             ph[4 * jj] = v.x; ph[4 * jj + 1] = v.y; ph[4 * jj + 2] = v.z; ph[4 * jj + 3] = v.w;
-            if (PRO == kProResolve) {
+            if (RES) {
                 const float4 vo = *reinterpret_cast<const float4 *>(rs.o + (size_t)a.row * K + ic);
                 const float4 va = *reinterpret_cast<const float4 *>(rs.alpha + ic);
-                const float4 vi = *reinterpret_cast<const float4 *>(rs.inp + (size_t)a.row * K + ic);
                 po[4 * jj] = vo.x; po[4 * jj + 1] = vo.y; po[4 * jj + 2] = vo.z; po[4 * jj + 3] = vo.w;
                 pa[4 * jj] = va.x; pa[4 * jj + 1] = va.y; pa[4 * jj + 2] = va.z; pa[4 * jj + 3] = va.w;
+            }
+            if (PRO == kProResolveInp) {
+                const float4 vi = *reinterpret_cast<const float4 *>(rs.inp + (size_t)a.row * K + ic);
                 pi[4 * jj] = vi.x; pi[4 * jj + 1] = vi.y; pi[4 * jj + 2] = vi.z; pi[4 * jj + 3] = vi.w;
+            } else {
+                pi[4 * jj] = pi[4 * jj + 1] = pi[4 * jj + 2] = pi[4 * jj + 3] = 0.f;
             }
         }
     }
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
 
     // 3. x in LDS.
-    if (PRO == kProResolve) {
+    if (RES) {
 #pragma unroll
         for (int jj = 0; jj < EPT / 4; ++jj)
             if (4 * tid + 1024 * jj >= K)
@@ -215,27 +227,37 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
 }
 
-template <int WT, int PRO, int EPI>
-hipError_t launch_c(const GemvArgs &a, hipStream_t s) {
+template <int WT, int PRO, int EPI, int ROWS>
+hipError_t launch_r(const GemvArgs &a, hipStream_t s) {
     const int nch = (a.K + 511) / 512;
     const int maxc = (nch + 3) / 4;
     dim3 grid((a.N + ROWS - 1) / ROWS), block(256);
     const size_t lds = sizeof(float) * (a.K + 8 + 4 * 2 * ROWS);
     switch (maxc) {
-        case 1: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 1>), grid, block, lds, s, a); break;
-        case 2: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 2>), grid, block, lds, s, a); break;
-        case 3: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 3>), grid, block, lds, s, a); break;
-        case 4: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 4>), grid, block, lds, s, a); break;
+        case 1: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 1, ROWS>), grid, block, lds, s, a); break;
+        case 2: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 2, ROWS>), grid, block, lds, s, a); break;
+        case 3: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 3, ROWS>), grid, block, lds, s, a); break;
+        case 4: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 4, ROWS>), grid, block, lds, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+// Rows per workgroup: enough workgroups to cover the chip twice, no more.
+template <int WT, int PRO, int EPI>
+hipError_t launch_c(const GemvArgs &a, hipStream_t s) {
+    if (a.N >= 16 * 1024) return launch_r<WT, PRO, EPI, 16>(a, s);
+    if (a.N >= 8 * 512) return launch_r<WT, PRO, EPI, 8>(a, s);
+    return launch_r<WT, PRO, EPI, 4>(a, s);
+}
+
 template <int WT>
 hipError_t launch_w(int pro, int epi, const GemvArgs &a, hipStream_t s) {
     if (pro == kProResolve && epi == kEpiStore) return launch_c<WT, kProResolve, kEpiStore>(a, s);
+    if (pro == kProResolveInp && epi == kEpiStore) return launch_c<WT, kProResolveInp, kEpiStore>(a, s);
     if (pro == kProNorm && epi == kEpiStore) return launch_c<WT, kProNorm, kEpiStore>(a, s);
     if (pro == kProResolve && epi == kEpiPair) return launch_c<WT, kProResolve, kEpiPair>(a, s);
+    if (pro == kProResolveInp && epi == kEpiPair) return launch_c<WT, kProResolveInp, kEpiPair>(a, s);
     if (pro == kProResolve && epi == kEpiHead) return launch_c<WT, kProResolve, kEpiHead>(a, s);
     if (pro == kProPlain && epi == kEpiHead) return launch_c<WT, kProPlain, kEpiHead>(a, s);
     return hipErrorInvalidValue;

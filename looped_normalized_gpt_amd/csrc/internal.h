@@ -64,7 +64,7 @@ enum WType { kF32 = 0, kBF16 = 1 };
 
 // ---------------------------------------------------------------- launchers
 // GEMV for one row (decode).  Prologue builds x in LDS, epilogue stores.
-enum GemvPro { kProPlain = 0, kProNorm = 1, kProResolve = 2 };
+enum GemvPro { kProPlain = 0, kProNorm = 1, kProResolve = 2, kProResolveInp = 3 };  // Inp: the loop's next pass reads the input
 enum GemvEpi { kEpiStore = 0, kEpiPair = 1, kEpiHead = 2 };
 
 struct GemvArgs {
