@@ -2,9 +2,12 @@
 // (dory.rs `attn_layer` / `mlp_layer`, the matmat branches), A fp32 [T][K]
 // activations, W [N][K] weights in bf16 or fp32, fp32 accumulation.
 //
-// This is the portable tiled form: 64x64 output tiles, K in steps of 16 staged
-// through LDS, 4x4 outputs per thread.  It keeps fp32 activations, so it also
-// serves the fp32-weight geometries exactly.
+// Two forms:
+//  * k_gemm_mfma (bf16 weights): v_mfma_f32_32x32x16_bf16 on 128 x BN tiles,
+//    K in steps of 32 through double-buffered LDS; activations are rounded to
+//    bf16 as they are staged (the prefill chunks are dense contractions).
+//  * k_gemm_tiled: 64x64 fp32 FMA tiles that keep fp32 activations; it serves
+//    the fp32-weight geometries exactly, and short chunks.
 #include "device.h"
 
 namespace dk {
@@ -75,11 +78,125 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const float *__restrict__ A,
     }
 }
 
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 256 threads = 4 waves in a 2 x 2 arrangement; a wave owns a (BM/2) x (BN/2)
+// block of C as 32x32 MFMA tiles.  Operand layout of the 32x32x16 bf16 MFMA:
+// lane l supplies row (l % 32) and k = 8 (l / 32) .. +7 of A (and of B); it
+// receives C[8 (j/4) + 4 (l/32) + j%4][l % 32] in accumulator j.
+template <int BN>
+__global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, int lda,
+                                                   const uint16_t *__restrict__ W, int N, int K,
+                                                   float *__restrict__ C, int ldc, int M) {
+    constexpr int BM = 128, BK = 32, LDK = BK + 8;  // padded LDS rows (bf16)
+    constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32; // MFMA tiles per wave
+    __shared__ __bf16 As[2][BM][LDK];
+    __shared__ __bf16 Bs[2][BN][LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    // loaders: A rows tid/2 (128 rows), 16 floats each; B rows tid/2 (< BN), 16 bf16 each
+    const int lr = tid >> 1, lc = (tid & 1) * 16;
+    float4 ra[4];
+    uint4 rb[2];
+    auto gload = [&](int k0) {
+        const int m = m0 + lr, k = k0 + lc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = m < M && k + 4 * i < K;
+            ra[i] = ok ? *reinterpret_cast<const float4 *>(A + (size_t)m * lda + k + 4 * i)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        const int n = n0 + lr;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bool ok = lr < BN && n < N && k + 8 * i < K;
+            rb[i] = ok ? *reinterpret_cast<const uint4 *>(W + (size_t)n * K + k + 8 * i) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto sstore = [&](int buf) {
+        bf16x8 v0, v1;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            v0[4 * i + 0] = (__bf16)ra[i].x; v0[4 * i + 1] = (__bf16)ra[i].y;
+            v0[4 * i + 2] = (__bf16)ra[i].z; v0[4 * i + 3] = (__bf16)ra[i].w;
+            v1[4 * i + 0] = (__bf16)ra[2 + i].x; v1[4 * i + 1] = (__bf16)ra[2 + i].y;
+            v1[4 * i + 2] = (__bf16)ra[2 + i].z; v1[4 * i + 3] = (__bf16)ra[2 + i].w;
+        }
+        *reinterpret_cast<bf16x8 *>(&As[buf][lr][lc]) = v0;
+        *reinterpret_cast<bf16x8 *>(&As[buf][lr][lc + 8]) = v1;
+        if (lr < BN) {
+            *reinterpret_cast<uint4 *>(&Bs[buf][lr][lc]) = rb[0];
+            *reinterpret_cast<uint4 *>(&Bs[buf][lr][lc + 8]) = rb[1];
+        }
+    };
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        const bool more = k0 + BK < K;
+        if (more) gload(k0 + BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            bf16x8 a[TM], b[TN];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                a[i] = *reinterpret_cast<const bf16x8 *>(&As[buf][wm * (BM / 2) + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[buf][wn * (BN / 2) + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+        if (more) {
+            sstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int col = n0 + wn * (BN / 2) + j * 32 + (lane & 31);
+            if (col >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * (BM / 2) + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (row < M) C[(size_t)row * ldc + col] = acc[i][j][e];
+            }
+        }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int wtype, const float *A, int lda, const void *W, int N, int K, float *C, int ldc,
                        int M, hipStream_t s) {
     if (K % 4 || lda % 4) return hipErrorInvalidValue;
+    if (wtype == kBF16 && M >= 32 && K % 8 == 0) {
+        // bf16 MFMA; narrower tiles when the 128-wide ones would leave CUs idle
+        const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W);
+        const int mt = (M + 127) / 128;
+        if ((long)mt * ((N + 127) / 128) >= 256) {
+            hipLaunchKernelGGL((k_gemm_mfma<128>), dim3((N + 127) / 128, mt), dim3(256), 0, s, A, lda, Wb, N, K, C, ldc, M);
+        } else {
+            hipLaunchKernelGGL((k_gemm_mfma<64>), dim3((N + 63) / 64, mt), dim3(256), 0, s, A, lda, Wb, N, K, C, ldc, M);
+        }
+        return hipGetLastError();
+    }
     dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
     if (wtype == kBF16) hipLaunchKernelGGL((k_gemm_tiled<kBF16>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);
     else hipLaunchKernelGGL((k_gemm_tiled<kF32>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);
