@@ -122,6 +122,17 @@ const char *dory_last_error(const dory_t *h);
 int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
                        int32_t loops, int32_t kv_mode, dory_stream_t stream, float *logits);
 
+/* One decode step of nseq sequences at once: row i is the next token of
+ * sequence seqs[i] (distinct, 0 <= seqs[i] < max_seqs), run with loops[i] passes
+ * of the recurrent block (1..16; per_loop sequences need their fixed count).
+ * Rows with fewer loops leave the recurrent block early; the weights are read
+ * once per pass for all rows that still run it (dory.rs `stack` for each row).
+ * nseq <= max_chunk.  tokens, seqs, loops: host int32 [nseq].  logits: device
+ * fp32 [nseq][vocab] (row i for seqs[i]) or NULL.  Checks as dory_forward_chunk,
+ * for every row, before any work.  Asynchronous on stream. */
+int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32_t *tokens,
+                       const int32_t *loops, int32_t kv_mode, dory_stream_t stream, float *logits);
+
 /* A new sequence (dory.rs `DoryState::clear`, kv_cache.rs `clear`): position 0,
  * kv mode and loop count free again, q8 fields unfrozen.  seq == -1: all. */
 int dory_kv_reset(dory_t *h, int32_t seq);

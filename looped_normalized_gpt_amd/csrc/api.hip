@@ -57,6 +57,7 @@ struct dory {
     float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
     float *z = nullptr, *zn = nullptr, *ga = nullptr, *gb = nullptr, *un = nullptr, *kstage = nullptr;
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
+    float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
     std::vector<SlotDesc> tab_host;
@@ -203,10 +204,15 @@ int ensure_slots(dory_t *h, int seq, int mode, int loops) {
 struct Enq {
     dory_t *h;
     hipStream_t s;
-    int T, loops, mode;
-    int64_t pos0;      // host copy, for the q8 freeze decisions
-    bool want_logits;  // head GEMV for a multi-row call
-    std::vector<uint8_t> froze;  // slots frozen by this call: [n_ord][kMaxLoops]
+    int T;                       // rows of the call
+    int loops;                   // loops of its longest row
+    int mode;
+    bool batch;                  // one decode row of each of T sequences
+    bool want_logits;
+    std::vector<int> act;        // rows that run loop i (a prefix: rows are sorted by loops)
+    std::vector<int64_t> pos;    // every row's position (host copy, for the q8 freeze)
+    std::vector<int> seq;        // every row's sequence
+    std::vector<uint8_t> froze;  // slots whose field this call froze: [max_seqs][n_ord][kMaxLoops]
 };
 
 #define LAUNCH(call)                                            \
@@ -215,24 +221,28 @@ struct Enq {
         if (e_ != hipSuccess) return hip_fail(q.h, e_, #call);  \
     } while (0)
 
-int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const float *x) {
+uint8_t &froze_at(Enq &q, int seq, int ord, int slot) {
+    return q.froze[((size_t)seq * q.h->n_ord + ord) * kMaxLoops + slot];
+}
+
+// One attention sub-layer over the first M rows of the call.
+int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const float *x, int M) {
     dory_t *h = q.h;
-    const int T = q.T, ld = 2 * h->Q + 2 * h->KV;
+    const int ld = 2 * h->Q + 2 * h->KV;
     const int slot = slot_of(h, l, q.mode, loop_i);
     const dory_layer_weights &w = l.w;
-    if (T == 1) {
+    if (q.T == 1) {
         GemvArgs a{};
         a.w[0] = w.wq; a.w[1] = w.wk; a.w[2] = w.wv; a.w[3] = w.wg;
         a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
         a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wq, h->Q, h->H, h->qkvg, ld, T, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wk, h->KV, h->H, h->qkvg + h->Q, ld, T, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wv, h->KV, h->H, h->qkvg + h->Q + h->KV, ld, T, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wg, h->Q, h->H, h->qkvg + h->Q + 2 * h->KV, ld, T, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wq, h->Q, h->H, h->qkvg, ld, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wk, h->KV, h->H, h->qkvg + h->Q, ld, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wv, h->KV, h->H, h->qkvg + h->Q + h->KV, ld, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wg, h->Q, h->H, h->qkvg + h->Q + 2 * h->KV, ld, M, q.s));
     }
-    const bool freeze_now = h->q8 && q.pos0 <= kWarmup && q.pos0 + T > kWarmup;
     AttnArgs aa{};
     aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part;
     aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l.ord; aa.slot = slot;
@@ -240,69 +250,80 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
     aa.window = l.sliding ? h->win_s : h->win_f;
     aa.q8 = h->q8; aa.rec = h->rec;
     aa.rope = l.sliding ? h->rope_s : h->rope_f; aa.sq = w.sq;
-    if (T == 1 && !freeze_now) {
-        // one row: prep and the cache write are fused into the attention kernel
+    if (q.T == 1 || q.batch) {
+        // One new row per sequence: prep and the cache write are fused into the
+        // decode attention kernel.  kv_cache.rs `append`: a slot's field freezes
+        // as its row of position 64 is appended, before that row is encoded.
+        if (h->q8)
+            for (int r = 0; r < M; ++r) {
+                uint8_t &fz = froze_at(q, q.seq[r], l.ord, slot);
+                if (q.pos[r] == kWarmup && !fz) {
+                    LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, r, q.s));
+                    fz = 1;
+                }
+            }
         aa.split = l.sliding ? h->split_ds : h->split_df;
         aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
-        aa.field = h->q8 && q.pos0 >= kWarmup + 1;
-        LAUNCH(launch_attn_dec(aa, q.s));
+        aa.field = -1;
+        LAUNCH(launch_attn_dec(aa, M, q.s));
     } else {
+        // A chunk of one sequence: rows pos0 .. pos0+M-1.
+        const int64_t pos0 = q.pos[0];
         PrepArgs pa{};
         pa.qkvg = h->qkvg; pa.qp = h->qp; pa.kstage = h->q8 ? h->kstage : nullptr;
         pa.rope = l.sliding ? h->rope_s : h->rope_f; pa.sq = w.sq; pa.tab = h->tab;
         pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = h->rec;
-        LAUNCH(launch_prep(pa, T, q.s));
+        LAUNCH(launch_prep(pa, M, q.s));
         bool field = false;
         if (h->q8) {
             // kv_cache.rs `append`: the field freezes when the 65th row (position 64)
             // is appended; rows before it were encoded without a field, rows after
             // against it.  A later loop's rewrite of the same rows finds it frozen.
-            uint8_t &froze = q.froze[l.ord * kMaxLoops + slot];
-            const bool frozen = q.pos0 >= kWarmup + 1 || froze;
+            uint8_t &fz = froze_at(q, q.seq[0], l.ord, slot);
+            const bool frozen = pos0 >= kWarmup + 1 || fz;
             Q8WriteArgs wa{};
             wa.ksrc = h->kstage; wa.kld = h->KV; wa.vsrc = h->qkvg + h->Q + h->KV; wa.vld = ld;
             wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = slot; wa.nk = h->nk; wa.hd = h->hd;
             wa.rec = h->rec;
             if (frozen) {
-                wa.r0 = 0; wa.r1 = T; wa.field = 1;
+                wa.r0 = 0; wa.r1 = M; wa.field = 1;
                 LAUNCH(launch_q8_write(wa, q.s));
-            } else if (q.pos0 + T <= kWarmup) {
-                wa.r0 = 0; wa.r1 = T; wa.field = 0;
+            } else if (pos0 + M <= kWarmup) {
+                wa.r0 = 0; wa.r1 = M; wa.field = 0;
                 LAUNCH(launch_q8_write(wa, q.s));
             } else {
-                const int split = (int)(kWarmup - q.pos0);
+                const int split = (int)(kWarmup - pos0);
                 wa.r0 = 0; wa.r1 = split; wa.field = 0;
                 LAUNCH(launch_q8_write(wa, q.s));
-                LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, q.s));
-                wa.r0 = split; wa.r1 = T; wa.field = 1;
+                LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, 0, q.s));
+                wa.r0 = split; wa.r1 = M; wa.field = 1;
                 LAUNCH(launch_q8_write(wa, q.s));
-                froze = 1;
+                fz = 1;
             }
-            field = q.pos0 >= kWarmup + 1 || froze;
+            field = pos0 >= kWarmup + 1 || fz;
         }
         aa.split = h->split_pf;
         aa.max_split = h->ms_pf;
         aa.field = field;
-        LAUNCH(launch_attn(aa, T, q.s));
-
+        LAUNCH(launch_attn(aa, M, q.s));
     }
-    if (T == 1) {
+    if (q.T == 1) {
         GemvArgs a{};
         a.w[0] = w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.row = 0;
         a.src = h->z; a.y = h->o; a.rec = h->rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->Q, T, q.s));
-        LAUNCH(launch_gemm(h->wt, h->zn, h->Q, w.wo, h->H, h->Q, h->o, h->H, T, q.s));
+        LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->Q, M, q.s));
+        LAUNCH(launch_gemm(h->wt, h->zn, h->Q, w.wo, h->H, h->Q, h->o, h->H, M, q.s));
     }
     return DORY_OK;
 }
 
-int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x) {
+// One MLP sub-layer over the first M rows of the call.
+int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M) {
     dory_t *h = q.h;
-    const int T = q.T;
     const dory_layer_weights &w = l.w;
-    if (T == 1) {
+    if (q.T == 1) {
         GemvArgs a{};
         a.w[0] = w.wgate; a.w[1] = w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H; a.row = 0;
         a.rs = rs; a.y = h->ga; a.sg = w.sg; a.su = w.su; a.rec = h->rec; a.hidden = h->H;
@@ -312,25 +333,29 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x) {
         d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wgate, h->F, h->H, h->ga, h->F, T, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wup, h->F, h->H, h->gb, h->F, T, q.s));
-        LAUNCH(launch_swiglu_norm(h->ga, h->gb, w.sg, w.su, h->un, h->F, T, q.s));
-        LAUNCH(launch_gemm(h->wt, h->un, h->F, w.wdown, h->H, h->F, h->o, h->H, T, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wgate, h->F, h->H, h->ga, h->F, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, w.wup, h->F, h->H, h->gb, h->F, M, q.s));
+        LAUNCH(launch_swiglu_norm(h->ga, h->gb, w.sg, w.su, h->un, h->F, M, q.s));
+        LAUNCH(launch_gemm(h->wt, h->un, h->F, w.wdown, h->H, h->F, h->o, h->H, M, q.s));
     }
     return DORY_OK;
 }
 
-// dory.rs `stack` and `head`: embedding, input block, `loops` passes of the
-// recurrent block with the loop mix, output block, head.  Sub-layer pass k
-// reads its x from hb[k % 2]; the step between passes k-1 and k (slerp, loop
-// mix) is fused into pass k's first kernel for one-row calls and is its own
-// row kernel otherwise.
+// dory.rs `stack` and `head`: embedding, input block, the recurrent block's
+// loops with the loop mix, output block, head.  Sub-layer pass k reads its x
+// from hb[k % 2]; the step between passes k-1 and k (slerp, loop mix) is fused
+// into pass k's first kernel for one-row calls and is its own row kernel
+// otherwise.  In a batch, loop i runs the first act[i] rows.
 int enqueue(Enq &q) {
     dory_t *h = q.h;
     const dory_config &c = h->cfg;
     const int T = q.T;
     LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], q.s));
     const int P = passes(h, q.loops);
+    auto rows_of = [&](int k) {
+        if (k < c.n_in || k >= c.n_in + c.n_rec * q.loops) return T;
+        return q.act[(k - c.n_in) / c.n_rec];
+    };
     int prev_li = -1;
     for (int k = 0; k < P; ++k) {
         int li, loop_i = 0, op = kLoopNone;
@@ -346,28 +371,33 @@ int enqueue(Enq &q) {
             li = c.n_in + c.n_rec + j;
             if (j == 0) op = kLoopExit;
         }
+        const int M = rows_of(k);
         Resolve rs{};
         rs.inp = h->inp;
         rs.loop_op = op;
+        rs.st = q.batch ? h->st : nullptr;
+        rs.n_next = M;
         if (k == 0) {
             // the first pass takes the embedding as it is; o and alpha only need
             // to be valid addresses (the GEMV prologue loads them unconditionally)
             rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0; rs.h_out = nullptr;
             rs.tap_pass = -1;
+            rs.n_prev = T;
         } else {
             rs.h = h->hb[(k - 1) % 2]; rs.o = h->o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
             rs.h_out = h->hb[k % 2]; rs.tap_pass = k - 1;
-            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, T, h->rec, q.s));
+            rs.n_prev = rows_of(k - 1);
+            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, h->rec, q.s));
         }
         const LayerInfo &l = h->L[li];
         const float *x = h->hb[k % 2];
-        int rc = l.attn ? enq_attn(q, l, loop_i, rs, x) : enq_mlp(q, l, rs, x);
+        int rc = l.attn ? enq_attn(q, l, loop_i, rs, x, M) : enq_mlp(q, l, rs, x, M);
         if (rc) return rc;
         prev_li = li;
     }
     Resolve rf{};
     rf.h = h->hb[(P - 1) % 2]; rf.o = h->o; rf.alpha = h->L[prev_li].w.alpha; rf.slerp = 1;
-    rf.loop_op = kLoopNone; rf.inp = h->inp; rf.tap_pass = P - 1;
+    rf.loop_op = kLoopNone; rf.inp = h->inp; rf.tap_pass = P - 1; rf.n_prev = rf.n_next = T;
     GemvArgs a{};
     a.w[0] = h->w.head; a.seg_end[0] = h->V; a.nseg = 1; a.N = h->V; a.K = h->H;
     a.logit_scale = h->w.logit_scale; a.rec = h->rec; a.hidden = h->H;
@@ -378,30 +408,50 @@ int enqueue(Enq &q) {
     } else {
         rf.h_out = h->hb[P % 2];
         LAUNCH(launch_resolve_rows(rf, h->H, T, h->rec, q.s));
-        if (q.want_logits) {
+        if (q.want_logits && !q.batch) {
             a.row = T - 1; a.src = h->hb[P % 2];
             LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));
+        } else if (q.want_logits) {
+            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->H, h->w.head, h->V, h->H, h->hlog, h->V, T, q.s));
+            LAUNCH(launch_logits_rows(h->hlog, h->w.logit_scale, h->V, T, h->rec, q.s));
         }
     }
     return DORY_OK;
 }
 
 // Copies a call record to the device on stream s (pinned staging ring).
-int put_record(dory_t *h, int seq, int64_t pos0, int n, const int32_t *tokens, float *logits, hipStream_t s) {
+int put_record(dory_t *h, const std::vector<RowRec> &rows, float *logits, hipStream_t s) {
     const int i = h->stage_i;
     h->stage_i = (i + 1) % kStages;
     if (h->stage_used[i]) HIPCHECK(h, hipEventSynchronize(h->stage_ev[i]));
     CallRec *r = reinterpret_cast<CallRec *>(h->stage + (size_t)i * h->rec_sz);
-    r->pos0 = pos0;
-    r->n = n;
-    r->seq = seq;
+    r->n = (int32_t)rows.size();
     r->logits = logits;
     r->tap = h->tap;
-    if (tokens) memcpy(r->tokens, tokens, sizeof(int32_t) * n);
-    HIPCHECK(h, hipMemcpyAsync(h->rec, r, h->rec_sz, hipMemcpyHostToDevice, s));
+    memcpy(r->rows, rows.data(), sizeof(RowRec) * rows.size());
+    HIPCHECK(h, hipMemcpyAsync(h->rec, r, rec_used((int)rows.size()), hipMemcpyHostToDevice, s));
     HIPCHECK(h, hipEventRecord(h->stage_ev[i], s));
     h->stage_used[i] = true;
     return DORY_OK;
+}
+
+// Rows of a chunk of one sequence: positions pos0.., logits (if any) of the last.
+std::vector<RowRec> chunk_rows(int seq, int64_t pos0, int n, const int32_t *tokens) {
+    std::vector<RowRec> rows(n);
+    for (int r = 0; r < n; ++r) rows[r] = RowRec{pos0 + r, seq, tokens ? tokens[r] : 0, 0, 0};
+    return rows;
+}
+
+Enq make_enq(dory_t *h, hipStream_t s, int T, int loops, int mode, bool batch, bool want_logits,
+             const std::vector<RowRec> &rows) {
+    Enq q{h, s, T, loops, mode, batch, want_logits, {}, {}, {}, {}};
+    q.act.assign(loops, T);
+    for (const RowRec &r : rows) {
+        q.pos.push_back(r.pos);
+        q.seq.push_back(r.seq);
+    }
+    q.froze.assign((size_t)h->cfg.max_seqs * h->n_ord * kMaxLoops, 0);
+    return q;
 }
 
 }  // namespace
@@ -470,7 +520,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     }
     h->seqs.resize(cfg->max_seqs);
     h->tab_host.assign((size_t)cfg->max_seqs * std::max(h->n_ord, 1) * kMaxLoops, SlotDesc{});
-    h->rec_sz = rec_bytes(chunk);
+    h->rec_sz = rec_bytes(std::max(chunk, cfg->max_seqs));
 
     auto bail = [&](int code) {
         g_create_error = h->err;
@@ -499,8 +549,12 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_v, (size_t)chunk * h->KV));
+    CREATE_CHECK(dmalloc(h, &h->st, TH));
+    CREATE_CHECK(dmalloc(h, &h->hlog, (size_t)std::min(chunk, cfg->max_seqs) * h->V));
     const size_t rep = h->nh / h->nk;
-    const size_t part = std::max((size_t)h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2);
+    // decode rows (one per sequence of a batch) or the rows of a chunk
+    const size_t dec_rows = std::min(chunk, cfg->max_seqs);
+    const size_t part = std::max(dec_rows * h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2);
     CREATE_CHECK(dmalloc(h, &h->part, part));
     CREATE_CHECK(dmalloc(h, &h->tab, h->tab_host.size()));
     CREATE_CHECK(hipMemset(h->tab, 0, sizeof(SlotDesc) * h->tab_host.size()));
@@ -573,9 +627,10 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     int rc = ensure_slots(h, seq, kv_mode, loops);
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    rc = put_record(h, seq, st.pos, n, tokens, logits, s);
+    const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens);
+    rc = put_record(h, rows, logits, s);
     if (rc) return rc;
-    Enq q{h, s, n, loops, kv_mode, st.pos, logits != nullptr, std::vector<uint8_t>((size_t)h->n_ord * kMaxLoops, 0)};
+    Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
     const bool graphable = n == 1 && (!h->q8 || st.pos >= kWarmup + 1);
     if (graphable) {
         auto key = std::make_tuple(loops, kv_mode);
@@ -609,6 +664,70 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     if (n == 1 && seq == 0) {
         h->last_loops = loops;
         h->last_mode = kv_mode;
+    }
+    return DORY_OK;
+}
+
+int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32_t *tokens, const int32_t *loops,
+                       int32_t kv_mode, dory_stream_t stream, float *logits) {
+    if (!h) return DORY_EINVAL;
+    const dory_config &c = h->cfg;
+    if (!seqs || !tokens || !loops || nseq < 1) return fail(h, DORY_EINVAL, "dory_forward_batch: need nseq >= 1 rows");
+    if (nseq > c.max_chunk || nseq > c.max_seqs) return fail(h, DORY_ERANGE, "dory_forward_batch: nseq > max_chunk or max_seqs");
+    if (kv_mode != DORY_PER_LOOP && kv_mode != DORY_LAST_LOOP)
+        return fail(h, DORY_EINVAL, "dory_forward_batch: kv_mode must be per_loop or last_loop");
+    std::vector<uint8_t> seen(c.max_seqs, 0);
+    for (int i = 0; i < nseq; ++i) {
+        const int sq = seqs[i];
+        if (sq < 0 || sq >= c.max_seqs) return fail(h, DORY_EINVAL, "dory_forward_batch: seq out of range");
+        if (seen[sq]) return fail(h, DORY_EINVAL, "dory_forward_batch: a sequence appears twice");
+        seen[sq] = 1;
+        if (loops[i] < 1 || loops[i] > DORY_MAX_LOOPS) return fail(h, DORY_EINVAL, "dory_forward_batch: loops must be in 1..16");
+        const SeqState &st = h->seqs[sq];
+        if (st.mode >= 0 && st.mode != kv_mode)
+            return fail(h, DORY_ESTATE, "dory_forward_batch: kv mode changed without dory_kv_reset");
+        if (kv_mode == DORY_PER_LOOP && st.loops > 0 && st.loops != loops[i])
+            return fail(h, DORY_ESTATE, "dory_forward_batch: per_loop needs the same loop count on every call");
+        if (st.pos + 1 > c.max_ctx) return fail(h, DORY_ERANGE, "dory_forward_batch: position past max_ctx");
+    }
+    if (h->tap) {
+        int lmax = 0;
+        for (int i = 0; i < nseq; ++i) lmax = std::max(lmax, (int)loops[i]);
+        if ((int64_t)passes(h, lmax) * nseq * h->H > h->tap_cap)
+            return fail(h, DORY_EINVAL, "dory_forward_batch: the tap buffer is too small for this call");
+    }
+    if (nseq == 1) return dory_forward_chunk(h, seqs[0], tokens, 1, loops[0], kv_mode, stream, logits);
+    HIPCHECK(h, hipSetDevice(h->device));
+    for (int i = 0; i < nseq; ++i) {
+        int rc = ensure_slots(h, seqs[i], kv_mode, loops[i]);
+        if (rc) return rc;
+    }
+    // rows sorted by loops, longest first: the rows of loop i are a prefix
+    std::vector<int> order(nseq);
+    for (int i = 0; i < nseq; ++i) order[i] = i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return loops[a] > loops[b]; });
+    std::vector<RowRec> rows(nseq);
+    for (int r = 0; r < nseq; ++r) {
+        const int i = order[r];
+        rows[r] = RowRec{h->seqs[seqs[i]].pos, seqs[i], tokens[i], i, 0};
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int rc = put_record(h, rows, logits, s);
+    if (rc) return rc;
+    const int lmax = loops[order[0]];
+    Enq q = make_enq(h, s, nseq, lmax, kv_mode, true, logits != nullptr, rows);
+    for (int i = 0; i < lmax; ++i) {
+        int a = 0;
+        while (a < nseq && loops[order[a]] > i) ++a;
+        q.act[i] = a;
+    }
+    rc = enqueue(q);
+    if (rc) return rc;
+    for (int i = 0; i < nseq; ++i) {
+        SeqState &st = h->seqs[seqs[i]];
+        st.pos += 1;
+        st.mode = kv_mode;
+        if (kv_mode == DORY_PER_LOOP) st.loops = loops[i];
     }
     return DORY_OK;
 }
@@ -714,7 +833,7 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
             bool froze = false;
             for (int64_t p0 = 0; p0 < npos; p0 += chunk) {
                 const int T = (int)std::min<int64_t>(chunk, npos - p0);
-                rc = put_record(h, seq, p0, T, nullptr, nullptr, nullptr);
+                rc = put_record(h, chunk_rows(seq, p0, T, nullptr), nullptr, nullptr);
                 if (rc) return rc;
                 HIPCHECK(h, hipMemcpy(h->ld_k, kb + p0 * row, sizeof(float) * T * row, hipMemcpyHostToDevice));
                 HIPCHECK(h, hipMemcpy(h->ld_v, vb + p0 * row, sizeof(float) * T * row, hipMemcpyHostToDevice));
@@ -734,7 +853,7 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
                         const int split = (int)(kWarmup - p0);
                         wa.r0 = 0; wa.r1 = split; wa.field = 0;
                         HIPCHECK(h, launch_q8_write(wa, nullptr));
-                        HIPCHECK(h, launch_q8_freeze(h->tab, h->n_ord, l.ord, s, h->nk, h->hd, h->rec, nullptr));
+                        HIPCHECK(h, launch_q8_freeze(h->tab, h->n_ord, l.ord, s, h->nk, h->hd, h->rec, 0, nullptr));
                         wa.r0 = split; wa.r1 = T; wa.field = 1;
                         HIPCHECK(h, launch_q8_write(wa, nullptr));
                         froze = true;
@@ -787,8 +906,8 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             aa.split = l->sliding ? h->split_ds : h->split_df;
             aa.max_split = l->sliding ? h->ms_ds : h->ms_df;
             aa.rope = l->sliding ? h->rope_s : h->rope_f; aa.sq = l->w.sq; aa.no_write = 1;
-            aa.q8 = h->q8; aa.field = h->q8 && h->seqs[0].pos >= kWarmup + 1; aa.rec = h->rec;
-            e = launch_attn_dec(aa, s);
+            aa.q8 = h->q8; aa.field = -1; aa.rec = h->rec;
+            e = launch_attn_dec(aa, 1, s);
         } else if (stage == 2) {
             a.w[0] = l->w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.src = h->z; a.y = h->o;
             e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);

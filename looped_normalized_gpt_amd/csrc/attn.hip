@@ -14,7 +14,7 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
     const int r = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
     const int hd = a.hd, half = hd / 2, Q = a.nh * hd, KV = a.nk * hd;
     const int ld = Q + 2 * KV + Q;
-    const int64_t p = a.rec->pos0 + r;
+    const int64_t p = a.rec->rows[r].pos;
     const bool isq = hh < a.nh;
     const int kh = hh - a.nh;
     const float *src = a.qkvg + (size_t)r * ld + (isq ? hh * hd : Q + kh * hd);
@@ -58,7 +58,7 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
         }
         return;
     }
-    const SlotDesc &sd = slot_at(a.tab, a.rec->seq, a.n_ord, a.ord, a.slot);
+    const SlotDesc &sd = slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot);
     const size_t row = (size_t)kh * sd.cap + (size_t)(p % sd.cap);
     float *kd = sd.k + row * hd;
 #pragma unroll
@@ -95,9 +95,10 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
     // what does not depend on the partials first
     const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + dc];
     const float sgv = a.sg[hq * hd + dc];
+    const int64_t p = a.rec->rows[r].pos;
     float vcol = 1.f;
-    if (Q8 && a.field) vcol = slot_at(a.tab, a.rec->seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + dc];
-    const int64_t p = a.rec->pos0 + r;
+    if (Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup)))
+        vcol = slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + dc];
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
     const size_t pstride = (size_t)rep * (hd + 2);
@@ -165,14 +166,14 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const CallRec *rec = a.rec;
-    const int64_t p = rec->pos0 + r;
+    const int64_t p = rec->rows[r].pos;
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int64_t nkeys = p - lo + 1;
     const int nsplit = (int)((nkeys + a.split - 1) / a.split);
     if (s >= nsplit) return;
     const int64_t e0 = lo + (int64_t)s * a.split;
     const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
-    const SlotDesc &sd = slot_at(a.tab, rec->seq, a.n_ord, a.ord, a.slot);
+    const SlotDesc &sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
     const int cap = sd.cap;
     const int Q = a.nh * HD;
     const float scale = 1.0f / sqrtf((float)HD);
@@ -313,10 +314,10 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     __shared__ int8_t kcn[HD], vcn[HD];
     __shared__ float ksn[NGK], vsn[1];
     __shared__ float stat[2][REP];
-    const int s = blockIdx.x, kh = blockIdx.y;
+    const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const CallRec *rec = a.rec;
-    const int64_t p = rec->pos0;
+    const int64_t p = rec->rows[r].pos;
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int64_t nkeys = p - lo + 1;
     const int nsplit = (int)((nkeys + a.split - 1) / a.split);
@@ -324,23 +325,25 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     const int64_t e0 = lo + (int64_t)s * a.split;
     const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
     const bool tail = s == nsplit - 1;
-    const SlotDesc &sd = slot_at(a.tab, rec->seq, a.n_ord, a.ord, a.slot);
+    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    const SlotDesc &sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
     const int cap = sd.cap;
     const int Q = a.nh * HD, KV = a.nk * HD;
     const int g = tid / LPK, dq = tid % LPK;
     const float scale = 1.0f / sqrtf((float)HD);
 
     // ---- 0. the prep's inputs (unconditional loads at clamped indices)
+    const float *qrow = a.qkvg + (size_t)r * (2 * Q + 2 * KV);
     float qv[QPT], sv[QPT];
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
         const int idx = tid + 256 * i < REP * HD ? tid + 256 * i : 0;
-        qv[i] = a.qkvg[(size_t)kh * REP * HD + idx];
+        qv[i] = qrow[(size_t)kh * REP * HD + idx];
         sv[i] = a.sq[(size_t)kh * REP * HD + idx];
     }
     const int td = tid < HD ? tid : 0;
-    const float kraw = a.qkvg[Q + (size_t)kh * HD + td];
-    const float vraw = a.qkvg[Q + KV + (size_t)kh * HD + td];
+    const float kraw = qrow[Q + (size_t)kh * HD + td];
+    const float vraw = qrow[Q + KV + (size_t)kh * HD + td];
     const float rv = a.rope[(size_t)p * HD + td];
 
     // ---- 1. every K and V row of the split, in flight at once
@@ -400,8 +403,8 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     if (tail) {
         const size_t row = (size_t)kh * cap + (size_t)(p % cap);
         if (Q8) {
-            if (wave == 0) encode_row(qs[REP], a.field ? sd.kcol + kh * HD : nullptr, HD, kKGroup, kcn, ksn);
-            if (wave == 1) encode_row(vn, a.field ? sd.vcol + kh * HD : nullptr, HD, HD, vcn, vsn);
+            if (wave == 0) encode_row(qs[REP], field ? sd.kcol + kh * HD : nullptr, HD, kKGroup, kcn, ksn);
+            if (wave == 1) encode_row(vn, field ? sd.vcol + kh * HD : nullptr, HD, HD, vcn, vsn);
             __syncthreads();
             if (!a.no_write) {
             for (int d = tid; d < HD; d += 256) {
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
         float4 q[REP];
 #pragma unroll
         for (int h = 0; h < REP; ++h) q[h] = *reinterpret_cast<const float4 *>(&qs[h][dq * 4]);
-        if (Q8 && a.field) {
+        if (field) {
             const float4 c = *reinterpret_cast<const float4 *>(sd.kcol + kh * HD + dq * 4);
 #pragma unroll
             for (int h = 0; h < REP; ++h) {
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     }
     __syncthreads();
     const size_t pstride = (size_t)REP * (HD + 2);
-    float *mine = a.part + ((size_t)kh * a.max_split + s) * pstride;
+    float *mine = a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride;
     for (int idx = tid; idx < REP * HD; idx += 256) {
         const int h = idx / HD, d = idx % HD;
         float v = 0.f;
@@ -522,8 +525,8 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
 
 template <int HD, int REP>
 hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
-    if (T == 0) {  // one-row decode kernel
-        dim3 grid(a.max_split, a.nk), block(256);
+    if (T < 0) {  // decode kernel: -T rows, each of its own sequence and position
+        dim3 grid(a.max_split, a.nk, -T), block(256);
         if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0>), grid, block, 0, s, a);
     } else {
@@ -535,8 +538,8 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     if (e != hipSuccess) return e;
     // one-row calls: 16 waves per head channel block; multi-row calls have
     // fewer, longer splits and many more rows, so 4
-    dim3 mgrid(T ? T : 1, a.nh, (HD + 63) / 64);
-    const int waves = T ? 4 : 16;
+    dim3 mgrid(T < 0 ? -T : T, a.nh, (HD + 63) / 64);
+    const int waves = T > 1 ? 4 : 16;
     if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(64 * waves), 0, s, a);
     else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(64 * waves), 0, s, a);
     return hipGetLastError();
@@ -582,9 +585,9 @@ int attn_dec_max_split(int hd) {
     return 8 * kb < 256 ? 8 * kb : 256;
 }
 
-hipError_t launch_attn_dec(const AttnArgs &a, hipStream_t s) {
-    if (a.split <= 0 || a.split > attn_dec_max_split(a.hd)) return hipErrorInvalidValue;
-    return launch_hd(a, 0, s);
+hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s) {
+    if (a.split <= 0 || a.split > attn_dec_max_split(a.hd) || T <= 0) return hipErrorInvalidValue;
+    return launch_hd(a, -T, s);
 }
 
 }  // namespace dk

@@ -81,6 +81,13 @@ __device__ __forceinline__ float norm_factor(float s) { return 1.0f / sqrtf(s + 
 __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, float *red, bool writer,
                                    const CallRec *rec) {
     const int tid = threadIdx.x;
+    if (rs.loop_op == kLoopExit && r >= rs.n_prev) {
+        // a batch row that stopped looping early: its state is kept in st
+        for (int i = tid; i < H; i += 256) xs[i] = rs.st[(size_t)r * H + i];
+        if (writer && rs.h_out)
+            for (int i = tid; i < H; i += 256) rs.h_out[(size_t)r * H + i] = xs[i];
+        return;
+    }
     const float *h = rs.h + (size_t)r * H;
     if (!rs.slerp) {
         for (int i = tid; i < H; i += 256) xs[i] = h[i];
@@ -131,9 +138,13 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
             if (rs.loop_op == kLoopExit) {
                 for (int i = tid; i < H; i += 256) xs[i] *= fs;
             } else {
+                for (int i = tid; i < H; i += 256) xs[i] *= fs;
+                if (writer && rs.st)
+                    for (int i = tid; i < H; i += 256) rs.st[(size_t)r * H + i] = xs[i];
+                if (r >= rs.n_next) return;  // this row's loops are over
                 float s2 = 0.f;
                 for (int i = tid; i < H; i += 256) {
-                    float x = xs[i] * fs + inp[i];
+                    float x = xs[i] + inp[i];
                     xs[i] = x;
                     s2 += x * x;
                 }

@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
                 float g = v * a.sg[n];
                 a.y[n] = g / (1.0f + expf(-g)) * (b * a.su[n]);
             } else {
-                rec->logits[n] = v * a.logit_scale[n];
+                rec->logits[(size_t)rec->rows[a.row].out * N + n] = v * a.logit_scale[n];
             }
         }
     }

@@ -11,17 +11,27 @@ constexpr int kWarmup = 64;     // kv_cache.rs `KV_COL_WARMUP`: rows before the 
 constexpr int kKGroup = 32;     // kv_cache.rs `KV_K_GROUP`: K channels per q8 scale
 constexpr float kEps = 1e-6f;   // dory.rs `EPS`: justnorm's epsilon
 
+// One row of a call: its position, its sequence (which selects the cache
+// slots), its token, and where its logits go.
+struct RowRec {
+    int64_t pos;
+    int32_t seq;
+    int32_t token;
+    int32_t out;       // logits row (rows of one sequence's chunk: only the last, at 0)
+    int32_t pad;
+};
+
 // The per-call record: written by the host into pinned memory and copied to the
 // device ahead of the call's kernels, so a captured graph replays unchanged.
 struct CallRec {
-    int64_t pos0;      // position of row 0
     int32_t n;         // rows
-    int32_t seq;       // sequence index (selects the cache slots)
-    float *logits;     // device [vocab] or null
+    int32_t pad;
+    float *logits;     // device [.][vocab] or null
     float *tap;        // device [passes][n][hidden] or null
-    int32_t tokens[1]; // [max_chunk]
+    RowRec rows[1];    // [max(max_chunk, max_seqs)]
 };
-inline size_t rec_bytes(int max_chunk) { return sizeof(CallRec) + sizeof(int32_t) * (max_chunk - 1); }
+inline size_t rec_bytes(int rows) { return sizeof(CallRec) + sizeof(RowRec) * (rows - 1); }
+inline size_t rec_used(int rows) { return sizeof(CallRec) + sizeof(RowRec) * (rows - 1); }
 
 // One cache slot (attention ordinal x loop slot) of one sequence.  Rings are
 // head-major: K, V [nk][cap][hd]; position p sits at ring row p % cap.
@@ -48,15 +58,21 @@ inline __host__ __device__ const SlotDesc &slot_at(const SlotDesc *tab, int seq,
 //   kLoopExit:  state = norm(e); x = state                          (after the loops)
 enum LoopOp { kLoopNone = 0, kLoopEnter = 1, kLoopNext = 2, kLoopExit = 3 };
 
+// Rows of a batch run different loop counts: they are sorted by loops, so the
+// rows of a pass are a prefix.  n_prev rows ran the previous sub-layer, n_next
+// run this one.  At a loop boundary the rows that stop keep their state in st;
+// after the loops, rows that stopped early take x = st.
 struct Resolve {
     const float *h;      // residual before the previous sub-layer [T][H]
     const float *o;      // previous sub-layer's output [T][H] (slerp only)
     const float *alpha;  // previous sub-layer's |alpha| [H] (slerp only)
     float *h_out;        // x for this sub-layer [T][H]
     float *inp;          // the loop's input [T][H]
+    float *st;           // the loop state of every row [T][H] (batches), or null
     int32_t slerp;       // 1: e = slerp(h, o, alpha); 0: e = h
     int32_t loop_op;
     int32_t tap_pass;    // pass index of e for the tap, or -1
+    int32_t n_prev, n_next;
     int32_t pad;
 };
 
@@ -94,6 +110,10 @@ hipError_t launch_rownorm(const float *src, int ld_src, float *dst, int N, int T
 hipError_t launch_swiglu_norm(const float *a, const float *b, const float *sg, const float *su,
                               float *dst, int F, int T, hipStream_t s);
 
+// Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
+hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,
+                              hipStream_t s);
+
 // C[T][ldc] (columns c0..c0+N) = A[T][K] . W[N][K]^T, fp32 accumulation.
 hipError_t launch_gemm(int wtype, const float *A, int lda, const void *W, int N, int K, float *C,
                        int ldc, int T, hipStream_t s);
@@ -125,7 +145,8 @@ struct AttnArgs {
     int32_t split;       // keys per workgroup
     int32_t max_split;   // grid.x; partial stride
     int32_t q8;          // cache encoding
-    int32_t field;       // q8: the field is frozen (apply kcol / vcol)
+    int32_t field;       // q8: 1 the field is frozen (apply kcol / vcol), 0 not, -1 by
+                         // each row's position (frozen from position 64 on)
     const CallRec *rec;
     // one-row calls: the RoPE, norms and cache write of the new row are fused in
     const float *rope;   // [max_ctx][hd] RoPE table of the layer's kind: cos half, sin half
@@ -134,8 +155,10 @@ struct AttnArgs {
 };
 // Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
-// One-row calls from the raw projections: grid (max_split, nk), then the merge.
-hipError_t launch_attn_dec(const AttnArgs &a, hipStream_t s);
+// Decode rows (one new row per sequence: a one-row call, or one row of each
+// sequence of a batch) from the raw projections: grid (max_split, nk, T), then
+// the merge.
+hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s);
 // Keys a one-row workgroup takes at most for head dim hd.
 int attn_dec_max_split(int hd);
 
@@ -150,8 +173,9 @@ struct Q8WriteArgs {
     const CallRec *rec;
 };
 hipError_t launch_q8_write(const Q8WriteArgs &a, hipStream_t s);
+// The field freeze of the slot of call row `row`'s sequence.
 hipError_t launch_q8_freeze(const SlotDesc *tab, int n_ord, int ord, int slot, int nk, int hd,
-                            const CallRec *rec, hipStream_t s);
+                            const CallRec *rec, int row, hipStream_t s);
 hipError_t launch_q8_encode_rows(const float *x, const float *col, int rows, int n, int group,
                                  int8_t *codes, float *scales, hipStream_t s);
 // fp32 rows straight into a ring (cache set-up).

@@ -20,8 +20,8 @@ __global__ __launch_bounds__(64) void k_q8_write(Q8WriteArgs a) {
     const int r = a.r0 + blockIdx.x, kh = blockIdx.y;
     const int hd = a.hd, ngk = (hd + kKGroup - 1) / kKGroup;
     const CallRec *rec = a.rec;
-    const SlotDesc &sd = slot_at(a.tab, rec->seq, a.n_ord, a.ord, a.slot);
-    const int64_t p = rec->pos0 + r;
+    const SlotDesc &sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
+    const int64_t p = rec->rows[r].pos;
     const size_t row = (size_t)kh * sd.cap + (size_t)(p % sd.cap);
     encode_row(a.ksrc + (size_t)r * a.kld + kh * hd, a.field ? sd.kcol + kh * hd : nullptr, hd, kKGroup,
                sd.kc + row * hd, sd.ks + row * ngk);
@@ -34,12 +34,12 @@ __global__ __launch_bounds__(64) void k_q8_write(Q8WriteArgs a) {
 // (positions 0..63, ring rows 0..63), then every stored row is re-encoded from
 // its dequantised values against the field.  One workgroup per kv head.
 __global__ __launch_bounds__(256) void k_q8_freeze(const SlotDesc *tab, int n_ord, int ord, int slot,
-                                                   int hd, const CallRec *rec) {
+                                                   int hd, const CallRec *rec, int crow) {
     __shared__ float kcol[256], vcol[256];
     __shared__ float deq[4][2][256];
     const int kh = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int ngk = (hd + kKGroup - 1) / kKGroup;
-    const SlotDesc &sd = slot_at(tab, rec->seq, n_ord, ord, slot);
+    const SlotDesc &sd = slot_at(tab, rec->rows[crow].seq, n_ord, ord, slot);
     const size_t base = (size_t)kh * sd.cap;
     const int n = kWarmup;
     if (tid < hd) {
@@ -82,8 +82,8 @@ __global__ __launch_bounds__(64) void k_q8_encode_rows(const float *x, const flo
 __global__ __launch_bounds__(64) void k_kv_store(const float *k, const float *v, const SlotDesc *tab, int n_ord,
                                                  int ord, int slot, int nk, int hd, const CallRec *rec) {
     const int r = blockIdx.x, kh = blockIdx.y;
-    const SlotDesc &sd = slot_at(tab, rec->seq, n_ord, ord, slot);
-    const int64_t p = rec->pos0 + r;
+    const SlotDesc &sd = slot_at(tab, rec->rows[r].seq, n_ord, ord, slot);
+    const int64_t p = rec->rows[r].pos;
     const size_t row = (size_t)kh * sd.cap + (size_t)(p % sd.cap);
     const size_t src = ((size_t)r * nk + kh) * hd;
     for (int d = threadIdx.x; d < hd; d += 64) {
@@ -101,8 +101,8 @@ hipError_t launch_q8_write(const Q8WriteArgs &a, hipStream_t s) {
 }
 
 hipError_t launch_q8_freeze(const SlotDesc *tab, int n_ord, int ord, int slot, int nk, int hd, const CallRec *rec,
-                            hipStream_t s) {
-    hipLaunchKernelGGL(k_q8_freeze, dim3(nk), dim3(256), 0, s, tab, n_ord, ord, slot, hd, rec);
+                            int row, hipStream_t s) {
+    hipLaunchKernelGGL(k_q8_freeze, dim3(nk), dim3(256), 0, s, tab, n_ord, ord, slot, hd, rec, row);
     return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ namespace {
 template <int WT>
 __global__ __launch_bounds__(256) void k_embed(const void *E, int V, int H, const CallRec *rec, float *h) {
     const int r = blockIdx.x;
-    const uint32_t id = (uint32_t)rec->tokens[r];
+    const uint32_t id = (uint32_t)rec->rows[r].token;
     float *out = h + (size_t)r * H;
     if (id >= (uint32_t)V) {
         for (int i = threadIdx.x; i < H; i += 256) out[i] = 0.f;
@@ -59,7 +59,21 @@ __global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float
     for (int i = threadIdx.x; i < F; i += 256) dst[off + i] = z[i] * f;
 }
 
+// dory.rs `head` for every row of a batch: the logit scale, and each row's
+// logits to its place in the caller's array.
+__global__ __launch_bounds__(256) void k_logits_rows(const float *hlog, const float *ls, int V, const CallRec *rec) {
+    const int r = blockIdx.y;
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= V || rec->logits == nullptr) return;
+    rec->logits[(size_t)rec->rows[r].out * V + v] = hlog[(size_t)r * V + v] * ls[v];
+}
+
 }  // namespace
+
+hipError_t launch_logits_rows(const float *hlog, const float *ls, int V, int T, const CallRec *rec, hipStream_t s) {
+    hipLaunchKernelGGL(k_logits_rows, dim3((V + 255) / 256, T), dim3(256), 0, s, hlog, ls, V, rec);
+    return hipGetLastError();
+}
 
 hipError_t launch_embed(int wtype, const void *E, int V, int H, const CallRec *rec, int T, float *h,
                         hipStream_t s) {

@@ -57,6 +57,7 @@ def _load():
     L.dory_last_error.argtypes = [vp]
     L.dory_last_error.restype = C.c_char_p
     L.dory_forward_chunk.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
+    L.dory_forward_batch.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp]
     L.dory_kv_reset.argtypes = [vp, i32]
     L.dory_position.argtypes = [vp, i32]
     L.dory_position.restype = i64
@@ -175,6 +176,24 @@ class Dory:
         mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
         rc = lib.dory_forward_chunk(self.h, seq, tok.ctypes.data_as(C.c_void_p), int(tok.shape[0]), loops,
                                     mode, _stream(stream), _ptr(out))
+        self._check(rc)
+        return out
+
+    def forward_batch(self, seqs, tokens, loops, kv_mode="last_loop", logits=True, stream=None):
+        """One decode step of several sequences: row i = next token of seqs[i] with
+        loops[i] passes.  Returns logits [nseq][vocab] (device) or None."""
+        import torch
+        sq = np.ascontiguousarray(seqs, dtype=np.int32)
+        tk = np.ascontiguousarray(tokens, dtype=np.int32)
+        lp = np.ascontiguousarray(loops, dtype=np.int32)
+        out = None
+        if logits is True:
+            out = torch.empty((len(sq), self.cfg["vocab"]), dtype=torch.float32, device=self.device)
+        elif logits is not None and logits is not False:
+            out = logits
+        mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
+        rc = lib.dory_forward_batch(self.h, len(sq), sq.ctypes.data_as(C.c_void_p), tk.ctypes.data_as(C.c_void_p),
+                                    lp.ctypes.data_as(C.c_void_p), mode, _stream(stream), _ptr(out))
         self._check(rc)
         return out
 
