@@ -1,21 +1,30 @@
 #!/usr/bin/env python
-"""Benchmark: Dory-2B decode on one MI355X.
+"""Benchmark of the Dory token forward on one MI355X.
 
-A step is one decode token: one call of the whole forward (input block, 4
-passes of the recurrent block, output block, head) for one row at the next
-position of a sequence whose cache already holds `--context` positions.
-Set-up (not timed): seeded synthetic bf16 weights, a prompt of `--context`
-seeded tokens run through the library's prefill path in calls of 512 rows
-(last_loop, loops 4), then `--warmup` decode steps.  Timed: `--steps` decode
-steps, bracketed by device synchronisation and HIP events on the stream the
-library launches on.  Prints one JSON line.
+Workloads (``--config``), all on seeded synthetic bf16 Dory-2B weights and
+seeded tokens:
 
-The roofline entry is for the dominant kernel, the gate|up projection GEMV
-with its SwiGLU epilogue (40% of a token's bytes): it is launched on its own
-over the 20 MLP sub-layers' weights in turn, timed with HIP events on the same
-stream, and its algorithmic bytes per launch are divided by the mean launch
-time.  The CPU baseline is the oracle on the host cores: a few decode tokens at
-the same context, after its cache is loaded with synthetic rows.
+* ``decode`` (default): batch-1 decode at context 4096, loops 4, last_loop, fp32
+  cache.  Set-up: a 4096-token prompt in calls of 512 through the prefill path.
+  A step is one decode token: one call of the whole forward (input block, 4
+  passes of the recurrent block, output block, head).
+* ``q8``: the same decode with the q8_2f cache, full_window 8192, at context
+  32768 (prompt of 32768 tokens in calls of 512).
+* ``prefill``: per_loop, loops 8; a step is one 8192-token prompt in 16 calls
+  of 512 rows (logits of the last call only), the cache reset before each.
+* ``batch``: 64 sequences, each prefilled to 8192 tokens (last_loop, loops 4);
+  a step is one batched decode call with one token per sequence and a loop
+  count per (sequence, step) drawn uniformly from 1..16.
+
+Timed: ``--steps`` steps after ``--warmup`` untimed ones, bracketed by device
+synchronisation and HIP events on the stream the library launches on.  One JSON
+line on stdout; progress on stderr.
+
+The roofline entry is for the workload's dominant kernel, launched on its own
+(dory_stage_bench) over the sub-layers' weights in turn on the same stream and
+timed with HIP events: the gate|up GEMV (decode, q8), the gate|up GEMM at 512
+rows (prefill), decode attention over the batch's 64 rows (batch).  The CPU
+baseline is the oracle on the host cores on a bounded sample of the workload.
 """
 import argparse
 import hashlib
@@ -28,129 +37,206 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 METRIC = "decode tokens/s (all loops) + achieved HBM GB/s, 1×MI355X, Dory-2B ctx 4096"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_gateup_2b_traffic.json")
-GEMV_SRC = os.path.join(ROOT, "looped_normalized_gpt_amd", "csrc", "gemv.hip")
+CSRC = os.path.join(ROOT, "looped_normalized_gpt_amd", "csrc")
+TRAFFIC = {  # committed counter runs: file, kernel source it was taken on
+    "decode": ("gemv_gateup_2b_traffic.json", "gemv.hip"),
+    "q8": ("gemv_gateup_2b_traffic.json", "gemv.hip"),
+    "prefill": ("gemm_gateup_2b_traffic.json", "gemm.hip"),
+    "batch": ("attn_dec_batch64_traffic.json", "attn.hip"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def token_bytes(cfg, pos, loops):
-    """Algorithmic HBM bytes of one decode token at position pos: every weight
-    byte once, every visible cache row once (K and V, fp32), the scale vectors,
-    the cache row written."""
-    H, F, V, Q, KV = cfg["hidden"], cfg["ffn"], cfg["vocab"], cfg["nh"] * cfg["hd"], cfg["nk"] * cfg["hd"]
+def n_ord(cfg):
+    return sum(1 for ch in cfg["pattern"] if ch != "-")
+
+
+def kv_row_bytes(cfg):
+    """Bytes of one cached position of one layer (all kv heads, K and V)."""
+    nk, hd = cfg["nk"], cfg["hd"]
+    if cfg.get("kv_encoding", "f32") == "q8_2f":
+        return nk * (hd + 4 * ((hd + 31) // 32) + hd + 4)
+    return nk * hd * 4 * 2
+
+
+def visible(cfg, kind, pos):
+    win = cfg["window"] if kind == "S" else (cfg.get("full_window") or 1 << 60)
+    return min(win, pos + 1)
+
+
+def sublayer_weight_bytes(cfg, kind):
+    H, F, Q, KV = cfg["hidden"], cfg["ffn"], cfg["nh"] * cfg["hd"], cfg["nk"] * cfg["hd"]
     wb = 2 if cfg["weight_dtype"] == "bf16" else 4
+    if kind == "-":
+        return 3 * F * H * wb + (2 * F + H) * 4
+    return (2 * Q + 2 * KV) * H * wb + H * Q * wb + (2 * Q + H) * 4
+
+
+def passes(cfg, loops):
     n_in, n_rec, n_out = cfg["n_in"], cfg["n_rec"], cfg["n_out"]
-    seq = [(li, 0) for li in range(n_in)] + [(n_in + j, i) for i in range(loops) for j in range(n_rec)] + \
-          [(n_in + n_rec + j, 0) for j in range(n_out)]
-    total = 0
-    for li, _ in seq:
-        kind = cfg["pattern"][li]
-        if kind == "-":
-            total += 3 * F * H * wb + (2 * F + H) * 4
-        else:
-            total += (2 * Q + 2 * KV) * H * wb + H * Q * wb + (2 * Q + H) * 4
-            win = cfg["window"] if kind == "S" else (cfg.get("full_window") or 1 << 60)
-            total += min(win, pos + 1) * KV * 4 * 2 + KV * 4 * 2
-    total += V * H * wb + V * 4
-    return total
+    return list(range(n_in)) + \
+           [n_in + j for _ in range(loops) for j in range(n_rec)] + \
+           [n_in + n_rec + j for j in range(n_out)]
 
 
-def gateup_bytes(cfg):
-    H, F = cfg["hidden"], cfg["ffn"]
+def token_bytes(cfg, pos, loops):
+    """Algorithmic HBM bytes of one batch-1 decode token at position pos: every
+    weight byte once per sub-layer pass, every visible cache row once, the scale
+    vectors, the cache row written, the head."""
+    H, V = cfg["hidden"], cfg["vocab"]
     wb = 2 if cfg["weight_dtype"] == "bf16" else 4
-    return 2 * F * H * wb + H * 4 + F * 4
+    rb = kv_row_bytes(cfg)
+    total = 0
+    for li in passes(cfg, loops):
+        kind = cfg["pattern"][li]
+        total += sublayer_weight_bytes(cfg, kind)
+        if kind != "-":
+            total += visible(cfg, kind, pos) * rb + rb
+    return total + V * H * wb + V * 4
 
 
-def traffic_entry():
-    """HBM bytes per launch of the gate|up GEMV from the committed counter runs,
-    or None when there are none or the kernel source changed since."""
-    if not os.path.exists(TRAFFIC_FILE):
+def batch_step_bytes(cfg, pos, loops_row):
+    """Algorithmic bytes of one batched decode step: the weights of every
+    sub-layer pass once (the recurrent block once per loop of the longest row),
+    and per row its own visible cache rows and written row; the head once."""
+    H, V = cfg["hidden"], cfg["vocab"]
+    wb = 2 if cfg["weight_dtype"] == "bf16" else 4
+    rb = kv_row_bytes(cfg)
+    total = sum(sublayer_weight_bytes(cfg, cfg["pattern"][li]) for li in passes(cfg, max(loops_row)))
+    for L in loops_row:
+        for li in passes(cfg, L):
+            kind = cfg["pattern"][li]
+            if kind != "-":
+                total += visible(cfg, kind, pos) * rb + rb
+    return total + V * H * wb + V * 4 * len(loops_row)
+
+
+def prefill_flops(cfg, T, loops):
+    """Projection GEMM flops of one T-row call (2 flop per multiply-add)."""
+    H, F, Q, KV, V = cfg["hidden"], cfg["ffn"], cfg["nh"] * cfg["hd"], cfg["nk"] * cfg["hd"], cfg["vocab"]
+    f = 0
+    for li in passes(cfg, loops):
+        if cfg["pattern"][li] == "-":
+            f += 2 * T * 3 * F * H
+        else:
+            f += 2 * T * ((2 * Q + 2 * KV) * H + H * Q)
+    return f
+
+
+def traffic_entry(mode):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    runs, or None when there are none or the kernel source changed since."""
+    fname, src = TRAFFIC[mode]
+    path = os.path.join(ROOT, "profiles", fname)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
-    src = hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest()
-    if t.get("gemv_source_sha256") != src:
+    digest = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+    if t.get("source_sha256") != digest:
         return None
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(cfg, w, context, loops, budget_s=20.0):
-    import numpy as np
+def time_stage(dory, g, stage, reps, stream):
+    import torch
+    dory.stage_bench(g, stage, min(reps, 40), stream)   # warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    dory.stage_bench(g, stage, reps, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
 
+
+# ------------------------------------------------------------------ CPU baseline
+
+def _cores():
+    return int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
+
+
+def cpu_decode(cfg, w, context, loops_of, budget_s, what):
+    """The oracle decoding single tokens after its cache is loaded with
+    `context` synthetic rows; loops_of(i) gives token i's loop count."""
     from looped_normalized_gpt_amd import synth
     from oracle import oracle as O
-    o = O.Oracle(cfg, w, max_ctx=context + 16)
-    n_ord = sum(1 for ch in cfg["pattern"] if ch != "-")
-    k, v = synth.make_kv_rows(n_ord * context, cfg["nk"], cfg["hd"], cfg["hidden"], seed=4)
-    o.kv_load(k.reshape(n_ord, 1, context, cfg["nk"], cfg["hd"]), v.reshape(n_ord, 1, context, cfg["nk"], cfg["hd"]))
+    o = O.Oracle(cfg, w, max_ctx=context + 40)
+    no = n_ord(cfg)
+    k, v = synth.make_kv_rows(no * context, cfg["nk"], cfg["hd"], cfg["hidden"], seed=4)
+    shp = (no, 1, context, cfg["nk"], cfg["hd"])
+    o.kv_load(k.reshape(shp), v.reshape(shp))
     del k, v
-    toks = synth.make_tokens(16, cfg["vocab"], seq=9)
+    toks = synth.make_tokens(32, cfg["vocab"], seq=9)
     n, t0 = 0, time.perf_counter()
-    while n < 16:
-        o.forward(toks[n:n + 1], loops, "last_loop")
+    while n < 32:
+        o.forward(toks[n:n + 1], loops_of(n), "last_loop")
         n += 1
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
     o.close()
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n} decode tokens of Dory-2B (loops {loops}, last_loop) at context {context}, "
-                      f"the oracle's cache loaded with {context} synthetic rows, {dt:.1f} s"}
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{n} {what} at context {context}, the oracle's cache loaded with {context} synthetic rows, "
+                      f"{dt:.1f} s"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--context", type=int, default=4096)
-    ap.add_argument("--loops", type=int, default=4)
-    ap.add_argument("--stage-reps", type=int, default=400)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
+def cpu_prefill(cfg, w, rows, loops):
+    from looped_normalized_gpt_amd import synth
+    from oracle import oracle as O
+    o = O.Oracle(cfg, w, max_ctx=rows + 8)
+    toks = synth.make_tokens(rows, cfg["vocab"], seq=9)
+    t0 = time.perf_counter()
+    o.forward(toks, loops, "per_loop")
+    dt = time.perf_counter() - t0
+    o.close()
+    return {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"one {rows}-row prompt call of Dory-2B (per_loop, loops {loops}) from position 0, {dt:.1f} s"}
 
+
+# ------------------------------------------------------------------ workloads
+
+def prompt(g, cfg, n, loops, mode, seq=0, chunk=512, tok_seed=None, last_logits=False):
+    from looped_normalized_gpt_amd import synth
+    toks = synth.make_tokens(n, cfg["vocab"], seq=seq if tok_seed is None else tok_seed)
+    for c in range(0, n, chunk):
+        g.forward(toks[c:c + chunk], loops, mode, seq=seq, logits=(last_logits and c + chunk >= n))
+
+
+def run_decode(args, q8):
     import numpy as np
     import torch
 
     from looped_normalized_gpt_amd import dory, synth
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    cfg = synth.config("2b")
-    log("bench: generating Dory-2B weights")
+    cfg = synth.config("2b", kv_encoding="q8_2f", full_window=8192) if q8 else synth.config("2b")
+    ctx = args.context or (32768 if q8 else 4096)
+    K, W, loops = args.steps or 256, 16 if args.warmup is None else args.warmup, 4
+    log(f"bench: Dory-2B weights; decode at context {ctx}{' (q8_2f cache)' if q8 else ''}")
     w = synth.make_weights(cfg)
-    K, W, ctx, loops = args.steps, args.warmup, args.context, args.loops
-    chunk = 512
-    g = dory.Dory(cfg, w, max_ctx=ctx + W + K + 8, max_chunk=chunk)
+    g = dory.Dory(cfg, w, max_ctx=ctx + W + K + 8, max_chunk=512)
     toks = synth.make_tokens(ctx + W + K, cfg["vocab"])
     stream = torch.cuda.current_stream()
-
-    log(f"bench: prompt of {ctx} tokens in calls of {chunk}")
+    log(f"bench: prompt of {ctx} tokens in calls of 512")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for c in range(0, ctx, chunk):
-        g.forward(toks[c:c + chunk], loops, "last_loop", logits=(c + chunk >= ctx))
+    for c in range(0, ctx, 512):
+        g.forward(toks[c:c + 512], loops, "last_loop", logits=(c + 512 >= ctx))
+        if c % 8192 == 0 and c:
+            log(f"bench:   {c} tokens")
     torch.cuda.synchronize()
     prefill_s = time.perf_counter() - t0
 
     logits = torch.empty(cfg["vocab"], dtype=torch.float32, device="cuda")
-    log(f"bench: {W} warm-up decode steps")
     for i in range(W):
         g.forward(toks[ctx + i:ctx + i + 1], loops, "last_loop", logits=logits)
     torch.cuda.synchronize()
-
     log(f"bench: {K} timed decode steps")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for i in range(W, W + K):
@@ -161,59 +247,220 @@ def main():
     ms = ev0.elapsed_time(ev1) / K
     assert torch.isfinite(logits).all().item(), "non-finite logits"
     tok_s = 1000.0 / ms
-    pos = [ctx + i for i in range(W, W + K)]
-    bytes_tok = float(np.mean([token_bytes(cfg, p, loops) for p in pos]))
+    bytes_tok = float(np.mean([token_bytes(cfg, ctx + i, loops) for i in range(W, W + K)]))
     gbs = bytes_tok * tok_s / 1e9
 
-    log(f"bench: dominant kernel (gate|up GEMV) x{args.stage_reps}")
-    dory.stage_bench(g, "gateup", 40, stream)   # warm the launch path
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    dory.stage_bench(g, "gateup", args.stage_reps, stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    gu_us = e0.elapsed_time(e1) * 1e3 / args.stage_reps
-    gu_bytes = gateup_bytes(cfg)
-    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
-    traffic = traffic_entry()
-
-    stages = {}
-    for st in ("qkvg", "attn", "o", "down", "head"):
-        reps = 100
-        e0.record(stream)
-        dory.stage_bench(g, st, reps, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        stages[st] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    log("bench: dominant kernel (gate|up GEMV) and the other stages")
+    H, F = cfg["hidden"], cfg["ffn"]
+    gu_bytes = 2 * F * H * 2 + H * 4 + F * 4
+    gu_us = time_stage(dory, g, "gateup", args.stage_reps, stream)
+    stages = {st: round(time_stage(dory, g, st, 96, stream), 2) for st in ("qkvg", "attn", "o", "down", "head")}
     stages["gateup"] = round(gu_us, 2)
     g.close()
+    gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle)")
-        cpu = cpu_baseline(cfg, w, ctx, loops)
-
-    out = {
-        "metric": METRIC, "value": round(tok_s, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        # q8: the windows (1024 sliding, 8192 full) cap the rows a token reads, so
+        # a context just past 8192 costs the oracle what 32768 does
+        cctx = 8200 if q8 else ctx
+        cpu = cpu_decode(cfg, w, cctx, lambda i: loops, 20.0,
+                         f"decode tokens of Dory-2B (loops {loops}, last_loop{', q8_2f' if q8 else ''})")
+    if q8:
+        metric = "q8_2f long-context decode tokens/s (all loops) + achieved HBM GB/s, 1×MI355X, Dory-2B ctx 32768"
+        workload = (f"Dory-2B decode, batch 1, context {ctx}, loops 4, last_loop, q8_2f KV cache "
+                    f"(full_window 8192), bf16 weights with fp32 arithmetic")
+    else:
+        metric = METRIC
+        workload = (f"Dory-2B decode, batch 1, context {ctx}, loops 4, last_loop, fp32 KV cache, "
+                    f"bf16 weights with fp32 arithmetic")
+    return {
+        "metric": metric, "value": round(tok_s, 2), "unit": "tokens/s", "steps": K, "warmup": W,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "Dory-2B decode, batch 1, context 4096, loops 4, last_loop, fp32 KV cache, "
-                               "bf16 weights with fp32 arithmetic",
-                   "context": ctx, "loops": loops, "kv_mode": "last_loop", "kv_encoding": "f32",
-                   "weights": "bf16", "parallelism": "none (one GPU)"},
-        "hbm_gbps_algorithmic": round(gbs, 1),
-        "bytes_per_token": int(bytes_tok),
-        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4),
-        "wall_ms_per_step": round(wall_ms / K, 4),
-        "prefill_tokens_per_s": round(ctx / prefill_s, 1),
-        "stage_us": stages,
+        "config": {"workload": workload, "context": ctx, "loops": loops, "kv_mode": "last_loop",
+                   "kv_encoding": cfg["kv_encoding"], "weights": "bf16", "parallelism": "none (one GPU)"},
+        "hbm_gbps_algorithmic": round(gbs, 1), "bytes_per_token": int(bytes_tok),
+        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "wall_ms_per_step": round(wall_ms / K, 4),
+        "prefill_tokens_per_s": round(ctx / prefill_s, 1), "stage_us": stages,
         "roofline": {"kernel": "k_gemv gate|up + SwiGLU (bf16 [2x5632][2048])", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_entry("q8" if q8 else "decode"),
                      "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3)},
         "cpu_baseline": cpu,
     }
+
+
+def run_prefill(args):
+    import torch
+
+    from looped_normalized_gpt_amd import dory, synth
+    cfg = synth.config("2b")
+    n = args.context or 8192
+    K, W, loops, chunk = args.steps or 2, 1 if args.warmup is None else args.warmup, 8, 512
+    log(f"bench: Dory-2B weights; prefill of {n} tokens, per_loop, loops {loops}")
+    w = synth.make_weights(cfg)
+    g = dory.Dory(cfg, w, max_ctx=n + 8, max_chunk=chunk)
+    stream = torch.cuda.current_stream()
+    for i in range(W):
+        g.reset()
+        prompt(g, cfg, n, loops, "per_loop", last_logits=True)
+    torch.cuda.synchronize()
+    log(f"bench: {K} timed prompts")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(K):
+        g.reset()
+        prompt(g, cfg, n, loops, "per_loop", last_logits=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms = ev0.elapsed_time(ev1) / K
+    tok_s = n * 1000.0 / ms
+    gemm_tflops = prefill_flops(cfg, n, loops) / (ms * 1e-3) / 1e12
+
+    log("bench: stages at 512 rows")
+    H, F, Q, KV = cfg["hidden"], cfg["ffn"], cfg["nh"] * cfg["hd"], cfg["nk"] * cfg["hd"]
+    shapes = {"gemm_qkvg": (2 * Q + 2 * KV, H), "gemm_o": (H, Q), "gemm_gateup": (2 * F, H), "gemm_down": (H, F)}
+    stages, tflops = {}, {}
+    for st, (N, Kd) in shapes.items():
+        us = time_stage(dory, g, st, args.stage_reps if st == "gemm_gateup" else 96, stream)
+        stages[st] = round(us, 2)
+        tflops[st] = round(2 * chunk * N * Kd / (us * 1e-6) / 1e12, 1)
+    stages["attn_chunk"] = round(time_stage(dory, g, "attn_chunk", 32, stream), 2)
+    g.close()
+    gu_flops = 2 * chunk * 2 * F * H
+    gu_tf = tflops["gemm_gateup"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU baseline (oracle)")
+        cpu = cpu_prefill(cfg, w, 16, loops)
+    return {
+        "metric": "prefill tokens/s, 1×MI355X, Dory-2B per_loop loops 8, 8192-token prompt in 512-row calls",
+        "value": round(tok_s, 1), "unit": "tokens/s", "steps": K, "warmup": W, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Dory-2B prefill, {n}-token prompt in calls of {chunk}, per_loop, loops {loops}, "
+                               f"bf16 MFMA projections (bf16 operands, fp32 accumulation), fp32 attention",
+                   "prompt": n, "chunk": chunk, "loops": loops, "kv_mode": "per_loop", "weights": "bf16",
+                   "parallelism": "none (one GPU)"},
+        "projection_tflops_overall": round(gemm_tflops, 1), "wall_ms_per_step": round(wall_ms / K, 3),
+        "stage_us": stages, "stage_tflops": tflops,
+        "roofline": {"kernel": "k_gemm_mfma gate|up (512 x 11264 x 2048, bf16)", "bound": "mfma",
+                     "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry("prefill"),
+                     "flops_per_launch": gu_flops, "us_per_launch": stages["gemm_gateup"]},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_batch(args):
+    import numpy as np
+    import torch
+
+    from looped_normalized_gpt_amd import dory, synth
+    cfg = synth.config("2b")
+    nseq, ctx = 64, args.context or 8192
+    K, W = args.steps or 128, 4 if args.warmup is None else args.warmup
+    log(f"bench: Dory-2B weights; {nseq} sequences prefilled to {ctx}")
+    w = synth.make_weights(cfg)
+    g = dory.Dory(cfg, w, max_ctx=ctx + W + K + 8, max_chunk=512, max_seqs=nseq)
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    for s in range(nseq):
+        prompt(g, cfg, ctx, 4, "last_loop", seq=s)
+        if s % 8 == 7:
+            torch.cuda.synchronize()
+            log(f"bench:   {s + 1} sequences prefilled, {time.perf_counter() - t0:.1f} s")
+    torch.cuda.synchronize()
+    prefill_s = time.perf_counter() - t0
+    loops = synth.make_loops((W + K) * nseq).reshape(W + K, nseq)
+    toks = np.stack([synth.make_tokens(W + K, cfg["vocab"], seq=100 + s) for s in range(nseq)], 1)
+    seqs = np.arange(nseq, dtype=np.int32)
+    logits = torch.empty((nseq, cfg["vocab"]), dtype=torch.float32, device="cuda")
+    for i in range(W):
+        g.forward_batch(seqs, toks[i], loops[i], "last_loop", logits=logits)
+    torch.cuda.synchronize()
+    log(f"bench: {K} timed batch steps")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(W, W + K):
+        g.forward_batch(seqs, toks[i], loops[i], "last_loop", logits=logits)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms = ev0.elapsed_time(ev1) / K
+    assert torch.isfinite(logits).all().item(), "non-finite logits"
+    tok_s = nseq * 1000.0 / ms
+    step_bytes = float(np.mean([batch_step_bytes(cfg, ctx + i, loops[i]) for i in range(W, W + K)]))
+    gbs = step_bytes * (1000.0 / ms) / 1e9
+
+    log("bench: dominant kernel (decode attention over the 64 rows)")
+    # stage 1 cycles the 8 attention sub-layers (S and full alternate); the last
+    # call's rows are all at position ctx + W + K - 1
+    p = ctx + W + K - 1
+    rb = kv_row_bytes(cfg)
+    Q = cfg["nh"] * cfg["hd"]
+    per_row = [visible(cfg, kind, p) * rb + Q * 4 * 2 + 2 * cfg["nk"] * cfg["hd"] * 4
+               for kind in cfg["pattern"] if kind != "-"]
+    at_bytes = nseq * float(np.mean(per_row))
+    at_us = time_stage(dory, g, "attn", 64, stream)
+    stages = {"attn": round(at_us, 2)}
+    g.close()
+    at_gbs = at_bytes / (at_us * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: CPU baseline (oracle)")
+        lp = loops[W:, 0]
+        cpu = cpu_decode(cfg, w, ctx, lambda i: int(lp[i % len(lp)]), 20.0,
+                         "single-sequence decode tokens of Dory-2B (loops drawn from 1..16, last_loop)")
+    return {
+        "metric": "batched decode tokens/s (64 sequences, all loops) + achieved HBM GB/s, 1×MI355X, Dory-2B ctx 8192",
+        "value": round(tok_s, 1), "unit": "tokens/s", "steps": K, "warmup": W, "ms_per_step": round(ms, 3),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"Dory-2B batched decode, {nseq} sequences at context {ctx}, last_loop, loops per "
+                               f"(sequence, step) uniform in 1..16, fp32 KV cache, bf16 weights",
+                   "sequences": nseq, "context": ctx, "kv_mode": "last_loop", "weights": "bf16",
+                   "parallelism": "none (one GPU)"},
+        "hbm_gbps_algorithmic": round(gbs, 1), "bytes_per_step": int(step_bytes),
+        "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "wall_ms_per_step": round(wall_ms / K, 3),
+        "prefill_tokens_per_s": round(nseq * ctx / prefill_s, 1), "stage_us": stages,
+        "roofline": {"kernel": "k_attn_dec + k_attn_merge over 64 rows (S and full layers alternating)",
+                     "bound": "hbm", "achieved": round(at_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(at_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_entry("batch"),
+                     "bytes_per_launch": int(at_bytes), "us_per_launch": round(at_us, 3)},
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--config", choices=("decode", "q8", "prefill", "batch"), default="decode")
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--context", type=int, default=None, help="decode context / prompt length")
+    ap.add_argument("--stage-reps", type=int, default=400)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.config in ("decode", "q8"):
+        out = run_decode(args, args.config == "q8")
+    elif args.config == "prefill":
+        out = run_prefill(args)
+    else:
+        out = run_batch(args)
+    out = {"metric": out.pop("metric"), "value": out.pop("value"), "unit": out.pop("unit"), "n_gpus": 1, **out}
     print(json.dumps(out), flush=True)
 
 

@@ -176,13 +176,19 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
 int dory_q8_encode_rows(const float *x, const float *col, int32_t rows, int32_t n, int32_t group,
                         int8_t *codes, float *scales, dory_stream_t stream);
 
-/* Benchmark tap: launches one kernel of the one-row forward `reps` times back to
- * back on stream, over the handle's current scratch (left by the last call) and
- * sequence 0's cache at its last position, cycling through the sub-layers that
- * have that kernel so each launch streams its own weights from HBM.  Stage:
- * 0 q|k|v|g projection, 1 attention, 2 O projection, 3 gate|up projection with
- * SwiGLU, 4 down projection, 5 head.  Needs a prior one-row call on sequence 0.
- * Leaves the scratch undefined (the cache and positions are untouched). */
+/* Benchmark tap: launches one kernel of the forward `reps` times back to back on
+ * stream, over the handle's current scratch (left by the last call) and the
+ * cache rows that call read, cycling through the sub-layers that have that
+ * kernel so each launch streams its own weights from HBM.  Stage:
+ *   0 q|k|v|g GEMV, 1 decode attention over the last call's rows (that call a
+ *   one-row or batch call), 2 O GEMV, 3 gate|up GEMV with SwiGLU, 4 down GEMV,
+ *   5 head GEMV;
+ *   6 q|k|v|g GEMM, 7 O GEMM, 8 gate|up GEMM, 9 down GEMM, each over max_chunk
+ *   rows; 10 chunk attention over the last call's rows (that call a multi-row
+ *   chunk).
+ * Needs a prior forward call (DORY_ESTATE otherwise, or when the last call was
+ * not of the kind stage 1 or 10 needs).  Leaves the scratch undefined; the cache
+ * and positions are untouched. */
 int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t stream);
 
 #ifdef __cplusplus

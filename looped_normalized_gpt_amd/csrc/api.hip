@@ -55,7 +55,7 @@ struct dory {
     int64_t win_s = 0, win_f = 0;
     // device scratch
     float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
-    float *z = nullptr, *zn = nullptr, *ga = nullptr, *gb = nullptr, *un = nullptr, *kstage = nullptr;
+    float *z = nullptr, *zn = nullptr, *ga = nullptr, *un = nullptr, *kstage = nullptr;
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     CallRec *rec = nullptr;
@@ -75,7 +75,10 @@ struct dory {
     std::vector<SeqState> seqs;
     std::string err;
     int device = 0;
-    int last_loops = 0, last_mode = -1;  // of the last one-row call on sequence 0
+    // the last successful forward call (its rows are in rec): rows, kind, loops, mode, first position
+    int last_T = 0, last_loops = 0, last_mode = -1;
+    bool last_chunk = false;
+    int64_t last_pos0 = 0;
 };
 
 namespace {
@@ -225,6 +228,14 @@ uint8_t &froze_at(Enq &q, int seq, int ord, int slot) {
     return q.froze[((size_t)seq * q.h->n_ord + ord) * kMaxLoops + slot];
 }
 
+// The fused projections of multi-row calls: q | k | v | g, and gate | up.
+GemmW qkvg_w(const dory_t *h, const dory_layer_weights &w) {
+    return GemmW{{w.wq, w.wk, w.wv, w.wg}, {h->Q, h->Q + h->KV, h->Q + 2 * h->KV, 2 * h->Q + 2 * h->KV}, 4};
+}
+GemmW gateup_w(const dory_t *h, const dory_layer_weights &w) {
+    return GemmW{{w.wgate, w.wup, w.wup, w.wup}, {h->F, 2 * h->F, 2 * h->F, 2 * h->F}, 2};
+}
+
 // One attention sub-layer over the first M rows of the call.
 int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const float *x, int M) {
     dory_t *h = q.h;
@@ -238,10 +249,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wq, h->Q, h->H, h->qkvg, ld, M, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wk, h->KV, h->H, h->qkvg + h->Q, ld, M, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wv, h->KV, h->H, h->qkvg + h->Q + h->KV, ld, M, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wg, h->Q, h->H, h->qkvg + h->Q + 2 * h->KV, ld, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s));
     }
     AttnArgs aa{};
     aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part;
@@ -314,7 +322,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
     } else {
         LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->Q, M, q.s));
-        LAUNCH(launch_gemm(h->wt, h->zn, h->Q, w.wo, h->H, h->Q, h->o, h->H, M, q.s));
+        LAUNCH(launch_gemm(h->wt, h->zn, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s));
     }
     return DORY_OK;
 }
@@ -333,10 +341,9 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
         d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wgate, h->F, h->H, h->ga, h->F, M, q.s));
-        LAUNCH(launch_gemm(h->wt, x, h->H, w.wup, h->F, h->H, h->gb, h->F, M, q.s));
-        LAUNCH(launch_swiglu_norm(h->ga, h->gb, w.sg, w.su, h->un, h->F, M, q.s));
-        LAUNCH(launch_gemm(h->wt, h->un, h->F, w.wdown, h->H, h->F, h->o, h->H, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
+        LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, h->un, h->F, M, q.s));
+        LAUNCH(launch_gemm(h->wt, h->un, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s));
     }
     return DORY_OK;
 }
@@ -412,7 +419,7 @@ int enqueue(Enq &q) {
             a.row = T - 1; a.src = h->hb[P % 2];
             LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));
         } else if (q.want_logits) {
-            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->H, h->w.head, h->V, h->H, h->hlog, h->V, T, q.s));
+            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->H, gemm_w(h->w.head, h->V), h->V, h->H, h->hlog, h->V, T, q.s));
             LAUNCH(launch_logits_rows(h->hlog, h->w.logit_scale, h->V, T, h->rec, q.s));
         }
     }
@@ -543,8 +550,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->qp, (size_t)chunk * h->Q));
     CREATE_CHECK(dmalloc(h, &h->z, (size_t)chunk * h->Q));
     CREATE_CHECK(dmalloc(h, &h->zn, (size_t)chunk * h->Q));
-    CREATE_CHECK(dmalloc(h, &h->ga, (size_t)chunk * h->F));
-    CREATE_CHECK(dmalloc(h, &h->gb, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->ga, (size_t)chunk * 2 * h->F));   // gate | up per row
     CREATE_CHECK(dmalloc(h, &h->un, (size_t)chunk * h->F));
     CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));
@@ -658,13 +664,14 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
         rc = enqueue(q);
         if (rc) return rc;
     }
+    h->last_T = n;
+    h->last_chunk = n > 1;
+    h->last_loops = loops;
+    h->last_mode = kv_mode;
+    h->last_pos0 = st.pos;
     st.pos += n;
     st.mode = kv_mode;
     if (kv_mode == DORY_PER_LOOP) st.loops = loops;
-    if (n == 1 && seq == 0) {
-        h->last_loops = loops;
-        h->last_mode = kv_mode;
-    }
     return DORY_OK;
 }
 
@@ -723,6 +730,10 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
     }
     rc = enqueue(q);
     if (rc) return rc;
+    h->last_T = nseq;
+    h->last_chunk = false;
+    h->last_loops = lmax;
+    h->last_mode = kv_mode;
     for (int i = 0; i < nseq; ++i) {
         SeqState &st = h->seqs[seqs[i]];
         st.pos += 1;
@@ -872,17 +883,22 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
 
 int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t stream) {
     if (!h) return DORY_EINVAL;
-    if (stage < 0 || stage > 5 || reps < 1) return fail(h, DORY_EINVAL, "dory_stage_bench: stage 0..5, reps >= 1");
-    if (h->last_loops == 0 || h->seqs[0].pos < 1)
-        return fail(h, DORY_ESTATE, "dory_stage_bench: needs a one-row call on sequence 0 first");
+    if (stage < 0 || stage > 10 || reps < 1) return fail(h, DORY_EINVAL, "dory_stage_bench: stage 0..10, reps >= 1");
+    if (h->last_T == 0) return fail(h, DORY_ESTATE, "dory_stage_bench: needs a forward call first");
+    if (stage == 1 && h->last_chunk)
+        return fail(h, DORY_ESTATE, "dory_stage_bench: decode attention needs a one-row or batch call last");
+    if (stage == 10 && !h->last_chunk)
+        return fail(h, DORY_ESTATE, "dory_stage_bench: chunk attention needs a multi-row call last");
     HIPCHECK(h, hipSetDevice(h->device));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool attn_stage = stage <= 2 || stage == 6 || stage == 7 || stage == 10;
     std::vector<const LayerInfo *> ls;
     for (const LayerInfo &l : h->L)
-        if ((stage <= 2) == l.attn) ls.push_back(&l);
+        if (attn_stage == l.attn) ls.push_back(&l);
     if (stage == 5) ls.assign(1, nullptr);
     if (ls.empty()) return fail(h, DORY_EINVAL, "dory_stage_bench: no sub-layer has this stage");
     const int ld = 2 * h->Q + 2 * h->KV;
+    const int MC = h->cfg.max_chunk;
     for (int i = 0; i < reps; ++i) {
         const LayerInfo *l = ls[i % ls.size()];
         Resolve rs{};
@@ -890,38 +906,66 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
         rs.inp = h->inp; rs.h_out = nullptr; rs.tap_pass = -1;
         GemvArgs a{};
         a.rec = h->rec; a.hidden = h->H; a.row = 0; a.rs = rs;
+        AttnArgs aa{};
+        if (stage == 1 || stage == 10) {
+            aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = l->w.sg; aa.z = h->z; aa.part = h->part;
+            aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l->ord;
+            aa.slot = slot_of(h, *l, h->last_mode, 0);
+            aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
+            aa.window = l->sliding ? h->win_s : h->win_f;
+            aa.rope = l->sliding ? h->rope_s : h->rope_f; aa.sq = l->w.sq; aa.no_write = 1;
+            aa.q8 = h->q8; aa.rec = h->rec;
+        }
         hipError_t e = hipSuccess;
-        if (stage == 0) {
+        switch (stage) {
+        case 0:
             a.w[0] = l->w.wq; a.w[1] = l->w.wk; a.w[2] = l->w.wv; a.w[3] = l->w.wg;
             a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
             a.nseg = 4; a.N = ld; a.K = h->H; a.y = h->qkvg;
             e = launch_gemv(h->wt, kProResolve, kEpiStore, a, s);
-        } else if (stage == 1) {
-            AttnArgs aa{};
-            aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = l->w.sg; aa.z = h->z; aa.part = h->part;
-            aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l->ord;
-            aa.slot = slot_of(h, *l, h->last_mode, h->last_loops - 1);
-            aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
-            aa.window = l->sliding ? h->win_s : h->win_f;
+            break;
+        case 1:
             aa.split = l->sliding ? h->split_ds : h->split_df;
             aa.max_split = l->sliding ? h->ms_ds : h->ms_df;
-            aa.rope = l->sliding ? h->rope_s : h->rope_f; aa.sq = l->w.sq; aa.no_write = 1;
-            aa.q8 = h->q8; aa.field = -1; aa.rec = h->rec;
-            e = launch_attn_dec(aa, 1, s);
-        } else if (stage == 2) {
+            aa.field = -1;
+            e = launch_attn_dec(aa, h->last_T, s);
+            break;
+        case 2:
             a.w[0] = l->w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.src = h->z; a.y = h->o;
             e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);
-        } else if (stage == 3) {
+            break;
+        case 3:
             a.w[0] = l->w.wgate; a.w[1] = l->w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H;
             a.y = h->ga; a.sg = l->w.sg; a.su = l->w.su;
             e = launch_gemv(h->wt, kProResolve, kEpiPair, a, s);
-        } else if (stage == 4) {
+            break;
+        case 4:
             a.w[0] = l->w.wdown; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->F; a.src = h->ga; a.y = h->o;
             e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);
-        } else {
+            break;
+        case 5:
             a.w[0] = h->w.head; a.seg_end[0] = h->V; a.nseg = 1; a.N = h->V; a.K = h->H;
             a.logit_scale = h->w.logit_scale;
             e = launch_gemv(h->wt, kProResolve, kEpiHead, a, s);
+            break;
+        case 6:
+            e = launch_gemm(h->wt, h->hb[0], h->H, qkvg_w(h, l->w), ld, h->H, h->qkvg, ld, MC, s);
+            break;
+        case 7:
+            e = launch_gemm(h->wt, h->zn, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->o, h->H, MC, s);
+            break;
+        case 8:
+            e = launch_gemm(h->wt, h->hb[0], h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
+            break;
+        case 9:
+            e = launch_gemm(h->wt, h->un, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s);
+            break;
+        default:
+            aa.split = h->split_pf;
+            aa.max_split = h->ms_pf;
+            aa.field = h->q8 && h->last_pos0 >= kWarmup + 1;
+            e = launch_attn(aa, h->last_T, s);
+            break;
         }
         if (e != hipSuccess) return hip_fail(h, e, "dory_stage_bench");
     }

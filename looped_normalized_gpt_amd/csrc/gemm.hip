@@ -16,9 +16,23 @@ namespace {
 
 constexpr int BM = 64, BN = 64, BK = 16;
 
+// Row n of the stacked weight segments.
+template <typename T>
+__device__ inline const T *seg_row(const GemmW &g, int n, int K) {
+    const void *b = g.w[0];
+    int start = 0;
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+        if (i < g.nseg && n >= g.seg_end[i - 1]) {
+            b = g.w[i];
+            start = g.seg_end[i - 1];
+        }
+    return reinterpret_cast<const T *>(b) + (size_t)(n - start) * K;
+}
+
 template <int WT>
 __global__ __launch_bounds__(256) void k_gemm_tiled(const float *__restrict__ A, int lda,
-                                                    const void *__restrict__ Wv, int N, int K,
+                                                    const GemmW Wv, int N, int K,
                                                     float *__restrict__ C, int ldc, int M) {
     __shared__ float As[BK][BM + 4];
     __shared__ float Ws[BK][BN + 4];
@@ -41,11 +55,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const float *__restrict__ A,
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (n < N && k < K) {
                 if (WT == kBF16) {
-                    const uint2 u = *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(Wv) +
-                                                                     (size_t)n * K + k);
+                    const uint2 u = *reinterpret_cast<const uint2 *>(seg_row<uint16_t>(Wv, n, K) + k);
                     v = make_float4(bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y));
                 } else {
-                    v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(Wv) + (size_t)n * K + k);
+                    v = *reinterpret_cast<const float4 *>(seg_row<float>(Wv, n, K) + k);
                 }
             }
             Ws[lk + 0][lr] = v.x;
@@ -88,7 +101,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // receives C[8 (j/4) + 4 (l/32) + j%4][l % 32] in accumulator j.
 template <int BN>
 __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, int lda,
-                                                   const uint16_t *__restrict__ W, int N, int K,
+                                                   const GemmW W, int N, int K,
                                                    float *__restrict__ C, int ldc, int M) {
     constexpr int BM = 128, BK = 32, LDK = BK + 8;  // padded LDS rows (bf16)
     constexpr int TM = BM / 2 / 32, TN = BN / 2 / 32; // MFMA tiles per wave
@@ -110,10 +123,11 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, 
                        : make_float4(0.f, 0.f, 0.f, 0.f);
         }
         const int n = n0 + lr;
+        const uint16_t *wr = seg_row<uint16_t>(W, n < N ? n : 0, K);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const bool ok = lr < BN && n < N && k + 8 * i < K;
-            rb[i] = ok ? *reinterpret_cast<const uint4 *>(W + (size_t)n * K + k + 8 * i) : make_uint4(0, 0, 0, 0);
+            rb[i] = ok ? *reinterpret_cast<const uint4 *>(wr + k + 8 * i) : make_uint4(0, 0, 0, 0);
         }
     };
     auto sstore = [&](int buf) {
@@ -183,17 +197,17 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, 
 
 }  // namespace
 
-hipError_t launch_gemm(int wtype, const float *A, int lda, const void *W, int N, int K, float *C, int ldc,
+hipError_t launch_gemm(int wtype, const float *A, int lda, const GemmW &Wb, int N, int K, float *C, int ldc,
                        int M, hipStream_t s) {
-    if (K % 4 || lda % 4) return hipErrorInvalidValue;
+    if (K % 4 || lda % 4 || Wb.nseg < 1 || Wb.nseg > 4 || Wb.seg_end[Wb.nseg - 1] != N) return hipErrorInvalidValue;
+    const GemmW W = Wb;
     if (wtype == kBF16 && M >= 32 && K % 8 == 0) {
         // bf16 MFMA; narrower tiles when the 128-wide ones would leave CUs idle
-        const uint16_t *Wb = reinterpret_cast<const uint16_t *>(W);
         const int mt = (M + 127) / 128;
         if ((long)mt * ((N + 127) / 128) >= 256) {
-            hipLaunchKernelGGL((k_gemm_mfma<128>), dim3((N + 127) / 128, mt), dim3(256), 0, s, A, lda, Wb, N, K, C, ldc, M);
+            hipLaunchKernelGGL((k_gemm_mfma<128>), dim3((N + 127) / 128, mt), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
         } else {
-            hipLaunchKernelGGL((k_gemm_mfma<64>), dim3((N + 63) / 64, mt), dim3(256), 0, s, A, lda, Wb, N, K, C, ldc, M);
+            hipLaunchKernelGGL((k_gemm_mfma<64>), dim3((N + 63) / 64, mt), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
         }
         return hipGetLastError();
     }

@@ -107,15 +107,25 @@ hipError_t launch_embed(int wtype, const void *embed, int V, int H, const CallRe
                         float *h, hipStream_t s);
 hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s);
 hipError_t launch_rownorm(const float *src, int ld_src, float *dst, int N, int T, hipStream_t s);
-hipError_t launch_swiglu_norm(const float *a, const float *b, const float *sg, const float *su,
+// a and b rows have stride ld; dst rows stride F.
+hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su,
                               float *dst, int F, int T, hipStream_t s);
 
 // Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
 hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,
                               hipStream_t s);
 
-// C[T][ldc] (columns c0..c0+N) = A[T][K] . W[N][K]^T, fp32 accumulation.
-hipError_t launch_gemm(int wtype, const float *A, int lda, const void *W, int N, int K, float *C,
+// Weights of a GEMM as up to 4 row segments stacked along N: output column n
+// reads row n - seg_end[i-1] of w[i] for seg_end[i-1] <= n < seg_end[i].
+struct GemmW {
+    const void *w[4];
+    int32_t seg_end[4];
+    int32_t nseg;
+};
+inline GemmW gemm_w(const void *w, int N) { return GemmW{{w, w, w, w}, {N, N, N, N}, 1}; }
+
+// C[T][ldc] (columns 0..N-1) = A[T][K] . W[N][K]^T, fp32 accumulation.
+hipError_t launch_gemm(int wtype, const float *A, int lda, const GemmW &W, int N, int K, float *C,
                        int ldc, int T, hipStream_t s);
 
 // Attention.

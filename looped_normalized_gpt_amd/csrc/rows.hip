@@ -43,15 +43,15 @@ __global__ __launch_bounds__(256) void k_rownorm(const float *src, int ld, float
 }
 
 // dory.rs `mlp_layer`: z = silu(a*sg) * (b*su), then justnorm over F.
-__global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float *b, const float *sg,
+__global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float *b, int ld, const float *sg,
                                                      const float *su, float *dst, int F) {
     extern __shared__ float smem[];
     float *red = smem, *z = smem + 8;
-    const size_t off = (size_t)blockIdx.x * F;
+    const size_t off = (size_t)blockIdx.x * F, offi = (size_t)blockIdx.x * ld;
     float s = 0.f;
     for (int i = threadIdx.x; i < F; i += 256) {
-        float g = a[off + i] * sg[i];
-        float v = g / (1.0f + expf(-g)) * (b[off + i] * su[i]);
+        float g = a[offi + i] * sg[i];
+        float v = g / (1.0f + expf(-g)) * (b[offi + i] * su[i]);
         z[i] = v;
         s += v * v;
     }
@@ -92,9 +92,9 @@ hipError_t launch_rownorm(const float *src, int ld, float *dst, int N, int T, hi
     return hipGetLastError();
 }
 
-hipError_t launch_swiglu_norm(const float *a, const float *b, const float *sg, const float *su, float *dst,
+hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su, float *dst,
                               int F, int T, hipStream_t s) {
-    hipLaunchKernelGGL(k_swiglu_norm, dim3(T), dim3(256), sizeof(float) * (F + 8), s, a, b, sg, su, dst, F);
+    hipLaunchKernelGGL(k_swiglu_norm, dim3(T), dim3(256), sizeof(float) * (F + 8), s, a, b, ld, sg, su, dst, F);
     return hipGetLastError();
 }
 

@@ -242,11 +242,12 @@ class Dory:
                                      k.ctypes.data_as(C.c_void_p), v.ctypes.data_as(C.c_void_p)))
 
 
-STAGES = {"qkvg": 0, "attn": 1, "o": 2, "gateup": 3, "down": 4, "head": 5}
+STAGES = {"qkvg": 0, "attn": 1, "o": 2, "gateup": 3, "down": 4, "head": 5,
+          "gemm_qkvg": 6, "gemm_o": 7, "gemm_gateup": 8, "gemm_down": 9, "attn_chunk": 10}
 
 
 def stage_bench(model: "Dory", stage: str, reps: int, stream=None):
-    """Launches one decode kernel `reps` times (see dory_stage_bench)."""
+    """Launches one kernel of the forward `reps` times (see dory_stage_bench)."""
     model._check(lib.dory_stage_bench(model.h, STAGES[stage], reps, _stream(stream)))
 
 
