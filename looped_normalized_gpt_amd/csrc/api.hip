@@ -228,6 +228,36 @@ uint8_t &froze_at(Enq &q, int seq, int ord, int slot) {
     return q.froze[((size_t)seq * q.h->n_ord + ord) * kMaxLoops + slot];
 }
 
+// Key splits of a chunk's attention (rows pos0 .. pos0+M-1, aa.window set).
+// MFMA blocks: about 512 workgroups, at least 256 keys each (a multiple of
+// the 64-key tile); otherwise one row per workgroup, 256 keys each.
+void chunk_split(const dory_t *h, int64_t pos0, int M, AttnArgs &aa) {
+    aa.max_split = h->ms_pf;
+    aa.blk = attn_chunk_block(h->hd, h->nh / h->nk);
+    if (aa.blk == 0) {
+        aa.split = h->split_pf;
+        aa.nsplit = 0;
+        return;
+    }
+    const int blk = aa.blk, nb = (M + blk - 1) / blk;
+    int64_t len = 0;  // the longest block key range
+    for (int b = 0; b < nb; ++b) {
+        const int rb0 = b * blk, rb1 = std::min(M, rb0 + blk) - 1;
+        const int64_t klo = std::max<int64_t>(0, pos0 + rb0 + 1 - aa.window);
+        len = std::max(len, pos0 + rb1 - klo + 1);
+    }
+    const int64_t per = (int64_t)nb * h->nk;
+    const int64_t want = std::max<int64_t>(1, (512 + per - 1) / per);
+    int64_t split = std::max<int64_t>(256, ((len + want - 1) / want + 63) / 64 * 64);
+    int64_t ns = (len + split - 1) / split;
+    if (ns > h->ms_pf) {  // never at the sizes create() allows for; kept safe
+        split = ((len + h->ms_pf - 1) / h->ms_pf + 63) / 64 * 64;
+        ns = (len + split - 1) / split;
+    }
+    aa.split = (int)split;
+    aa.nsplit = (int)ns;
+}
+
 // The fused projections of multi-row calls: q | k | v | g, and gate | up.
 GemmW qkvg_w(const dory_t *h, const dory_layer_weights &w) {
     return GemmW{{w.wq, w.wk, w.wv, w.wg}, {h->Q, h->Q + h->KV, h->Q + 2 * h->KV, 2 * h->Q + 2 * h->KV}, 4};
@@ -310,8 +340,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
             }
             field = pos0 >= kWarmup + 1 || fz;
         }
-        aa.split = h->split_pf;
-        aa.max_split = h->ms_pf;
+        chunk_split(h, pos0, M, aa);
         aa.field = field;
         LAUNCH(launch_attn(aa, M, q.s));
     }
@@ -519,8 +548,10 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     h->ms_ds = (int)((ws + h->split_ds - 1) / h->split_ds);
     h->ms_df = (int)((wf + h->split_df - 1) / h->split_df);
     h->ms_dec = std::max(h->ms_ds, h->ms_df);
+    // multi-row calls: at least 256 keys per split over a block's key range,
+    // which is at most wmax + 127 keys
     h->split_pf = 256;
-    h->ms_pf = (int)((wmax + h->split_pf - 1) / h->split_pf);
+    h->ms_pf = (int)((wmax + 127 + h->split_pf - 1) / h->split_pf);
     if (h->ms_dec > 1024 || h->ms_pf > 1024) {
         delete h;
         return fail(nullptr, DORY_EINVAL, "dory_create: attention window too long (more than 262144 keys)");
@@ -961,8 +992,7 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_gemm(h->wt, h->un, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s);
             break;
         default:
-            aa.split = h->split_pf;
-            aa.max_split = h->ms_pf;
+            chunk_split(h, h->last_pos0, h->last_T, aa);
             aa.field = h->q8 && h->last_pos0 >= kWarmup + 1;
             e = launch_attn(aa, h->last_T, s);
             break;

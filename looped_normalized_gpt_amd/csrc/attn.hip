@@ -99,8 +99,16 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
     float vcol = 1.f;
     if (Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup)))
         vcol = slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + dc];
-    const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
-    const int nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
+    int nsplit;
+    if (a.blk > 0) {  // k_fattn: the splits of the row's block of a.blk rows
+        const int rb0 = r / a.blk * a.blk, rb1 = (rb0 + a.blk < a.rec->n ? rb0 + a.blk : a.rec->n) - 1;
+        const int64_t pos0 = a.rec->rows[0].pos;
+        const int64_t klo = pos0 + rb0 + 1 - a.window > 0 ? pos0 + rb0 + 1 - a.window : 0;
+        nsplit = (int)((pos0 + rb1 - klo + a.split) / a.split);
+    } else {
+        const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+        nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
+    }
     const size_t pstride = (size_t)rep * (hd + 2);
     const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride + (size_t)h * (hd + 2);
     float M = -INFINITY, L = 0.f, acc = 0.f;
@@ -117,6 +125,7 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (base + nw * u >= nsplit) break;
+            if (m[u] == -INFINITY) continue;  // a split with no key this row sees
             const float Mn = fmaxf(M, m[u]);
             const float c0 = expf(M - Mn), c1 = expf(m[u] - Mn);
             L = L * c0 + l[u] * c1;
@@ -523,12 +532,259 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Grouped-query attention of a chunk of one sequence on bf16 MFMA (the
+// pages' attend_chunk: a panel of queries per kv head against the cache), for
+// rows at consecutive positions pos0 .. pos0+T-1 after launch_prep has written
+// their keys and values.
+//
+// Workgroup (s, kh, b): kv head kh, rows b*BQ .. b*BQ+BQ-1 with their REP q
+// heads (128 query vectors, qv = h*BQ + row), and split s of the keys the block
+// sees: [klo + s*split, ..) with klo = max(0, pos0 + b*BQ + 1 - window).  Wave w
+// owns query vectors 32w .. 32w+31.  Per tile of 64 keys, staged in LDS as
+// bf16 (K as [key][d]; V transposed as [d][slot]):
+//   S^T = K Q^T   (v_mfma_f32_32x32x16_bf16: A = K rows, B = Q from registers):
+//                 lane l then holds query vector l%32 and 16 keys of each
+//                 32-key block, keys 8(j/4) + 4(l/32) + j%4 in element j;
+//   online softmax per lane (the partner lane l^32 holds the other 16 keys);
+//   O^T += V^T P^T (A = V^T from LDS, B = P^T straight from the registers):
+//                 the key slots of V^T are laid out in the order the P^T
+//                 registers hold them, so no shuffle is needed.
+// O^T leaves lane l with 16 channels of query vector l%32 per 32-channel tile,
+// so the softmax rescale is one multiplier per lane.  Each workgroup writes
+// (max, sum, unnormalised sum of p*v) per (row, head) for k_attn_merge.
+template <int HD, int REP, int Q8>
+__global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
+    static_assert(HD == 128, "the loaders assume 32 lanes per 128-channel row");
+    constexpr int BQ = 128 / REP;        // rows per workgroup
+    constexpr int KT = 64;               // keys per tile
+    constexpr int KP = HD + 8, VP = KT + 8;
+    constexpr int NGK = (HD + kKGroup - 1) / kKGroup;
+    constexpr int DT = HD / 32;          // output tiles of 32 channels
+    constexpr int KS = HD / 16;          // k-steps of the score MFMA
+    constexpr int KL = 256 / (HD / 4);   // keys a pass of the K loader covers
+    __shared__ __bf16 Ks[2][KT][KP];
+    __shared__ __bf16 Vt[2][HD][VP];
+    const int s = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
+    const CallRec *rec = a.rec;
+    const int T = rec->n;
+    const int r0 = b * BQ, r1 = (r0 + BQ < T ? r0 + BQ : T) - 1;
+    const int64_t pos0 = rec->rows[0].pos;
+    const int64_t klo = pos0 + r0 + 1 - a.window > 0 ? pos0 + r0 + 1 - a.window : 0;
+    const int64_t khi = pos0 + r1;
+    const int64_t eb = klo + (int64_t)s * a.split;
+    if (eb > khi) return;
+    const int64_t ee = eb + a.split - 1 < khi ? eb + a.split - 1 : khi;  // last key of the split
+    const int ntiles = (int)((ee - eb + KT) / KT);
+    const SlotDesc &sd = slot_at(a.tab, rec->rows[0].seq, a.n_ord, a.ord, a.slot);
+    const int cap = sd.cap;
+    const int Q = a.nh * HD;
+
+    // ---- this lane's query vector
+    const int qv = wave * 32 + (lane & 31), h = qv / BQ, r = r0 + qv % BQ;
+    const bool rok = r < T;
+    const int64_t p = pos0 + (rok ? r : r1);
+    const int64_t lo_r = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+    bf16x8_t qb[KS];
+    {
+        const float *qrow = a.qp + (size_t)(rok ? r : r1) * Q + (size_t)(kh * REP + h) * HD;
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            const int d = 16 * t + 8 * g;
+            float4 x0 = *reinterpret_cast<const float4 *>(qrow + d);
+            float4 x1 = *reinterpret_cast<const float4 *>(qrow + d + 4);
+            if (Q8 && a.field) {
+                const float4 c0 = *reinterpret_cast<const float4 *>(sd.kcol + kh * HD + d);
+                const float4 c1 = *reinterpret_cast<const float4 *>(sd.kcol + kh * HD + d + 4);
+                x0.x *= c0.x; x0.y *= c0.y; x0.z *= c0.z; x0.w *= c0.w;
+                x1.x *= c1.x; x1.y *= c1.y; x1.z *= c1.z; x1.w *= c1.w;
+            }
+            qb[t][0] = (__bf16)x0.x; qb[t][1] = (__bf16)x0.y; qb[t][2] = (__bf16)x0.z; qb[t][3] = (__bf16)x0.w;
+            qb[t][4] = (__bf16)x1.x; qb[t][5] = (__bf16)x1.y; qb[t][6] = (__bf16)x1.z; qb[t][7] = (__bf16)x1.w;
+        }
+    }
+
+    // ---- loaders.  K: thread (key tid/(HD/4) + KL*i, channels 4*(tid%(HD/4))).
+    // V: thread (slot chunk ci = tid / (HD/4) (+ 256/(HD/4) per pass), channels
+    // 4*(tid%(HD/4))); chunk ci holds keys 16(ci/2) + 4(ci%2) + {0..3} and
+    // 16(ci/2) + 8 + 4(ci%2) + {0..3} in slots 8ci .. 8ci+7.
+    constexpr int KPASS = KT / KL;           // K rows per thread
+    constexpr int VPASS = (KT / 8) / KL;     // V slot chunks per thread
+    const int lc = tid % (HD / 4), lk = tid / (HD / 4);
+    float4 kr[KPASS], vr[VPASS][8];
+    float ksr[KPASS], vsr[VPASS][8];
+    auto key_row = [&](int64_t e) -> size_t {
+        e = e < ee ? e : ee;
+        return (size_t)kh * cap + (size_t)(e % cap);
+    };
+    auto gload = [&](int tile) {
+        const int64_t t0 = eb + (int64_t)tile * KT;
+#pragma unroll
+        for (int i = 0; i < KPASS; ++i) {
+            const size_t row = key_row(t0 + lk + KL * i);
+            if (Q8) {
+                const char4 c = *reinterpret_cast<const char4 *>(sd.kc + row * HD + 4 * lc);
+                kr[i] = make_float4((float)c.x, (float)c.y, (float)c.z, (float)c.w);
+                ksr[i] = sd.ks[row * NGK + (4 * lc) / kKGroup];
+            } else {
+                kr[i] = *reinterpret_cast<const float4 *>(sd.k + row * HD + 4 * lc);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < VPASS; ++i) {
+            const int ci = lk + KL * i;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kk = 16 * (ci >> 1) + 8 * (j >> 2) + 4 * (ci & 1) + (j & 3);
+                const size_t row = key_row(t0 + kk);
+                if (Q8) {
+                    const char4 c = *reinterpret_cast<const char4 *>(sd.vc + row * HD + 4 * lc);
+                    vr[i][j] = make_float4((float)c.x, (float)c.y, (float)c.z, (float)c.w);
+                    vsr[i][j] = sd.vs[row];
+                } else {
+                    vr[i][j] = *reinterpret_cast<const float4 *>(sd.v + row * HD + 4 * lc);
+                }
+            }
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < KPASS; ++i) {
+            float4 x = kr[i];
+            if (Q8) { x.x *= ksr[i]; x.y *= ksr[i]; x.z *= ksr[i]; x.w *= ksr[i]; }
+            __bf16 *dst = &Ks[buf][lk + KL * i][4 * lc];
+            dst[0] = (__bf16)x.x; dst[1] = (__bf16)x.y; dst[2] = (__bf16)x.z; dst[3] = (__bf16)x.w;
+        }
+#pragma unroll
+        for (int i = 0; i < VPASS; ++i) {
+            const int ci = lk + KL * i;
+            bf16x8_t col[4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float4 x = vr[i][j];
+                if (Q8) { x.x *= vsr[i][j]; x.y *= vsr[i][j]; x.z *= vsr[i][j]; x.w *= vsr[i][j]; }
+                col[0][j] = (__bf16)x.x; col[1][j] = (__bf16)x.y; col[2][j] = (__bf16)x.z; col[3][j] = (__bf16)x.w;
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<bf16x8_t *>(&Vt[buf][4 * lc + c][8 * ci]) = col[c];
+        }
+    };
+
+    f32x16_t o[DT];
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
+    float m = -INFINITY, l = 0.f;
+    const float scale = 1.0f / sqrtf((float)HD);
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int tile = 0; tile < ntiles; ++tile) {
+        const bool more = tile + 1 < ntiles;
+        if (more) gload(tile + 1);
+        const int64_t t0 = eb + (int64_t)tile * KT;
+        // scores of the two 32-key blocks
+        f32x16_t sc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sc[kb][e] = 0.f;
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                const bf16x8_t kv = *reinterpret_cast<const bf16x8_t *>(&Ks[buf][32 * kb + (lane & 31)][16 * t + 8 * g]);
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[t], sc[kb], 0, 0, 0);
+            }
+        }
+        // mask and tile maximum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t key = t0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+                const bool vis = rok && key >= lo_r && key <= p && key <= ee;
+                const float v = vis ? sc[kb][e] * scale : -INFINITY;
+                sc[kb][e] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(m, mx);
+        const float alpha = mn == -INFINITY ? 1.f : expf(m - mn);
+        m = mn;
+        bf16x8_t pb[2][2];
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float pv = mn == -INFINITY ? 0.f : expf(sc[kb][e] - mn);
+                ls += pv;
+                pb[kb][e >> 3][e & 7] = (__bf16)pv;
+            }
+        l = l * alpha + ls;
+#pragma unroll
+        for (int t = 0; t < DT; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+        // O^T += V^T P^T over the 64 keys (4 MFMA k-steps of 16 slots)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int t = 0; t < DT; ++t) {
+                    const bf16x8_t vv = *reinterpret_cast<const bf16x8_t *>(
+                        &Vt[buf][32 * t + (lane & 31)][32 * kb + 16 * mm + 8 * g]);
+                    o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[kb][mm], o[t], 0, 0, 0);
+                }
+        if (more) {
+            sstore(buf ^ 1);
+            __syncthreads();
+            buf ^= 1;
+        }
+    }
+    l += __shfl_xor(l, 32);
+    if (!rok) return;
+    const size_t pstride = (size_t)REP * (HD + 2);
+    float *mine = a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride + (size_t)h * (HD + 2);
+    if (g == 0) {
+        mine[0] = m;
+        mine[1] = l;
+    }
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            float *dst = mine + 2 + 32 * t + 8 * q4 + 4 * g;
+            dst[0] = o[t][4 * q4 + 0];
+            dst[1] = o[t][4 * q4 + 1];
+            dst[2] = o[t][4 * q4 + 2];
+            dst[3] = o[t][4 * q4 + 3];
+        }
+}
+
 template <int HD, int REP>
 hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     if (T < 0) {  // decode kernel: -T rows, each of its own sequence and position
         dim3 grid(a.max_split, a.nk, -T), block(256);
         if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1>), grid, block, 0, s, a);
         else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0>), grid, block, 0, s, a);
+    } else if (a.blk > 0) {
+        if constexpr (HD == 128 && 128 % REP == 0) {
+            if (a.blk != 128 / REP) return hipErrorInvalidValue;
+            if (a.nsplit < 1 || a.nsplit > a.max_split) return hipErrorInvalidValue;
+            dim3 grid(a.nsplit, a.nk, (T + a.blk - 1) / a.blk), block(256);
+            if (a.q8) hipLaunchKernelGGL((k_fattn<HD, REP, 1>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_fattn<HD, REP, 0>), grid, block, 0, s, a);
+        } else {
+            return hipErrorInvalidValue;
+        }
     } else {
         dim3 grid(a.max_split, a.nk, T), block(256);
         if (a.q8) hipLaunchKernelGGL((k_attn<HD, REP, 1>), grid, block, 0, s, a);
@@ -576,9 +832,12 @@ hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
 }
 
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
-    if (a.split <= 0 || a.split > 256 || T <= 0) return hipErrorInvalidValue;
+    if (a.split <= 0 || T <= 0 || (a.blk == 0 && a.split > 256) || (a.blk > 0 && a.split % 64))
+        return hipErrorInvalidValue;
     return launch_hd(a, T, s);
 }
+
+int attn_chunk_block(int hd, int rep) { return hd == 128 && 128 % rep == 0 ? 128 / rep : 0; }
 
 int attn_dec_max_split(int hd) {
     const int kb = 256 / (hd / 4);

@@ -162,6 +162,11 @@ struct AttnArgs {
     const float *rope;   // [max_ctx][hd] RoPE table of the layer's kind: cos half, sin half
     const float *sq;     // [Q]
     int32_t no_write;    // benchmark only: leave the cache row of p untouched
+    // multi-row calls on MFMA (k_fattn): rows per block (attn_chunk_block), and
+    // then `split` keys per workgroup of the block's key range, a multiple of
+    // 64; 0: one row per workgroup (k_attn), split <= 256
+    int32_t blk;
+    int32_t nsplit;      // k_fattn: grid.x, the most splits a block has
 };
 // Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
@@ -169,6 +174,9 @@ hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
 // sequence of a batch) from the raw projections: grid (max_split, nk, T), then
 // the merge.
 hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s);
+// Rows per block of the MFMA chunk attention for this geometry, or 0 when it
+// does not serve it (head dim other than 128).
+int attn_chunk_block(int hd, int rep);
 // Keys a one-row workgroup takes at most for head dim hd.
 int attn_dec_max_split(int hd);
 

@@ -116,3 +116,33 @@ def test_2b_q8_long_context_decode(model2b, D):
     toks = synth.make_tokens(2, cfg["vocab"], seq=11)
     check_pair(run_pair(g, o, [toks[:1], toks[1:]], 4, "last_loop"), COS, DLOGIT, "2b q8 decode")
     g.close()
+
+
+def test_2b_long_chunk_on_loaded_context(model2b, D):
+    """A 160-row call at position 3000: the MFMA chunk attention with several
+    row blocks (the last one ragged) and several key splits per block."""
+    cfg, w = model2b
+    k, v = _rows(cfg, 3000, 1, seed=12)
+    g = D.Dory(cfg, w, max_ctx=3200, max_chunk=512)
+    o = O.Oracle(cfg, w, max_ctx=3200)
+    g.kv_load(k, v, "last_loop", 1)
+    o.kv_load(k, v, "last_loop", 1)
+    toks = synth.make_tokens(161, cfg["vocab"], seq=13)
+    say("2b chunk of 160 at 3000 + 1 decode")
+    check_pair(run_pair(g, o, [toks[:160], toks[160:]], 2, "last_loop"), COS, DLOGIT, "2b long chunk")
+    g.close()
+
+
+def test_2b_q8_prompt_crosses_freeze_and_wrap(model2b, D):
+    """q8_2f prompt in calls of 40, 30, 100, 30 rows: the field freezes inside
+    the second call, the full ring (full_window 96 + 100 rows) wraps in the
+    last, and every call's attention reads dequantised codes."""
+    cfg, w = model2b
+    cfg = dict(cfg, full_window=96)
+    toks = synth.make_tokens(201, cfg["vocab"], seq=14)
+    say("2b q8 prompt 40+30+100+30 + 1 decode")
+    g = D.Dory(cfg, w, max_ctx=400, max_chunk=100, kv_encoding="q8_2f")
+    o = O.Oracle(cfg, w, max_ctx=400, kv_q8=True)
+    calls = [toks[:40], toks[40:70], toks[70:170], toks[170:200], toks[200:]]
+    check_pair(run_pair(g, o, calls, 2, "last_loop"), COS, DLOGIT, "2b q8 prompt")
+    g.close()
