@@ -153,6 +153,71 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
     a.z[(size_t)r * Q + hq * hd + d] = y / (1.0f + expf(-(gate * sgv)));
 }
 
+
+// The merge of multi-row calls: workgroup per (row r, kv head kh), thread per
+// (q head of the group, channel); each walks the row's splits in order with a
+// running (max, sum, acc).  Same arithmetic as k_attn_merge, laid out for many
+// rows with few splits each.
+template <int Q8>
+__global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
+    const int r = blockIdx.x, kh = blockIdx.y;
+    const int hd = a.hd, rep = a.nh / a.nk, Q = a.nh * hd, ld = 2 * Q + 2 * a.nk * hd;
+    const int64_t p = a.rec->rows[r].pos;
+    int nsplit;
+    if (a.blk > 0) {
+        const int rb0 = r / a.blk * a.blk, rb1 = (rb0 + a.blk < a.rec->n ? rb0 + a.blk : a.rec->n) - 1;
+        const int64_t pos0 = a.rec->rows[0].pos;
+        const int64_t klo = pos0 + rb0 + 1 - a.window > 0 ? pos0 + rb0 + 1 - a.window : 0;
+        nsplit = (int)((pos0 + rb1 - klo + a.split) / a.split);
+    } else {
+        const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+        nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
+    }
+    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    const size_t pstride = (size_t)rep * (hd + 2);
+    const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride;
+    for (int c = threadIdx.x; c < rep * hd; c += 256) {
+        const int h = c / hd, d = c % hd, hq = kh * rep + h;
+        const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + d];
+        const float sgv = a.sg[hq * hd + d];
+        const float vcol = field ? slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + d] : 1.f;
+        const float *ph = all + (size_t)h * (hd + 2);
+        float M = -INFINITY, L = 0.f, acc = 0.f;
+        int j = 0;
+        for (; j + 4 <= nsplit; j += 4) {
+            float m[4], l[4], v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float *pj = ph + (size_t)(j + u) * pstride;
+                m[u] = pj[0];
+                l[u] = pj[1];
+                v[u] = pj[2 + d];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (m[u] == -INFINITY) continue;  // a split with no key this row sees
+                const float Mn = fmaxf(M, m[u]);
+                const float c0 = expf(M - Mn), c1 = expf(m[u] - Mn);
+                L = L * c0 + l[u] * c1;
+                acc = acc * c0 + v[u] * c1;
+                M = Mn;
+            }
+        }
+        for (; j < nsplit; ++j) {
+            const float *pj = ph + (size_t)j * pstride;
+            const float mj = pj[0];
+            if (mj == -INFINITY) continue;
+            const float Mn = fmaxf(M, mj);
+            const float c0 = expf(M - Mn), c1 = expf(mj - Mn);
+            L = L * c0 + pj[1] * c1;
+            acc = acc * c0 + pj[2 + d] * c1;
+            M = Mn;
+        }
+        const float y = acc / L * vcol;
+        a.z[(size_t)r * Q + hq * hd + d] = y / (1.0f + expf(-(gate * sgv)));
+    }
+}
+
 // Grouped-query attention of one row over keys max(p+1-window, 0) ..= p for the
 // REP q heads of one kv head (dory.rs `attn_layer`, the per-(row, kv head)
 // task; kv_cache.rs `attend_group_upto` for the q8_2f rows).
@@ -792,12 +857,18 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // one-row calls: 16 waves per head channel block; multi-row calls have
-    // fewer, longer splits and many more rows, so 4
-    dim3 mgrid(T < 0 ? -T : T, a.nh, (HD + 63) / 64);
-    const int waves = T > 1 ? 4 : 16;
-    if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(64 * waves), 0, s, a);
-    else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(64 * waves), 0, s, a);
+    // one row: 16 waves per head channel block walk the splits in parallel;
+    // several rows: a workgroup per (row, kv head)
+    const int rows = T < 0 ? -T : T;
+    if (rows == 1) {
+        dim3 mgrid(1, a.nh, (HD + 63) / 64);
+        if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(1024), 0, s, a);
+        else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(1024), 0, s, a);
+    } else {
+        dim3 mgrid(rows, a.nk);
+        if (a.q8) hipLaunchKernelGGL((k_attn_merge_rows<1>), mgrid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_attn_merge_rows<0>), mgrid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
 }
 

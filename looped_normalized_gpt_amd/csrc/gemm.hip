@@ -195,12 +195,87 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, 
         }
 }
 
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Few-row projections (batched decode, short chunks): M <= 16*MT rows against
+// bf16 weights, on v_mfma_f32_16x16x32_bf16.  Workgroup = 16 weight rows
+// (output columns n0 .. n0+15), its 4 waves take the K blocks of 128 in turn
+// and add their partial tiles in LDS at the end.  Every weight byte is read
+// once, straight into registers.  Operand layout of the 16x16x32 MFMA: lane l
+// supplies row l % 16 and k-slots 8 (l/16) .. +7 of A (and of B), and receives
+// C[4 (l/16) + i][l % 16] in accumulator i.  The sum over k does not care which
+// k sits in which slot as long as A and B agree, so lane group g takes the 32
+// contiguous k at 32g of each block (one 64-byte run of a weight row) and
+// feeds them to 4 MFMAs, 8 at a time; the activations are read the same way.
+template <int MT>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const float *__restrict__ A, int lda, const GemmW W, int N,
+                                                     int K, float *__restrict__ C, int ldc, int M) {
+    __shared__ float red[4][MT][16][17];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int n0 = blockIdx.x * 16;
+    const int n = n0 + r < N ? n0 + r : N - 1;
+    const uint16_t *wrow = seg_row<uint16_t>(W, n, K);
+    const float *arow[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + r < M ? 16 * mt + r : M - 1;
+        arow[mt] = A + (size_t)m * lda;
+    }
+    f32x4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int nkb = K / 128;
+    for (int kb = wave; kb < nkb; kb += 4) {
+        const int k = kb * 128 + 32 * g;
+        uint4 wv[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wv[t] = *reinterpret_cast<const uint4 *>(wrow + k + 8 * t);
+        float4 av[MT][8];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) av[mt][t] = *reinterpret_cast<const float4 *>(arow[mt] + k + 4 * t);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const bf16x8 b = __builtin_bit_cast(bf16x8, wv[t]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const float4 x0 = av[mt][2 * t], x1 = av[mt][2 * t + 1];
+                bf16x8 a;
+                a[0] = (__bf16)x0.x; a[1] = (__bf16)x0.y; a[2] = (__bf16)x0.z; a[3] = (__bf16)x0.w;
+                a[4] = (__bf16)x1.x; a[5] = (__bf16)x1.y; a[6] = (__bf16)x1.z; a[7] = (__bf16)x1.w;
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mt], 0, 0, 0);
+            }
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave][mt][4 * g + i][r] = acc[mt][i];
+    __syncthreads();
+    for (int idx = tid; idx < MT * 256; idx += 256) {
+        const int mt = idx >> 8, mm = (idx >> 4) & 15, c = idx & 15;
+        const int m = 16 * mt + mm, nn = n0 + c;
+        if (m < M && nn < N)
+            C[(size_t)m * ldc + nn] = red[0][mt][mm][c] + red[1][mt][mm][c] + red[2][mt][mm][c] + red[3][mt][mm][c];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int wtype, const float *A, int lda, const GemmW &Wb, int N, int K, float *C, int ldc,
                        int M, hipStream_t s) {
     if (K % 4 || lda % 4 || Wb.nseg < 1 || Wb.nseg > 4 || Wb.seg_end[Wb.nseg - 1] != N) return hipErrorInvalidValue;
     const GemmW W = Wb;
+    if (wtype == kBF16 && M <= 64 && K % 128 == 0 && lda % 4 == 0) {
+        const dim3 grid((N + 15) / 16);
+        if (M <= 16) hipLaunchKernelGGL((k_gemm_skinny<1>), grid, dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
+        else if (M <= 32) hipLaunchKernelGGL((k_gemm_skinny<2>), grid, dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
+        else hipLaunchKernelGGL((k_gemm_skinny<4>), grid, dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
+        return hipGetLastError();
+    }
     if (wtype == kBF16 && M >= 32 && K % 8 == 0) {
         // bf16 MFMA; narrower tiles when the 128-wide ones would leave CUs idle
         const int mt = (M + 127) / 128;
