@@ -56,6 +56,7 @@ struct dory {
     // device scratch
     float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
     float *z = nullptr, *zn = nullptr, *ga = nullptr, *un = nullptr, *kstage = nullptr;
+    uint16_t *xb = nullptr, *znb = nullptr, *unb = nullptr;  // bf16 copies of x, zn, un (GEMM operands)
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     CallRec *rec = nullptr;
@@ -279,7 +280,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s));
     }
     AttnArgs aa{};
     aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part;
@@ -350,8 +351,8 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         a.src = h->z; a.y = h->o; a.rec = h->rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->Q, M, q.s));
-        LAUNCH(launch_gemm(h->wt, h->zn, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s));
+        LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->znb, h->Q, M, q.s));
+        LAUNCH(launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s));
     }
     return DORY_OK;
 }
@@ -370,9 +371,9 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
         d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
-        LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, h->un, h->F, M, q.s));
-        LAUNCH(launch_gemm(h->wt, h->un, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s));
+        LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
+        LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, h->un, h->unb, h->F, M, q.s));
+        LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s));
     }
     return DORY_OK;
 }
@@ -386,7 +387,7 @@ int enqueue(Enq &q) {
     dory_t *h = q.h;
     const dory_config &c = h->cfg;
     const int T = q.T;
-    LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], q.s));
+    LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], T > 1 ? h->xb : nullptr, q.s));
     const int P = passes(h, q.loops);
     auto rows_of = [&](int k) {
         if (k < c.n_in || k >= c.n_in + c.n_rec * q.loops) return T;
@@ -421,7 +422,7 @@ int enqueue(Enq &q) {
             rs.n_prev = T;
         } else {
             rs.h = h->hb[(k - 1) % 2]; rs.o = h->o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
-            rs.h_out = h->hb[k % 2]; rs.tap_pass = k - 1;
+            rs.h_out = h->hb[k % 2]; rs.hb_out = h->xb; rs.tap_pass = k - 1;
             rs.n_prev = rows_of(k - 1);
             if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, h->rec, q.s));
         }
@@ -443,12 +444,13 @@ int enqueue(Enq &q) {
         LAUNCH(launch_gemv(h->wt, kProResolve, kEpiHead, a, q.s));
     } else {
         rf.h_out = h->hb[P % 2];
+        rf.hb_out = h->xb;
         LAUNCH(launch_resolve_rows(rf, h->H, T, h->rec, q.s));
         if (q.want_logits && !q.batch) {
             a.row = T - 1; a.src = h->hb[P % 2];
             LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));
         } else if (q.want_logits) {
-            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->H, gemm_w(h->w.head, h->V), h->V, h->H, h->hlog, h->V, T, q.s));
+            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->xb, h->H, gemm_w(h->w.head, h->V), h->V, h->H, h->hlog, h->V, T, q.s));
             LAUNCH(launch_logits_rows(h->hlog, h->w.logit_scale, h->V, T, h->rec, q.s));
         }
     }
@@ -583,6 +585,9 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->zn, (size_t)chunk * h->Q));
     CREATE_CHECK(dmalloc(h, &h->ga, (size_t)chunk * 2 * h->F));   // gate | up per row
     CREATE_CHECK(dmalloc(h, &h->un, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->xb, (size_t)chunk * h->H));
+    CREATE_CHECK(dmalloc(h, &h->znb, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->unb, (size_t)chunk * h->F));
     CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_v, (size_t)chunk * h->KV));
@@ -980,16 +985,16 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_gemv(h->wt, kProResolve, kEpiHead, a, s);
             break;
         case 6:
-            e = launch_gemm(h->wt, h->hb[0], h->H, qkvg_w(h, l->w), ld, h->H, h->qkvg, ld, MC, s);
+            e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, qkvg_w(h, l->w), ld, h->H, h->qkvg, ld, MC, s);
             break;
         case 7:
-            e = launch_gemm(h->wt, h->zn, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->o, h->H, MC, s);
+            e = launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->o, h->H, MC, s);
             break;
         case 8:
-            e = launch_gemm(h->wt, h->hb[0], h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
+            e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
             break;
         case 9:
-            e = launch_gemm(h->wt, h->un, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s);
+            e = launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s);
             break;
         default:
             chunk_split(h, h->last_pos0, h->last_T, aa);

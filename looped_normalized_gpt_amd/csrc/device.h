@@ -10,6 +10,8 @@ namespace dk {
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// fp32 -> bf16 bits, round to nearest even
+__device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
 // Cross-lane steps on wave64 without LDS traffic: DPP quad permutes and row
 // mirrors inside 16-lane rows, a swizzle across the two rows of a 32-lane half,
@@ -86,6 +88,8 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
         for (int i = tid; i < H; i += 256) xs[i] = rs.st[(size_t)r * H + i];
         if (writer && rs.h_out)
             for (int i = tid; i < H; i += 256) rs.h_out[(size_t)r * H + i] = xs[i];
+        if (writer && rs.hb_out)
+            for (int i = tid; i < H; i += 256) rs.hb_out[(size_t)r * H + i] = f2bf(xs[i]);
         return;
     }
     const float *h = rs.h + (size_t)r * H;
@@ -156,6 +160,10 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
     if (writer && rs.h_out) {
         float *ho = rs.h_out + (size_t)r * H;
         for (int i = tid; i < H; i += 256) ho[i] = xs[i];
+    }
+    if (writer && rs.hb_out) {
+        uint16_t *hb = rs.hb_out + (size_t)r * H;
+        for (int i = tid; i < H; i += 256) hb[i] = f2bf(xs[i]);
     }
 }
 

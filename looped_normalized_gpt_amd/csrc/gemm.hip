@@ -100,7 +100,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // lane l supplies row (l % 32) and k = 8 (l / 32) .. +7 of A (and of B); it
 // receives C[8 (j/4) + 4 (l/32) + j%4][l % 32] in accumulator j.
 template <int BN>
-__global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, int lda,
+__global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t *__restrict__ A, int lda,
                                                    const GemmW W, int N, int K,
                                                    float *__restrict__ C, int ldc, int M) {
     constexpr int BM = 128, BK = 32, LDK = BK + 8;  // padded LDS rows (bf16)
@@ -110,17 +110,16 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-    // loaders: A rows tid/2 (128 rows), 16 floats each; B rows tid/2 (< BN), 16 bf16 each
+    // loaders: A rows tid/2 (128 rows), 16 bf16 each; B rows tid/2 (< BN), 16 bf16 each
     const int lr = tid >> 1, lc = (tid & 1) * 16;
-    float4 ra[4];
+    uint4 ra[2];
     uint4 rb[2];
     auto gload = [&](int k0) {
         const int m = m0 + lr, k = k0 + lc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = m < M && k + 4 * i < K;
-            ra[i] = ok ? *reinterpret_cast<const float4 *>(A + (size_t)m * lda + k + 4 * i)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < 2; ++i) {
+            const bool ok = m < M && k + 8 * i < K;
+            ra[i] = ok ? *reinterpret_cast<const uint4 *>(A + (size_t)m * lda + k + 8 * i) : make_uint4(0, 0, 0, 0);
         }
         const int n = n0 + lr;
         const uint16_t *wr = seg_row<uint16_t>(W, n < N ? n : 0, K);
@@ -131,16 +130,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, 
         }
     };
     auto sstore = [&](int buf) {
-        bf16x8 v0, v1;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            v0[4 * i + 0] = (__bf16)ra[i].x; v0[4 * i + 1] = (__bf16)ra[i].y;
-            v0[4 * i + 2] = (__bf16)ra[i].z; v0[4 * i + 3] = (__bf16)ra[i].w;
-            v1[4 * i + 0] = (__bf16)ra[2 + i].x; v1[4 * i + 1] = (__bf16)ra[2 + i].y;
-            v1[4 * i + 2] = (__bf16)ra[2 + i].z; v1[4 * i + 3] = (__bf16)ra[2 + i].w;
-        }
-        *reinterpret_cast<bf16x8 *>(&As[buf][lr][lc]) = v0;
-        *reinterpret_cast<bf16x8 *>(&As[buf][lr][lc + 8]) = v1;
+        *reinterpret_cast<uint4 *>(&As[buf][lr][lc]) = ra[0];
+        *reinterpret_cast<uint4 *>(&As[buf][lr][lc + 8]) = ra[1];
         if (lr < BN) {
             *reinterpret_cast<uint4 *>(&Bs[buf][lr][lc]) = rb[0];
             *reinterpret_cast<uint4 *>(&Bs[buf][lr][lc + 8]) = rb[1];
@@ -198,93 +189,121 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const float *__restrict__ A, 
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Few-row projections (batched decode, short chunks): M <= 16*MT rows against
-// bf16 weights, on v_mfma_f32_16x16x32_bf16.  Workgroup = 16 weight rows
-// (output columns n0 .. n0+15), its 4 waves take the K blocks of 128 in turn
-// and add their partial tiles in LDS at the end.  Every weight byte is read
-// once, straight into registers.  Operand layout of the 16x16x32 MFMA: lane l
-// supplies row l % 16 and k-slots 8 (l/16) .. +7 of A (and of B), and receives
-// C[4 (l/16) + i][l % 16] in accumulator i.  The sum over k does not care which
-// k sits in which slot as long as A and B agree, so lane group g takes the 32
-// contiguous k at 32g of each block (one 64-byte run of a weight row) and
-// feeds them to 4 MFMAs, 8 at a time; the activations are read the same way.
-template <int MT>
-__global__ __launch_bounds__(256) void k_gemm_skinny(const float *__restrict__ A, int lda, const GemmW W, int N,
+// Few-row projections (batched decode, short chunks): M <= 16*MT rows of bf16
+// activations against bf16 weights, on v_mfma_f32_16x16x32_bf16.  Workgroup =
+// 16*NT weight rows (output columns); its 4 waves take the K blocks of 128 in
+// turn, two blocks in flight per wave (the next block's loads are issued before
+// the current block's MFMAs), and add their partial tiles in LDS at the end.
+// Every weight byte is read once, straight into registers.
+// Operand layout of the 16x16x32 MFMA: lane l supplies row l % 16 and k-slots
+// 8 (l/16) .. +7 of A (and of B), and receives C[4 (l/16) + i][l % 16] in
+// accumulator i.  The sum over k does not care which k sits in which slot as
+// long as A and B agree, so lane group g takes the 32 contiguous k at 32g of a
+// block (one 64-byte run of a row) and feeds them to 4 MFMAs, 8 at a time.
+template <int MT, int NT>
+__global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict__ A, int lda, const GemmW W, int N,
                                                      int K, float *__restrict__ C, int ldc, int M) {
-    __shared__ float red[4][MT][16][17];
+    __shared__ float red[4][NT * MT][16][17];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;
-    const int n = n0 + r < N ? n0 + r : N - 1;
-    const uint16_t *wrow = seg_row<uint16_t>(W, n, K);
-    const float *arow[MT];
+    const int n0 = blockIdx.x * 16 * NT;
+    const uint16_t *wrow[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int n = n0 + 16 * nt + r < N ? n0 + 16 * nt + r : N - 1;
+        wrow[nt] = seg_row<uint16_t>(W, n, K) + 32 * g;
+    }
+    const uint16_t *arow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + r < M ? 16 * mt + r : M - 1;
-        arow[mt] = A + (size_t)m * lda;
+        arow[mt] = A + (size_t)m * lda + 32 * g;
     }
-    f32x4_t acc[MT];
+    f32x4_t acc[NT][MT];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int nkb = K / 128;
-    for (int kb = wave; kb < nkb; kb += 4) {
-        const int k = kb * 128 + 32 * g;
-        uint4 wv[4];
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) wv[t] = *reinterpret_cast<const uint4 *>(wrow + k + 8 * t);
-        float4 av[MT][8];
+        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    uint4 w0[NT][4], a0[MT][4], w1[NT][4], a1[MT][4];
+    auto load = [&](uint4 (&wv)[NT][4], uint4 (&av)[MT][4], int kb) {
+        const int k = kb * 128;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) wv[nt][t] = *reinterpret_cast<const uint4 *>(wrow[nt] + k + 8 * t);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int t = 0; t < 8; ++t) av[mt][t] = *reinterpret_cast<const float4 *>(arow[mt] + k + 4 * t);
+            for (int t = 0; t < 4; ++t) av[mt][t] = *reinterpret_cast<const uint4 *>(arow[mt] + k + 8 * t);
+    };
+    auto mma = [&](const uint4 (&wv)[NT][4], const uint4 (&av)[MT][4]) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const bf16x8 b = __builtin_bit_cast(bf16x8, wv[t]);
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const float4 x0 = av[mt][2 * t], x1 = av[mt][2 * t + 1];
-                bf16x8 a;
-                a[0] = (__bf16)x0.x; a[1] = (__bf16)x0.y; a[2] = (__bf16)x0.z; a[3] = (__bf16)x0.w;
-                a[4] = (__bf16)x1.x; a[5] = (__bf16)x1.y; a[6] = (__bf16)x1.z; a[7] = (__bf16)x1.w;
-                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mt], 0, 0, 0);
-            }
-        }
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, av[mt][t]), __builtin_bit_cast(bf16x8, wv[nt][t]), acc[nt][mt],
+                        0, 0, 0);
+    };
+    const int nkb = K / 128;
+    if (wave < nkb) load(w0, a0, wave);
+    for (int kb = wave; kb < nkb; kb += 8) {
+        if (kb + 4 < nkb) load(w1, a1, kb + 4);
+        mma(w0, a0);
+        if (kb + 8 < nkb) load(w0, a0, kb + 8);
+        if (kb + 4 < nkb) mma(w1, a1);
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) red[wave][mt][4 * g + i][r] = acc[mt][i];
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][nt * MT + mt][4 * g + i][r] = acc[nt][mt][i];
     __syncthreads();
-    for (int idx = tid; idx < MT * 256; idx += 256) {
-        const int mt = idx >> 8, mm = (idx >> 4) & 15, c = idx & 15;
-        const int m = 16 * mt + mm, nn = n0 + c;
+    for (int idx = tid; idx < NT * MT * 256; idx += 256) {
+        const int tt = idx >> 8, mm = (idx >> 4) & 15, c = idx & 15;
+        const int nt = tt / MT, mt = tt % MT;
+        const int m = 16 * mt + mm, nn = n0 + 16 * nt + c;
         if (m < M && nn < N)
-            C[(size_t)m * ldc + nn] = red[0][mt][mm][c] + red[1][mt][mm][c] + red[2][mt][mm][c] + red[3][mt][mm][c];
+            C[(size_t)m * ldc + nn] = red[0][tt][mm][c] + red[1][tt][mm][c] + red[2][tt][mm][c] + red[3][tt][mm][c];
     }
+}
+
+template <int MT>
+void launch_skinny(const uint16_t *A, int lda, const GemmW &W, int N, int K, float *C, int ldc, int M,
+                   hipStream_t s) {
+    if ((N + 15) / 16 >= 512)
+        hipLaunchKernelGGL((k_gemm_skinny<MT, 2>), dim3((N + 31) / 32), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
+    else
+        hipLaunchKernelGGL((k_gemm_skinny<MT, 1>), dim3((N + 15) / 16), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(int wtype, const float *A, int lda, const GemmW &Wb, int N, int K, float *C, int ldc,
-                       int M, hipStream_t s) {
+hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &Wb, int N, int K,
+                       float *C, int ldc, int M, hipStream_t s) {
     if (K % 4 || lda % 4 || Wb.nseg < 1 || Wb.nseg > 4 || Wb.seg_end[Wb.nseg - 1] != N) return hipErrorInvalidValue;
     const GemmW W = Wb;
-    if (wtype == kBF16 && M <= 64 && K % 128 == 0 && lda % 4 == 0) {
-        const dim3 grid((N + 15) / 16);
-        if (M <= 16) hipLaunchKernelGGL((k_gemm_skinny<1>), grid, dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
-        else if (M <= 32) hipLaunchKernelGGL((k_gemm_skinny<2>), grid, dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
-        else hipLaunchKernelGGL((k_gemm_skinny<4>), grid, dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
-        return hipGetLastError();
-    }
-    if (wtype == kBF16 && M >= 32 && K % 8 == 0) {
-        // bf16 MFMA; narrower tiles when the 128-wide ones would leave CUs idle
-        const int mt = (M + 127) / 128;
-        if ((long)mt * ((N + 127) / 128) >= 256) {
-            hipLaunchKernelGGL((k_gemm_mfma<128>), dim3((N + 127) / 128, mt), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
-        } else {
-            hipLaunchKernelGGL((k_gemm_mfma<64>), dim3((N + 63) / 64, mt), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
+    if (wtype == kBF16 && Ab && lda % 8 == 0) {
+        if (M <= 64 && K % 128 == 0) {
+            if (M <= 16) launch_skinny<1>(Ab, lda, W, N, K, C, ldc, M, s);
+            else if (M <= 32) launch_skinny<2>(Ab, lda, W, N, K, C, ldc, M, s);
+            else launch_skinny<4>(Ab, lda, W, N, K, C, ldc, M, s);
+            return hipGetLastError();
         }
-        return hipGetLastError();
+        if (M >= 32 && K % 8 == 0) {
+            // bf16 MFMA; narrower tiles when the 128-wide ones would leave CUs idle
+            const int mt = (M + 127) / 128;
+            if ((long)mt * ((N + 127) / 128) >= 256)
+                hipLaunchKernelGGL((k_gemm_mfma<128>), dim3((N + 127) / 128, mt), dim3(256), 0, s, Ab, lda, W, N, K,
+                                   C, ldc, M);
+            else
+                hipLaunchKernelGGL((k_gemm_mfma<64>), dim3((N + 63) / 64, mt), dim3(256), 0, s, Ab, lda, W, N, K, C,
+                                   ldc, M);
+            return hipGetLastError();
+        }
     }
     dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
     if (wtype == kBF16) hipLaunchKernelGGL((k_gemm_tiled<kBF16>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);

@@ -67,6 +67,7 @@ struct Resolve {
     const float *o;      // previous sub-layer's output [T][H] (slerp only)
     const float *alpha;  // previous sub-layer's |alpha| [H] (slerp only)
     float *h_out;        // x for this sub-layer [T][H]
+    uint16_t *hb_out;    // the same rows rounded to bf16 (the GEMMs' operand), or null
     float *inp;          // the loop's input [T][H]
     float *st;           // the loop state of every row [T][H] (batches), or null
     int32_t slerp;       // 1: e = slerp(h, o, alpha); 0: e = h
@@ -103,13 +104,15 @@ struct GemvArgs {
 hipError_t launch_gemv(int wtype, int pro, int epi, const GemvArgs &a, hipStream_t s);
 
 // Prefill row kernels.
+// The row kernels also write a bf16 copy of what they write (hb, dstb: may be
+// null) for the bf16 GEMMs that read it next.
 hipError_t launch_embed(int wtype, const void *embed, int V, int H, const CallRec *rec, int T,
-                        float *h, hipStream_t s);
+                        float *h, uint16_t *hb, hipStream_t s);
 hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s);
-hipError_t launch_rownorm(const float *src, int ld_src, float *dst, int N, int T, hipStream_t s);
+hipError_t launch_rownorm(const float *src, int ld_src, float *dst, uint16_t *dstb, int N, int T, hipStream_t s);
 // a and b rows have stride ld; dst rows stride F.
 hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su,
-                              float *dst, int F, int T, hipStream_t s);
+                              float *dst, uint16_t *dstb, int F, int T, hipStream_t s);
 
 // Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
 hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,
@@ -124,9 +127,11 @@ struct GemmW {
 };
 inline GemmW gemm_w(const void *w, int N) { return GemmW{{w, w, w, w}, {N, N, N, N}, 1}; }
 
-// C[T][ldc] (columns 0..N-1) = A[T][K] . W[N][K]^T, fp32 accumulation.
-hipError_t launch_gemm(int wtype, const float *A, int lda, const GemmW &W, int N, int K, float *C,
-                       int ldc, int T, hipStream_t s);
+// C[T][ldc] (columns 0..N-1) = A[T][K] . W[N][K]^T, fp32 accumulation.  A is
+// given in fp32 and, for bf16 weights, also rounded to bf16 (Ab, same lda):
+// the bf16 MFMA kernels read Ab, the fp32 tiled kernel reads A.
+hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &W, int N, int K,
+                       float *C, int ldc, int T, hipStream_t s);
 
 // Attention.
 struct PrepArgs {
