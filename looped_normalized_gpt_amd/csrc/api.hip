@@ -56,6 +56,7 @@ struct dory {
     // device scratch
     float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
     float *z = nullptr, *zn = nullptr, *ga = nullptr, *un = nullptr, *kstage = nullptr;
+    int64_t o_stride = 0;   // elements between the split-K slabs of o
     uint16_t *xb = nullptr, *znb = nullptr, *unb = nullptr;  // bf16 copies of x, zn, un (GEMM operands)
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
@@ -217,6 +218,7 @@ struct Enq {
     std::vector<int64_t> pos;    // every row's position (host copy, for the q8 freeze)
     std::vector<int> seq;        // every row's sequence
     std::vector<uint8_t> froze;  // slots whose field this call froze: [max_seqs][n_ord][kMaxLoops]
+    int o_parts = 1;             // split-K slabs of o the last output projection wrote
 };
 
 #define LAUNCH(call)                                            \
@@ -352,7 +354,10 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
     } else {
         LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->znb, h->Q, M, q.s));
-        LAUNCH(launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s));
+        const int S = gemm_pick_splits(h->wt, true, M, h->H, h->Q);
+        LAUNCH(launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s, S,
+                           h->o_stride));
+        q.o_parts = S;
     }
     return DORY_OK;
 }
@@ -373,7 +378,10 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
     } else {
         LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
         LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, h->un, h->unb, h->F, M, q.s));
-        LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s));
+        const int S = gemm_pick_splits(h->wt, true, M, h->H, h->F);
+        LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s, S,
+                           h->o_stride));
+        q.o_parts = S;
     }
     return DORY_OK;
 }
@@ -412,6 +420,8 @@ int enqueue(Enq &q) {
         Resolve rs{};
         rs.inp = h->inp;
         rs.loop_op = op;
+        rs.o_parts = q.o_parts;
+        rs.o_stride = h->o_stride;
         rs.st = q.batch ? h->st : nullptr;
         rs.n_next = M;
         if (k == 0) {
@@ -433,6 +443,8 @@ int enqueue(Enq &q) {
         prev_li = li;
     }
     Resolve rf{};
+    rf.o_parts = q.o_parts;
+    rf.o_stride = h->o_stride;
     rf.h = h->hb[(P - 1) % 2]; rf.o = h->o; rf.alpha = h->L[prev_li].w.alpha; rf.slerp = 1;
     rf.loop_op = kLoopNone; rf.inp = h->inp; rf.tap_pass = P - 1; rf.n_prev = rf.n_next = T;
     GemvArgs a{};
@@ -578,7 +590,8 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->hb[0], TH));
     CREATE_CHECK(dmalloc(h, &h->hb[1], TH));
     CREATE_CHECK(dmalloc(h, &h->inp, TH));
-    CREATE_CHECK(dmalloc(h, &h->o, TH));
+    h->o_stride = TH;
+    CREATE_CHECK(dmalloc(h, &h->o, TH * kMaxKParts));   // split-K slabs of the output projections
     CREATE_CHECK(dmalloc(h, &h->qkvg, (size_t)chunk * (2 * h->Q + 2 * h->KV)));
     CREATE_CHECK(dmalloc(h, &h->qp, (size_t)chunk * h->Q));
     CREATE_CHECK(dmalloc(h, &h->z, (size_t)chunk * h->Q));
@@ -988,13 +1001,15 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, qkvg_w(h, l->w), ld, h->H, h->qkvg, ld, MC, s);
             break;
         case 7:
-            e = launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->o, h->H, MC, s);
+            e = launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->o, h->H, MC, s,
+                            gemm_pick_splits(h->wt, true, MC, h->H, h->Q), h->o_stride);
             break;
         case 8:
             e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
             break;
         case 9:
-            e = launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s);
+            e = launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s,
+                            gemm_pick_splits(h->wt, true, MC, h->H, h->F), h->o_stride);
             break;
         default:
             chunk_split(h, h->last_pos0, h->last_T, aa);

@@ -97,10 +97,16 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
         for (int i = tid; i < H; i += 256) xs[i] = h[i];
     } else {
         // dory.rs `slerp`: x^ = norm(h), o^ = norm(o), e = norm(x^ + alpha*(o^ - x^))
+        // o: the sum of the split-K slabs of the sub-layer's output projection
         const float *o = rs.o + (size_t)r * H;
+        auto oval = [&](int i) {
+            float v = o[i];
+            for (int p = 1; p < rs.o_parts; ++p) v += o[(size_t)p * rs.o_stride + i];
+            return v;
+        };
         float sx = 0.f, so = 0.f;
         for (int i = tid; i < H; i += 256) {
-            float a = h[i], b = o[i];
+            float a = h[i], b = oval(i);
             xs[i] = a;
             sx += a * a;
             so += b * b;
@@ -109,7 +115,7 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
         const float rx = norm_factor(sx), ro = norm_factor(so);
         float se = 0.f;
         for (int i = tid; i < H; i += 256) {
-            float xh = xs[i] * rx, oh = o[i] * ro;
+            float xh = xs[i] * rx, oh = oval(i) * ro;
             float e = xh + rs.alpha[i] * (oh - xh);
             xs[i] = e;
             se += e * e;

@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled(const float *__restrict__ A,
 
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // 256 threads = 4 waves in a 2 x 2 arrangement; a wave owns a (BM/2) x (BN/2)
@@ -186,6 +187,105 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t *__restrict__ 
         }
 }
 
+
+
+// Multi-row projections (prefill chunks): 128 x 128 tiles of C, K in steps of
+// 64 through double-buffered LDS (rows padded to 72 bf16), with the global
+// loads of the next two K steps in flight in registers.  256 threads = 4 waves
+// in a 2 x 2 arrangement, each owning a 64 x 64 block as 2 x 2 tiles of
+// v_mfma_f32_32x32x16_bf16 (lane l supplies row l % 32 and k = 8 (l/32) .. +7
+// of A and of B, and receives C[8 (j/4) + 4 (l/32) + j%4][l % 32] in
+// accumulator j).  73.7 KB of LDS: two workgroups per CU.
+// Split K: workgroup z takes K range [z K/S, (z+1) K/S) and writes its partial
+// C to C + z * pstride; the caller's consumer adds the S slabs.
+__global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restrict__ A, int lda, const GemmW W, int N,
+                                                       int K, float *__restrict__ C, int ldc, int M, int S,
+                                                       size_t pstride) {
+    constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
+    __shared__ __bf16 As[2][BM][LDK];
+    __shared__ __bf16 Bs[2][BN][LDK];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int Kp = K / S, kz = blockIdx.z * Kp;
+    // loaders: row tid/2 of the A and B tiles, 32 bf16 at (tid%2)*32
+    const int lr = tid >> 1, lc = (tid & 1) * 32;
+    const int am = m0 + lr < M ? m0 + lr : M - 1;
+    const int bn = n0 + lr < N ? n0 + lr : N - 1;
+    const uint16_t *arow = A + (size_t)am * lda + kz + lc;
+    const uint16_t *brow = seg_row<uint16_t>(W, bn, K) + kz + lc;
+    u32x4_t ra0[4], rb0[4];
+    // (macros rather than lambdas over array references: the latter left the
+    // staging registers in scratch memory)
+#define GLOAD(ra, rb, ks)                                                                   \
+    do {                                                                                    \
+        const int k_ = (ks) * BK;                                                           \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) ra[i] =                               \
+            *reinterpret_cast<const u32x4_t *>(arow + k_ + 8 * i);                            \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) rb[i] =                               \
+            *reinterpret_cast<const u32x4_t *>(brow + k_ + 8 * i);                            \
+    } while (0)
+#define SSTORE(buf, ra, rb)                                                                 \
+    do {                                                                                    \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
+            *reinterpret_cast<u32x4_t *>(&As[buf][lr][lc + 8 * i]) = ra[i];                   \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
+            *reinterpret_cast<u32x4_t *>(&Bs[buf][lr][lc + 8 * i]) = rb[i];                   \
+    } while (0)
+#define COMPUTE(buf)                                                                        \
+    do {                                                                                    \
+        _Pragma("unroll") for (int kk = 0; kk < BK; kk += 16) {                             \
+            bf16x8 a_[2], b_[2];                                                            \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i) a_[i] = *reinterpret_cast<const bf16x8 *>( \
+                &As[buf][wm * 64 + i * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);            \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) b_[j] = *reinterpret_cast<const bf16x8 *>( \
+                &Bs[buf][wn * 64 + j * 32 + (lane & 31)][kk + 8 * (lane >> 5)]);            \
+            _Pragma("unroll") for (int i = 0; i < 2; ++i)                                   \
+                _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] =                   \
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_[i], b_[j], acc[i][j], 0, 0, 0); \
+        }                                                                                   \
+    } while (0)
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    // One K step of loads in flight in registers while the other LDS buffer is
+    // computed on.  The loads are unconditional (past the last step they repeat
+    // it), so the compiler's count of outstanding loads stays exact.
+    const int nks = Kp / BK, last = nks - 1;
+    GLOAD(ra0, rb0, 0);
+    SSTORE(0, ra0, rb0);
+    GLOAD(ra0, rb0, 1 < last ? 1 : last);
+    __syncthreads();
+    for (int ks = 0; ks < nks; ++ks) {
+        const int buf = ks & 1;
+        COMPUTE(buf);
+        if (ks + 1 < nks) {
+            SSTORE(buf ^ 1, ra0, rb0);
+            GLOAD(ra0, rb0, ks + 2 < last ? ks + 2 : last);
+        }
+        __syncthreads();
+    }
+#undef GLOAD
+#undef SSTORE
+#undef COMPUTE
+    float *Cz = C + (size_t)blockIdx.z * pstride;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int col = n0 + wn * 64 + j * 32 + (lane & 31);
+            if (col >= N) continue;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (row < M) Cz[(size_t)row * ldc + col] = acc[i][j][e];
+            }
+        }
+}
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -283,7 +383,8 @@ void launch_skinny(const uint16_t *A, int lda, const GemmW &W, int N, int K, flo
 }  // namespace
 
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &Wb, int N, int K,
-                       float *C, int ldc, int M, hipStream_t s) {
+                       float *C, int ldc, int M, hipStream_t s, int kparts, size_t pstride) {
+    if (kparts < 1 || (kparts > 1 && !gemm_splits_ok(wtype, Ab != nullptr, M, K, kparts))) return hipErrorInvalidValue;
     if (K % 4 || lda % 4 || Wb.nseg < 1 || Wb.nseg > 4 || Wb.seg_end[Wb.nseg - 1] != N) return hipErrorInvalidValue;
     const GemmW W = Wb;
     if (wtype == kBF16 && Ab && lda % 8 == 0) {
@@ -291,6 +392,11 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
             if (M <= 16) launch_skinny<1>(Ab, lda, W, N, K, C, ldc, M, s);
             else if (M <= 32) launch_skinny<2>(Ab, lda, W, N, K, C, ldc, M, s);
             else launch_skinny<4>(Ab, lda, W, N, K, C, ldc, M, s);
+            return hipGetLastError();
+        }
+        if (M > 64 && K % 64 == 0) {
+            hipLaunchKernelGGL(k_gemm_mfma2, dim3((N + 127) / 128, (M + 127) / 128, kparts), dim3(256), 0, s, Ab, lda,
+                               W, N, K, C, ldc, M, kparts, pstride);
             return hipGetLastError();
         }
         if (M >= 32 && K % 8 == 0) {
@@ -309,6 +415,18 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
     if (wtype == kBF16) hipLaunchKernelGGL((k_gemm_tiled<kBF16>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);
     else hipLaunchKernelGGL((k_gemm_tiled<kF32>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);
     return hipGetLastError();
+}
+
+bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts) {
+    return wtype == kBF16 && have_bf16 && M > 64 && kparts <= kMaxKParts && K % (64 * kparts) == 0;
+}
+
+int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K) {
+    if (!gemm_splits_ok(wtype, have_bf16, M, K, 1)) return 1;
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    int S = 1;
+    while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K % (64 * S * 2) == 0 && K / (S * 2) >= 512) S *= 2;
+    return S;
 }
 
 }  // namespace dk

@@ -8,6 +8,7 @@ namespace dk {
 
 constexpr int kMaxLoops = 16;
 constexpr int kWarmup = 64;     // kv_cache.rs `KV_COL_WARMUP`: rows before the q8 field freezes
+constexpr int kMaxKParts = 8;  // split-K slabs of the multi-row output projections
 constexpr int kKGroup = 32;     // kv_cache.rs `KV_K_GROUP`: K channels per q8 scale
 constexpr float kEps = 1e-6f;   // dory.rs `EPS`: justnorm's epsilon
 
@@ -68,6 +69,8 @@ struct Resolve {
     const float *alpha;  // previous sub-layer's |alpha| [H] (slerp only)
     float *h_out;        // x for this sub-layer [T][H]
     uint16_t *hb_out;    // the same rows rounded to bf16 (the GEMMs' operand), or null
+    int32_t o_parts;     // multi-row calls: o is the sum of o_parts slabs o + s * o_stride
+    int64_t o_stride;
     float *inp;          // the loop's input [T][H]
     float *st;           // the loop state of every row [T][H] (batches), or null
     int32_t slerp;       // 1: e = slerp(h, o, alpha); 0: e = h
@@ -130,8 +133,13 @@ inline GemmW gemm_w(const void *w, int N) { return GemmW{{w, w, w, w}, {N, N, N,
 // C[T][ldc] (columns 0..N-1) = A[T][K] . W[N][K]^T, fp32 accumulation.  A is
 // given in fp32 and, for bf16 weights, also rounded to bf16 (Ab, same lda):
 // the bf16 MFMA kernels read Ab, the fp32 tiled kernel reads A.
+// kparts > 1 (split K, only where gemm_splits_ok): part z of the sum over K goes
+// to C + z * pstride, and the reader adds the kparts slabs.
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &W, int N, int K,
-                       float *C, int ldc, int T, hipStream_t s);
+                       float *C, int ldc, int T, hipStream_t s, int kparts = 1, size_t pstride = 0);
+bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts);
+// Split-K count that fills the chip with 128 x 128 tiles (1 where it does not apply).
+int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K);
 
 // Attention.
 struct PrepArgs {
