@@ -161,6 +161,15 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
         for (int j = 0; j < WR; ++j) wv[j][c].load(base[j], roff[j] + kc);
     }
+    // Pin the prologue's inputs here: otherwise the compiler sinks their loads
+    // into the branches of the prologue that use them, behind the weight loads,
+    // and the prologue then waits for every weight load.
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+        asm volatile("" ::"v"(ph[j]));
+        if (RES) asm volatile("" ::"v"(po[j]), "v"(pa[j]));
+        if (PRO == kProResolveInp) asm volatile("" ::"v"(pi[j]));
+    }
 
     // 3. x in LDS.
     if (RES) {
