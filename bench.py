@@ -446,6 +446,9 @@ def main():
     ap.add_argument("--context", type=int, default=None, help="decode context / prompt length")
     ap.add_argument("--stage-reps", type=int, default=400)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first copy this many MiB device to device 3 times (a known-size kernel for "
+                         "calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -454,6 +457,14 @@ def main():
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 18   # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.config in ("decode", "q8"):
         out = run_decode(args, args.config == "q8")
     elif args.config == "prefill":
