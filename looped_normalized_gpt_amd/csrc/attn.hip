@@ -154,14 +154,19 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
 }
 
 
-// The merge of multi-row calls: workgroup per (row r, kv head kh), thread per
-// (q head of the group, channel); each walks the row's splits in order with a
-// running (max, sum, acc).  Same arithmetic as k_attn_merge, laid out for many
-// rows with few splits each.
-template <int Q8>
+// The merge of multi-row calls: workgroup per (row r, kv head kh), k_attn_merge's
+// arithmetic.  Wave w takes splits w, w+4, ... (4 at a time in flight), lane l
+// the CPL channels l*CPL .. of the group's REP*HD (one head); the 4 waves'
+// running (max, sum, acc) are then combined through LDS.
+template <int Q8, int HD, int REP>
 __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
+    constexpr int CH = REP * HD, CPL = CH >= 64 ? CH / 64 : 1;
+    static_assert(CH % 64 == 0 || CH < 64, "channels split evenly over the lanes");
+    static_assert(HD % CPL == 0, "a lane's channels lie in one head");
+    __shared__ float wm[4][64], wl[4][64], wacc[4][CH];
     const int r = blockIdx.x, kh = blockIdx.y;
-    const int hd = a.hd, rep = a.nh / a.nk, Q = a.nh * hd, ld = 2 * Q + 2 * a.nk * hd;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int Q = a.nh * HD, ld = 2 * Q + 2 * a.nk * HD;
     const int64_t p = a.rec->rows[r].pos;
     int nsplit;
     if (a.blk > 0) {
@@ -173,48 +178,58 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
         const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
         nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
     }
-    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
-    const size_t pstride = (size_t)rep * (hd + 2);
-    const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride;
-    for (int c = threadIdx.x; c < rep * hd; c += 256) {
-        const int h = c / hd, d = c % hd, hq = kh * rep + h;
-        const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + d];
-        const float sgv = a.sg[hq * hd + d];
-        const float vcol = field ? slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + d] : 1.f;
-        const float *ph = all + (size_t)h * (hd + 2);
-        float M = -INFINITY, L = 0.f, acc = 0.f;
-        int j = 0;
-        for (; j + 4 <= nsplit; j += 4) {
-            float m[4], l[4], v[4];
+    const size_t pstride = (size_t)REP * (HD + 2);
+    const int c0 = lane * CPL < CH ? lane * CPL : 0, h = c0 / HD, d0 = c0 % HD;  // lanes past CH: a copy, unused
+    const float *ph = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride + (size_t)h * (HD + 2);
+    float M = -INFINITY, L = 0.f, acc[CPL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float *pj = ph + (size_t)(j + u) * pstride;
-                m[u] = pj[0];
-                l[u] = pj[1];
-                v[u] = pj[2 + d];
-            }
+    for (int i = 0; i < CPL; ++i) acc[i] = 0.f;
+    for (int j0 = wave; j0 < nsplit; j0 += 16) {
+        float m[4], l[4], v[4][CPL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (m[u] == -INFINITY) continue;  // a split with no key this row sees
-                const float Mn = fmaxf(M, m[u]);
-                const float c0 = expf(M - Mn), c1 = expf(m[u] - Mn);
-                L = L * c0 + l[u] * c1;
-                acc = acc * c0 + v[u] * c1;
-                M = Mn;
-            }
-        }
-        for (; j < nsplit; ++j) {
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 4 * u < nsplit ? j0 + 4 * u : j0;
             const float *pj = ph + (size_t)j * pstride;
-            const float mj = pj[0];
-            if (mj == -INFINITY) continue;
-            const float Mn = fmaxf(M, mj);
-            const float c0 = expf(M - Mn), c1 = expf(mj - Mn);
-            L = L * c0 + pj[1] * c1;
-            acc = acc * c0 + pj[2 + d] * c1;
+            m[u] = pj[0];
+            l[u] = pj[1];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) v[u][i] = pj[2 + d0 + i];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (j0 + 4 * u >= nsplit || m[u] == -INFINITY) continue;  // past the end, or no key seen
+            const float Mn = fmaxf(M, m[u]);
+            const float e0 = expf(M - Mn), e1 = expf(m[u] - Mn);
+            L = L * e0 + l[u] * e1;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc[i] = acc[i] * e0 + v[u][i] * e1;
             M = Mn;
         }
-        const float y = acc / L * vcol;
-        a.z[(size_t)r * Q + hq * hd + d] = y / (1.0f + expf(-(gate * sgv)));
+    }
+    wm[wave][lane] = M;
+    wl[wave][lane] = L;
+    if (lane * CPL < CH)
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) wacc[wave][c0 + i] = acc[i];
+    __syncthreads();
+    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    for (int c = tid; c < CH; c += 256) {
+        const int ln = c / CPL, hh = c / HD, d = c % HD, hq = kh * REP + hh;
+        float Mt = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, wm[w][ln]);
+        float Lt = 0.f, y = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (wm[w][ln] == -INFINITY) continue;  // a wave with no split
+            const float e = expf(wm[w][ln] - Mt);
+            Lt += wl[w][ln] * e;
+            y += wacc[w][c] * e;
+        }
+        const float vcol = field ? slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * HD + d] : 1.f;
+        const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * HD + hq * HD + d];
+        y = y / Lt * vcol;
+        a.z[(size_t)r * Q + hq * HD + d] = y / (1.0f + expf(-(gate * a.sg[hq * HD + d])));
     }
 }
 
@@ -866,8 +881,8 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
         else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(1024), 0, s, a);
     } else {
         dim3 mgrid(rows, a.nk);
-        if (a.q8) hipLaunchKernelGGL((k_attn_merge_rows<1>), mgrid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_attn_merge_rows<0>), mgrid, dim3(256), 0, s, a);
+        if (a.q8) hipLaunchKernelGGL((k_attn_merge_rows<1, HD, REP>), mgrid, dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((k_attn_merge_rows<0, HD, REP>), mgrid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }

@@ -208,12 +208,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
     const int wm = wave >> 1, wn = wave & 1;
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int Kp = K / S, kz = blockIdx.z * Kp;
-    // loaders: row tid/2 of the A and B tiles, 32 bf16 at (tid%2)*32
-    const int lr = tid >> 1, lc = (tid & 1) * 32;
-    const int am = m0 + lr < M ? m0 + lr : M - 1;
-    const int bn = n0 + lr < N ? n0 + lr : N - 1;
-    const uint16_t *arow = A + (size_t)am * lda + kz + lc;
-    const uint16_t *brow = seg_row<uint16_t>(W, bn, K) + kz + lc;
+    // loaders: load i of thread t reads row 32 i + t/8, 8 bf16 at 8 (t%8) of the
+    // tile (8 consecutive threads read one 128-byte row run)
+    const int lr = tid >> 3, lc = (tid & 7) * 8;
+    const uint16_t *arow[4], *brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int am = m0 + 32 * i + lr < M ? m0 + 32 * i + lr : M - 1;
+        const int bn = n0 + 32 * i + lr < N ? n0 + 32 * i + lr : N - 1;
+        arow[i] = A + (size_t)am * lda + kz + lc;
+        brow[i] = seg_row<uint16_t>(W, bn, K) + kz + lc;
+    }
     u32x4_t ra0[4], rb0[4];
     // (macros rather than lambdas over array references: the latter left the
     // staging registers in scratch memory)
@@ -221,16 +226,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
     do {                                                                                    \
         const int k_ = (ks) * BK;                                                           \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) ra[i] =                               \
-            *reinterpret_cast<const u32x4_t *>(arow + k_ + 8 * i);                            \
+            *reinterpret_cast<const u32x4_t *>(arow[i] + k_);                               \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) rb[i] =                               \
-            *reinterpret_cast<const u32x4_t *>(brow + k_ + 8 * i);                            \
+            *reinterpret_cast<const u32x4_t *>(brow[i] + k_);                               \
     } while (0)
 #define SSTORE(buf, ra, rb)                                                                 \
     do {                                                                                    \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
-            *reinterpret_cast<u32x4_t *>(&As[buf][lr][lc + 8 * i]) = ra[i];                   \
+            *reinterpret_cast<u32x4_t *>(&As[buf][32 * i + lr][lc]) = ra[i];                \
         _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
-            *reinterpret_cast<u32x4_t *>(&Bs[buf][lr][lc + 8 * i]) = rb[i];                   \
+            *reinterpret_cast<u32x4_t *>(&Bs[buf][32 * i + lr][lc]) = rb[i];                \
     } while (0)
 #define COMPUTE(buf)                                                                        \
     do {                                                                                    \
@@ -297,9 +302,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // Every weight byte is read once, straight into registers.
 // Operand layout of the 16x16x32 MFMA: lane l supplies row l % 16 and k-slots
 // 8 (l/16) .. +7 of A (and of B), and receives C[4 (l/16) + i][l % 16] in
-// accumulator i.  The sum over k does not care which k sits in which slot as
-// long as A and B agree, so lane group g takes the 32 contiguous k at 32g of a
-// block (one 64-byte run of a row) and feeds them to 4 MFMAs, 8 at a time.
+// accumulator i.  MFMA t of a 128-wide K block takes k = 32t .. 32t+31, so the
+// 4 lanes of a row read one contiguous 64-byte run per load instruction.
 template <int MT, int NT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict__ A, int lda, const GemmW W, int N,
                                                      int K, float *__restrict__ C, int ldc, int M) {
@@ -311,13 +315,13 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict_
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int n = n0 + 16 * nt + r < N ? n0 + 16 * nt + r : N - 1;
-        wrow[nt] = seg_row<uint16_t>(W, n, K) + 32 * g;
+        wrow[nt] = seg_row<uint16_t>(W, n, K) + 8 * g;
     }
     const uint16_t *arow[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int m = 16 * mt + r < M ? 16 * mt + r : M - 1;
-        arow[mt] = A + (size_t)m * lda + 32 * g;
+        arow[mt] = A + (size_t)m * lda + 8 * g;
     }
     f32x4_t acc[NT][MT];
 #pragma unroll
@@ -330,11 +334,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict_
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) wv[nt][t] = *reinterpret_cast<const uint4 *>(wrow[nt] + k + 8 * t);
+            for (int t = 0; t < 4; ++t) wv[nt][t] = *reinterpret_cast<const uint4 *>(wrow[nt] + k + 32 * t);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) av[mt][t] = *reinterpret_cast<const uint4 *>(arow[mt] + k + 8 * t);
+            for (int t = 0; t < 4; ++t) av[mt][t] = *reinterpret_cast<const uint4 *>(arow[mt] + k + 32 * t);
     };
     auto mma = [&](const uint4 (&wv)[NT][4], const uint4 (&av)[MT][4]) {
 #pragma unroll
