@@ -668,17 +668,18 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
     const bool rok = r < T;
     const int64_t p = pos0 + (rok ? r : r1);
     const int64_t lo_r = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+    const int lo_i = (int)lo_r, p_i = (int)p, ee_i = (int)ee;
     bf16x8_t qb[KS];
     {
         const float *qrow = a.qp + (size_t)(rok ? r : r1) * Q + (size_t)(kh * REP + h) * HD;
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
             const int d = 16 * t + 8 * g;
-            float4 x0 = *reinterpret_cast<const float4 *>(qrow + d);
-            float4 x1 = *reinterpret_cast<const float4 *>(qrow + d + 4);
+            float4 x0 = gld4(qrow + d);
+            float4 x1 = gld4(qrow + d + 4);
             if (Q8 && a.field) {
-                const float4 c0 = *reinterpret_cast<const float4 *>(sd.kcol + kh * HD + d);
-                const float4 c1 = *reinterpret_cast<const float4 *>(sd.kcol + kh * HD + d + 4);
+                const float4 c0 = gld4(sd.kcol + kh * HD + d);
+                const float4 c1 = gld4(sd.kcol + kh * HD + d + 4);
                 x0.x *= c0.x; x0.y *= c0.y; x0.z *= c0.z; x0.w *= c0.w;
                 x1.x *= c1.x; x1.y *= c1.y; x1.z *= c1.z; x1.w *= c1.w;
             }
@@ -696,21 +697,26 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
     const int lc = tid % (HD / 4), lk = tid / (HD / 4);
     float4 kr[KPASS], vr[VPASS][8];
     float ksr[KPASS], vsr[VPASS][8];
-    auto key_row = [&](int64_t e) -> size_t {
-        e = e < ee ? e : ee;
-        return (size_t)kh * cap + (size_t)(e % cap);
-    };
+    // Ring rows of a tile: one wave-uniform remainder per tile, then a wrap
+    // check per key (positions fit in 32 bits: they are below max_ctx); keys
+    // past the split's last re-read its row and are masked.
     auto gload = [&](int tile) {
-        const int64_t t0 = eb + (int64_t)tile * KT;
+        const int t0 = (int)eb + tile * KT;
+        const int rb = (int)((unsigned)t0 % (unsigned)cap);
+        const int last = (int)ee - t0;
+        auto key_row = [&](int k) -> size_t {
+            int rr = rb + (k < last ? k : last);
+            rr = rr >= cap ? rr - cap : rr;
+            return (size_t)kh * cap + rr;
+        };
 #pragma unroll
         for (int i = 0; i < KPASS; ++i) {
-            const size_t row = key_row(t0 + lk + KL * i);
+            const size_t row = key_row(lk + KL * i);
             if (Q8) {
-                const char4 c = *reinterpret_cast<const char4 *>(sd.kc + row * HD + 4 * lc);
-                kr[i] = make_float4((float)c.x, (float)c.y, (float)c.z, (float)c.w);
-                ksr[i] = sd.ks[row * NGK + (4 * lc) / kKGroup];
+                kr[i] = gld_codes4(sd.kc + row * HD + 4 * lc);
+                ksr[i] = gld<float>(sd.ks + row * NGK + (4 * lc) / kKGroup);
             } else {
-                kr[i] = *reinterpret_cast<const float4 *>(sd.k + row * HD + 4 * lc);
+                kr[i] = gld4(sd.k + row * HD + 4 * lc);
             }
         }
 #pragma unroll
@@ -719,13 +725,12 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int kk = 16 * (ci >> 1) + 8 * (j >> 2) + 4 * (ci & 1) + (j & 3);
-                const size_t row = key_row(t0 + kk);
+                const size_t row = key_row(kk);
                 if (Q8) {
-                    const char4 c = *reinterpret_cast<const char4 *>(sd.vc + row * HD + 4 * lc);
-                    vr[i][j] = make_float4((float)c.x, (float)c.y, (float)c.z, (float)c.w);
-                    vsr[i][j] = sd.vs[row];
+                    vr[i][j] = gld_codes4(sd.vc + row * HD + 4 * lc);
+                    vsr[i][j] = gld<float>(sd.vs + row);
                 } else {
-                    vr[i][j] = *reinterpret_cast<const float4 *>(sd.v + row * HD + 4 * lc);
+                    vr[i][j] = gld4(sd.v + row * HD + 4 * lc);
                 }
             }
         }
@@ -758,8 +763,13 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
     for (int t = 0; t < DT; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[t][e] = 0.f;
-    float m = -INFINITY, l = 0.f;
-    const float scale = 1.0f / sqrtf((float)HD);
+    float m = -INFINITY, l = 0.f;  // running maximum (log2 units) and sum
+    const float scale2 = 1.4426950408889634f / sqrtf((float)HD);
+    // keys every row of this wave sees (rows rlo .. rhi, consecutive positions):
+    // [wlo, whi]; empty when the wave has a row past T
+    const int rlo = r0 + (BQ >= 32 ? (wave * 32) % BQ : 0), rhi = rlo + (BQ >= 32 ? 32 : BQ) - 1;
+    const int wlo = rhi < T ? (int)(pos0 + rhi + 1 - a.window > 0 ? pos0 + rhi + 1 - a.window : 0) : 1 << 30;
+    const int whi = (int)(pos0 + rlo) < ee_i ? (int)(pos0 + rlo) : ee_i;
 
     gload(0);
     sstore(0);
@@ -768,7 +778,7 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
     for (int tile = 0; tile < ntiles; ++tile) {
         const bool more = tile + 1 < ntiles;
         if (more) gload(tile + 1);
-        const int64_t t0 = eb + (int64_t)tile * KT;
+        const int t0 = (int)eb + tile * KT;
         // scores of the two 32-key blocks
         f32x16_t sc[2];
 #pragma unroll
@@ -781,21 +791,32 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qb[t], sc[kb], 0, 0, 0);
             }
         }
-        // mask and tile maximum
+        // mask (only on tiles some row of this wave does not see whole) and
+        // tile maximum; scores in log2 units (scale * log2 e folded in)
         float mx = -INFINITY;
+        if (t0 >= wlo && t0 + KT - 1 <= whi) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t key = t0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
-                const bool vis = rok && key >= lo_r && key <= p && key <= ee;
-                const float v = vis ? sc[kb][e] * scale : -INFINITY;
-                sc[kb][e] = v;
-                mx = fmaxf(mx, v);
-            }
+                for (int e = 0; e < 16; ++e) {
+                    sc[kb][e] *= scale2;
+                    mx = fmaxf(mx, sc[kb][e]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int key = t0 + 32 * kb + 8 * (e >> 2) + 4 * g + (e & 3);
+                    const bool vis = rok && key >= lo_i && key <= p_i && key <= ee_i;
+                    const float v = vis ? sc[kb][e] * scale2 : -INFINITY;
+                    sc[kb][e] = v;
+                    mx = fmaxf(mx, v);
+                }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float mn = fmaxf(m, mx);
-        const float alpha = mn == -INFINITY ? 1.f : expf(m - mn);
+        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - mn);
         m = mn;
         bf16x8_t pb[2][2];
         float ls = 0.f;
@@ -803,15 +824,16 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const float pv = mn == -INFINITY ? 0.f : expf(sc[kb][e] - mn);
+                const float pv = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[kb][e] - mn);
                 ls += pv;
                 pb[kb][e >> 3][e & 7] = (__bf16)pv;
             }
         l = l * alpha + ls;
+        if (__ballot(alpha != 1.f) != 0)  // some lane's maximum moved
 #pragma unroll
-        for (int t = 0; t < DT; ++t)
+            for (int t = 0; t < DT; ++t)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
+                for (int e = 0; e < 16; ++e) o[t][e] *= alpha;
         // O^T += V^T P^T over the 64 keys (4 MFMA k-steps of 16 slots)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -834,7 +856,7 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
     const size_t pstride = (size_t)REP * (HD + 2);
     float *mine = a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride + (size_t)h * (HD + 2);
     if (g == 0) {
-        mine[0] = m;
+        mine[0] = m * 0.6931471805599453f;  // log2 units -> natural units for the merge
         mine[1] = l;
     }
 #pragma unroll

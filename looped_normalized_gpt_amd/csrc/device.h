@@ -10,6 +10,25 @@ namespace dk {
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// A load through a global-address-space pointer.  Pointers fetched from memory
+// (the slot table) are generic to the compiler, which then emits flat loads;
+// those also count against the LDS wait counter, so an LDS wait would wait for
+// them too.
+typedef float gf32x4_t __attribute__((ext_vector_type(4)));
+template <typename T>
+__device__ __forceinline__ T gld(const void *p) {  // scalars
+    return *(const __attribute__((address_space(1))) T *)(p);
+}
+__device__ __forceinline__ float4 gld4(const float *p) {
+    const gf32x4_t v = *(const __attribute__((address_space(1))) gf32x4_t *)(p);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 gld_codes4(const int8_t *p) {  // 4 int8 codes as floats
+    const int u = *(const __attribute__((address_space(1))) int *)(p);
+    return make_float4((float)(int8_t)(u & 0xff), (float)(int8_t)((u >> 8) & 0xff), (float)(int8_t)((u >> 16) & 0xff),
+                       (float)(int8_t)((u >> 24) & 0xff));
+}
+
 // fp32 -> bf16 bits, round to nearest even
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
