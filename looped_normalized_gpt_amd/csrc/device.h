@@ -254,14 +254,20 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
 #pragma unroll
         for (int j = 0; j < EPT; ++j) s += e[j] * e[j];
         const float fs = norm_factor(block_sum(s, red));
-        if (rs.loop_op == kLoopExit) {
 #pragma unroll
-            for (int j = 0; j < EPT; ++j) e[j] *= fs;
-        } else {
+        for (int j = 0; j < EPT; ++j) e[j] *= fs;
+        if (rs.loop_op == kLoopNext) {
+            if (writer && rs.st)  // batches: every row's loop state
+#pragma unroll
+                for (int j = 0; j < EPT; j += 4)
+                    if (reg_index(j) < H)
+                        *reinterpret_cast<float4 *>(rs.st + (size_t)r * H + reg_index(j)) =
+                            make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
+            if (r >= rs.n_next) return;  // this row's loops are over (uniform over the workgroup)
             float s2 = 0.f;
 #pragma unroll
             for (int j = 0; j < EPT; ++j) {
-                e[j] = e[j] * fs + in[j];
+                e[j] = e[j] + in[j];
                 s2 += e[j] * e[j];
             }
             const float f = norm_factor(block_sum(s2, red));
@@ -274,8 +280,12 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
         const int i = reg_index(j);
         if (i < H) {
             const float4 v = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
-            *reinterpret_cast<float4 *>(xs + i) = v;
+            if (xs) *reinterpret_cast<float4 *>(xs + i) = v;
             if (writer && rs.h_out) *reinterpret_cast<float4 *>(rs.h_out + (size_t)r * H + i) = v;
+            if (writer && rs.hb_out) {
+                uint16_t *hb = rs.hb_out + (size_t)r * H + i;
+                hb[0] = f2bf(v.x); hb[1] = f2bf(v.y); hb[2] = f2bf(v.z); hb[3] = f2bf(v.w);
+            }
         }
     }
 }

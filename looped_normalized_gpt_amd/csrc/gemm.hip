@@ -292,6 +292,112 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
         }
 }
 
+
+// The same tiles fed by LDS DMA (global_load_lds_dwordx4: lane i of a wave's
+// load writes 16 bytes at the wave's LDS address + 16 i, no staging
+// registers), STAGES deep: the loads of STAGES-1 K steps stay in flight while
+// one step is computed, which covers the memory latency that a one-step
+// register prefetch left exposed.  A tile row (64 bf16 = 8 chunks of 16 bytes)
+// is stored with chunk c at position c ^ (row % 8), so the 32 rows a wave
+// reads for one MFMA operand fall in different banks.  One workgroup per CU
+// (STAGES x 32 KB of LDS).
+// LDS byte address of a shared-memory pointer
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+template <int STAGES>
+__global__ __launch_bounds__(512) void k_gemm_dma(const uint16_t *__restrict__ A, int lda, const GemmW W, int N, int K,
+                                                  float *__restrict__ C, int ldc, int M, int S, size_t pstride) {
+    constexpr int BM = 128, BN = 128, BK = 64, TE = BM * BK;  // elements of one operand tile
+    __shared__ __attribute__((aligned(16))) uint16_t lds[STAGES][2][TE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;  // 8 waves: 2 per SIMD
+    const int wm = wave >> 2, wn = wave & 3;                        // wave block: rows 64 wm, cols 32 wn
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+    const int Kp = K / S, kz = blockIdx.z * Kp;
+    // DMA: load j (0..1) of wave w covers tile rows 16 w + 8 j .. +7; lane l
+    // reads row 16 w + 8 j + l/8, global chunk (l % 8) ^ (l / 8), and lands at
+    // chunk l % 8 of that row
+    const int crow = lane >> 3, csrc = (lane & 7) ^ crow;
+    const uint16_t *asrc[2], *bsrc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int row = 16 * wave + 8 * j + crow;
+        const int gm = m0 + row < M ? m0 + row : M - 1;
+        const int gn = n0 + row < N ? n0 + row : N - 1;
+        asrc[j] = A + (size_t)gm * lda + kz + 8 * csrc;
+        bsrc[j] = seg_row<uint16_t>(W, gn, K) + kz + 8 * csrc;
+    }
+    auto issue = [&](int st, int ks) {
+        const int k = ks * BK;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(asrc[j] + k),
+                                             (__attribute__((address_space(3))) void *)(&lds[st][0][(16 * wave + 8 * j) * BK]),
+                                             16, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(bsrc[j] + k),
+                                             (__attribute__((address_space(3))) void *)(&lds[st][1][(16 * wave + 8 * j) * BK]),
+                                             16, 0, 0);
+    };
+    f32x16 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    const int nks = Kp / BK, last = nks - 1;
+#pragma unroll
+    for (int st = 0; st < STAGES - 1; ++st) issue(st, st < last ? st : last);
+    for (int ks = 0; ks < nks; ++ks) {
+        // refill the buffer step ks-1 used (every wave passed the barrier after
+        // computing it); unconditional, so every wave always has the same loads
+        // outstanding: steps ks .. ks+STAGES-1, 4 per step, oldest first
+        const int nx = ks + STAGES - 1;
+        issue(nx % STAGES, nx < last ? nx : last);
+        // this wave's loads of step ks have landed; the barrier makes every
+        // wave's (plain s_barrier: a fence here would wait for all loads)
+        if constexpr (STAGES == 4) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        else if constexpr (STAGES == 3) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        const uint32_t As = lds_addr(lds[ks % STAGES][0]), Bs = lds_addr(lds[ks % STAGES][1]);
+        const int ra0 = wm * 64 + (lane & 31), ra1 = ra0 + 32, rb = wn * 32 + (lane & 31);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            const int ch = (kk >> 3) + (lane >> 5);   // the global 16-byte chunk this lane supplies
+            bf16x8 a0, a1, b;
+            // LDS reads in asm: the compiler cannot tell them from the DMA's
+            // destinations and would otherwise wait for every load in flight
+            asm volatile(
+                "ds_read_b128 %0, %3\n\t"
+                "ds_read_b128 %1, %4\n\t"
+                "ds_read_b128 %2, %5\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=v"(a0), "=v"(a1), "=v"(b)
+                : "v"(As + 2 * (ra0 * BK + 8 * (ch ^ (ra0 & 7)))), "v"(As + 2 * (ra1 * BK + 8 * (ch ^ (ra1 & 7)))),
+                  "v"(Bs + 2 * (rb * BK + 8 * (ch ^ (rb & 7)))));
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+        }
+        // every wave's reads of this buffer are done (lgkmcnt 0 above) before
+        // the next iteration's loads refill it
+        __builtin_amdgcn_s_barrier();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated tail loads, before the workgroup ends
+    float *Cz = C + (size_t)blockIdx.z * pstride;
+    const int col = n0 + wn * 32 + (lane & 31);
+    if (col < N) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (row < M) Cz[(size_t)row * ldc + col] = acc[i][e];
+            }
+    }
+}
+
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Few-row projections (batched decode, short chunks): M <= 16*MT rows of bf16
@@ -399,8 +505,13 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
             return hipGetLastError();
         }
         if (M > 64 && K % 64 == 0) {
-            hipLaunchKernelGGL(k_gemm_mfma2, dim3((N + 127) / 128, (M + 127) / 128, kparts), dim3(256), 0, s, Ab, lda,
-                               W, N, K, C, ldc, M, kparts, pstride);
+            // one workgroup per CU when the tiles fit the chip in one round (LDS
+            // DMA, 4 stages); two per CU otherwise (register prefetch, 2 stages)
+            const dim3 grid((N + 127) / 128, (M + 127) / 128, kparts);
+            if ((long)grid.x * grid.y * grid.z <= 256)
+                hipLaunchKernelGGL(k_gemm_dma<4>, grid, dim3(512), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
+            else
+                hipLaunchKernelGGL(k_gemm_mfma2, grid, dim3(256), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
             return hipGetLastError();
         }
         if (M >= 32 && K % 8 == 0) {

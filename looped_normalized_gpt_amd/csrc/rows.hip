@@ -25,9 +25,54 @@ __global__ __launch_bounds__(256) void k_embed(const void *E, int V, int H, cons
     }
 }
 
+// One row per workgroup; thread t holds the float4 groups at 4t + 1024 jj of
+// the row in registers (EPT / 4 groups), every input load issued before any
+// arithmetic.
+template <int EPT>
 __global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const CallRec *rec) {
-    extern __shared__ float smem[];
-    resolve_row(rs, blockIdx.x, H, smem + 8, smem, true, rec);
+    __shared__ float red[8];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const bool from_st = rs.loop_op == kLoopExit && r >= rs.n_prev;  // a batch row whose loops ended early
+    const bool slerp = rs.slerp && !from_st;
+    const float *hs = (from_st ? rs.st : rs.h) + (size_t)r * H;
+    float h[EPT], o[EPT], al[EPT], in[EPT];
+#pragma unroll
+    for (int jj = 0; jj < EPT / 4; ++jj) {
+        const int i = 4 * tid + 1024 * jj, ic = i < H ? i : 0;
+        const float4 vh = *reinterpret_cast<const float4 *>(hs + ic);
+        float4 vo = make_float4(0.f, 0.f, 0.f, 0.f), va = vo, vi = vo;
+        if (slerp) {
+            // o: the sum of the output projection's split-K slabs
+            for (int p = 0; p < (rs.o_parts > 1 ? rs.o_parts : 1); ++p) {
+                const float4 t = *reinterpret_cast<const float4 *>(rs.o + (size_t)p * rs.o_stride + (size_t)r * H + ic);
+                vo.x += t.x; vo.y += t.y; vo.z += t.z; vo.w += t.w;
+            }
+            va = *reinterpret_cast<const float4 *>(rs.alpha + ic);
+        }
+        if (rs.loop_op == kLoopNext) vi = *reinterpret_cast<const float4 *>(rs.inp + (size_t)r * H + ic);
+        const bool ok = i < H;
+        h[4 * jj] = ok ? vh.x : 0.f; h[4 * jj + 1] = ok ? vh.y : 0.f; h[4 * jj + 2] = ok ? vh.z : 0.f; h[4 * jj + 3] = ok ? vh.w : 0.f;
+        o[4 * jj] = ok ? vo.x : 0.f; o[4 * jj + 1] = ok ? vo.y : 0.f; o[4 * jj + 2] = ok ? vo.z : 0.f; o[4 * jj + 3] = ok ? vo.w : 0.f;
+        al[4 * jj] = va.x; al[4 * jj + 1] = va.y; al[4 * jj + 2] = va.z; al[4 * jj + 3] = va.w;
+        in[4 * jj] = ok ? vi.x : 0.f; in[4 * jj + 1] = ok ? vi.y : 0.f; in[4 * jj + 2] = ok ? vi.z : 0.f; in[4 * jj + 3] = ok ? vi.w : 0.f;
+    }
+    if (from_st) {
+#pragma unroll
+        for (int jj = 0; jj < EPT / 4; ++jj) {
+            const int i = 4 * tid + 1024 * jj;
+            if (i >= H) continue;
+            const float4 v = make_float4(h[4 * jj], h[4 * jj + 1], h[4 * jj + 2], h[4 * jj + 3]);
+            if (rs.h_out) *reinterpret_cast<float4 *>(rs.h_out + (size_t)r * H + i) = v;
+            if (rs.hb_out) {
+                uint16_t *hb = rs.hb_out + (size_t)r * H + i;
+                hb[0] = f2bf(v.x); hb[1] = f2bf(v.y); hb[2] = f2bf(v.z); hb[3] = f2bf(v.w);
+            }
+        }
+        return;
+    }
+    Resolve rr = rs;
+    rr.slerp = slerp;
+    resolve_regs<EPT>(rr, r, H, h, o, al, in, nullptr, red, true, rec);
 }
 
 // dst[r] = justnorm(src[r]) over N values.
@@ -66,6 +111,71 @@ __global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float
     }
 }
 
+// Register versions of the two renorms for rows of 4-aligned length: thread t
+// holds the float4 groups t + 256 j (j < G) of its row, all loads issued first.
+template <int G>
+__global__ __launch_bounds__(256) void k_rownorm_v(const float *src, int ld, float *dst, uint16_t *dstb, int N) {
+    __shared__ float red[8];
+    const float *x = src + (size_t)blockIdx.x * ld;
+    float4 v[G];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int i = 4 * (threadIdx.x + 256 * j);
+        v[j] = *reinterpret_cast<const float4 *>(x + (i < N ? i : 0));
+        if (i >= N) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        s += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+    }
+    const float f = norm_factor(block_sum(s, red));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int i = 4 * (threadIdx.x + 256 * j);
+        if (i >= N) continue;
+        const float4 y = make_float4(v[j].x * f, v[j].y * f, v[j].z * f, v[j].w * f);
+        *reinterpret_cast<float4 *>(dst + (size_t)blockIdx.x * N + i) = y;
+        if (dstb) {
+            uint16_t *b = dstb + (size_t)blockIdx.x * N + i;
+            b[0] = f2bf(y.x); b[1] = f2bf(y.y); b[2] = f2bf(y.z); b[3] = f2bf(y.w);
+        }
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(256) void k_swiglu_norm_v(const float *a, const float *b, int ld, const float *sg,
+                                                       const float *su, float *dst, uint16_t *dstb, int F) {
+    __shared__ float red[8];
+    const size_t offi = (size_t)blockIdx.x * ld, off = (size_t)blockIdx.x * F;
+    float4 z[G];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int i = 4 * (threadIdx.x + 256 * j), ic = i < F ? i : 0;
+        const float4 va = *reinterpret_cast<const float4 *>(a + offi + ic);
+        const float4 vb = *reinterpret_cast<const float4 *>(b + offi + ic);
+        const float4 vg = *reinterpret_cast<const float4 *>(sg + ic);
+        const float4 vu = *reinterpret_cast<const float4 *>(su + ic);
+        const float ga[4] = {va.x * vg.x, va.y * vg.y, va.z * vg.z, va.w * vg.w};
+        const float ub[4] = {vb.x * vu.x, vb.y * vu.y, vb.z * vu.z, vb.w * vu.w};
+        float zz[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) zz[c] = i < F ? ga[c] / (1.0f + expf(-ga[c])) * ub[c] : 0.f;
+        z[j] = make_float4(zz[0], zz[1], zz[2], zz[3]);
+        s += zz[0] * zz[0] + zz[1] * zz[1] + zz[2] * zz[2] + zz[3] * zz[3];
+    }
+    const float f = norm_factor(block_sum(s, red));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int i = 4 * (threadIdx.x + 256 * j);
+        if (i >= F) continue;
+        const float4 y = make_float4(z[j].x * f, z[j].y * f, z[j].z * f, z[j].w * f);
+        *reinterpret_cast<float4 *>(dst + off + i) = y;
+        if (dstb) {
+            uint16_t *q = dstb + off + i;
+            q[0] = f2bf(y.x); q[1] = f2bf(y.y); q[2] = f2bf(y.z); q[3] = f2bf(y.w);
+        }
+    }
+}
+
 // dory.rs `head` for every row of a batch: the logit scale, and each row's
 // logits to its place in the caller's array.
 __global__ __launch_bounds__(256) void k_logits_rows(const float *hlog, const float *ls, int V, const CallRec *rec) {
@@ -90,17 +200,40 @@ hipError_t launch_embed(int wtype, const void *E, int V, int H, const CallRec *r
 }
 
 hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s) {
-    hipLaunchKernelGGL(k_resolve_rows, dim3(T), dim3(256), sizeof(float) * (H + 8), s, rs, H, rec);
+    if (H <= 2048) hipLaunchKernelGGL((k_resolve_rows<8>), dim3(T), dim3(256), 0, s, rs, H, rec);
+    else if (H <= 4096) hipLaunchKernelGGL((k_resolve_rows<16>), dim3(T), dim3(256), 0, s, rs, H, rec);
+    else if (H <= 8192) hipLaunchKernelGGL((k_resolve_rows<32>), dim3(T), dim3(256), 0, s, rs, H, rec);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
+#define DK_G_SWITCH(G, KERNEL, ...)                                                          \
+    switch (G) {                                                                              \
+        case 1: hipLaunchKernelGGL((KERNEL<1>), __VA_ARGS__); break;                          \
+        case 2: hipLaunchKernelGGL((KERNEL<2>), __VA_ARGS__); break;                          \
+        case 3: hipLaunchKernelGGL((KERNEL<3>), __VA_ARGS__); break;                          \
+        case 4: hipLaunchKernelGGL((KERNEL<4>), __VA_ARGS__); break;                          \
+        case 5: case 6: hipLaunchKernelGGL((KERNEL<6>), __VA_ARGS__); break;                  \
+        default: hipLaunchKernelGGL((KERNEL<8>), __VA_ARGS__); break;                         \
+    }
+
 hipError_t launch_rownorm(const float *src, int ld, float *dst, uint16_t *dstb, int N, int T, hipStream_t s) {
+    const int G = (N / 4 + 255) / 256;
+    if (N % 4 == 0 && ld % 4 == 0 && G <= 8) {
+        DK_G_SWITCH(G, k_rownorm_v, dim3(T), dim3(256), 0, s, src, ld, dst, dstb, N)
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_rownorm, dim3(T), dim3(256), 0, s, src, ld, dst, dstb, N);
     return hipGetLastError();
 }
 
 hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su, float *dst,
                               uint16_t *dstb, int F, int T, hipStream_t s) {
+    const int G = (F / 4 + 255) / 256;
+    if (F % 4 == 0 && ld % 4 == 0 && G <= 8) {
+        DK_G_SWITCH(G, k_swiglu_norm_v, dim3(T), dim3(256), 0, s, a, b, ld, sg, su, dst, dstb, F)
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(k_swiglu_norm, dim3(T), dim3(256), sizeof(float) * (F + 8), s, a, b, ld, sg, su, dst, dstb, F);
     return hipGetLastError();
 }
