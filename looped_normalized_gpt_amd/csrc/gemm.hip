@@ -402,92 +402,105 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Few-row projections (batched decode, short chunks): M <= 16*MT rows of bf16
 // activations against bf16 weights, on v_mfma_f32_16x16x32_bf16.  Workgroup =
-// 16*NT weight rows (output columns); its 4 waves take the K blocks of 128 in
-// turn, two blocks in flight per wave (the next block's loads are issued before
-// the current block's MFMAs), and add their partial tiles in LDS at the end.
-// Every weight byte is read once, straight into registers.
-// Operand layout of the 16x16x32 MFMA: lane l supplies row l % 16 and k-slots
-// 8 (l/16) .. +7 of A (and of B), and receives C[4 (l/16) + i][l % 16] in
-// accumulator i.  MFMA t of a 128-wide K block takes k = 32t .. 32t+31, so the
-// 4 lanes of a row read one contiguous 64-byte run per load instruction.
-template <int MT, int NT>
+// 64 weight rows (output columns), wave w the 16 rows 16w..; K blocks of 128
+// in order, the workgroup's share of them when K is split (part z of S writes
+// C + z * pstride, the reader adds the slabs).  Each activation block (M rows
+// x 128) is loaded once per workgroup, coalesced, into LDS and read by all four
+// waves; each wave streams its weight rows straight into registers, four K
+// blocks ahead.  Operand layout of the 16x16x32 MFMA: lane l supplies row
+// l % 16 and k-slots 8 (l/16) .. +7 of A (and of B), and receives
+// C[4 (l/16) + i][l % 16] in accumulator i; MFMA t of a block takes k = 32t ..
+// 32t+31.
+template <int MT>
 __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict__ A, int lda, const GemmW W, int N,
-                                                     int K, float *__restrict__ C, int ldc, int M) {
-    __shared__ float red[4][NT * MT][16][17];
+                                                     int K, float *__restrict__ C, int ldc, int M, int S,
+                                                     size_t pstride) {
+    constexpr int AP = 128 + 8;                    // LDS row pitch (bf16)
+    __shared__ __attribute__((aligned(16))) __bf16 As[2][16 * MT][AP];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16 * NT;
-    const uint16_t *wrow[NT];
+    const int n0 = blockIdx.x * 64 + 16 * wave;
+    const int nkb = K / 128, kb0 = (int)((long)blockIdx.y * nkb / S), kb1 = (int)((long)(blockIdx.y + 1) * nkb / S);
+    const int nk = kb1 - kb0, last = nk - 1;
+    const uint16_t *wrow = seg_row<uint16_t>(W, n0 + r < N ? n0 + r : N - 1, K) + (size_t)kb0 * 128 + 8 * g;
+    // activation loader: thread t takes row t / 4 (rows >= 16 MT idle), the 32
+    // bf16 at 32 (t % 4) of the block
+    const int arw = tid >> 2, acl = (tid & 3) * 32;
+    const bool aload = arw < 16 * MT;
+    const uint16_t *arow = A + (size_t)(arw < M ? arw : M - 1) * lda + (size_t)kb0 * 128 + acl;
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    u4 w0[4], w1[4], w2[4], w3[4], a0[4], a1[4], a2[4], a3[4];
+#define WLOAD(wv, j)                                                                        \
+    do {                                                                                    \
+        const int k_ = ((j) < last ? (j) : last) * 128;                                     \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) wv[t] = *reinterpret_cast<const u4 *>(wrow + k_ + 32 * t); \
+    } while (0)
+#define ALOAD(av, j)                                                                        \
+    do {                                                                                    \
+        const int k_ = ((j) < last ? (j) : last) * 128;                                     \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) av[t] = *reinterpret_cast<const u4 *>(arow + k_ + 8 * t); \
+    } while (0)
+#define ASTORE(buf, av)                                                                     \
+    do {                                                                                    \
+        if (aload) _Pragma("unroll") for (int t = 0; t < 4; ++t)                            \
+            *reinterpret_cast<u4 *>(&As[buf][arw][acl + 8 * t]) = av[t];                    \
+    } while (0)
+    f32x4_t acc[MT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int n = n0 + 16 * nt + r < N ? n0 + 16 * nt + r : N - 1;
-        wrow[nt] = seg_row<uint16_t>(W, n, K) + 8 * g;
-    }
-    const uint16_t *arow[MT];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        const int m = 16 * mt + r < M ? 16 * mt + r : M - 1;
-        arow[mt] = A + (size_t)m * lda + 8 * g;
-    }
-    f32x4_t acc[NT][MT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[nt][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    uint4 w0[NT][4], a0[MT][4], w1[NT][4], a1[MT][4];
-    auto load = [&](uint4 (&wv)[NT][4], uint4 (&av)[MT][4], int kb) {
-        const int k = kb * 128;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) wv[nt][t] = *reinterpret_cast<const uint4 *>(wrow[nt] + k + 32 * t);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) av[mt][t] = *reinterpret_cast<const uint4 *>(arow[mt] + k + 32 * t);
-    };
-    auto mma = [&](const uint4 (&wv)[NT][4], const uint4 (&av)[MT][4]) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                    acc[nt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av[mt][t]), __builtin_bit_cast(bf16x8, wv[nt][t]), acc[nt][mt],
-                        0, 0, 0);
-    };
-    const int nkb = K / 128;
-    if (wave < nkb) load(w0, a0, wave);
-    for (int kb = wave; kb < nkb; kb += 8) {
-        if (kb + 4 < nkb) load(w1, a1, kb + 4);
-        mma(w0, a0);
-        if (kb + 8 < nkb) load(w0, a0, kb + 8);
-        if (kb + 4 < nkb) mma(w1, a1);
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) red[wave][nt * MT + mt][4 * g + i][r] = acc[nt][mt][i];
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#define MMA(wv, buf)                                                                        \
+    do {                                                                                    \
+        _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                     \
+            const bf16x8 b_ = __builtin_bit_cast(bf16x8, wv[t]);                            \
+            _Pragma("unroll") for (int mt = 0; mt < MT; ++mt) {                             \
+                const bf16x8 a_ = *reinterpret_cast<const bf16x8 *>(&As[buf][16 * mt + r][32 * t + 8 * g]); \
+                acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_, b_, acc[mt], 0, 0, 0); \
+            }                                                                               \
+        }                                                                                   \
+    } while (0)
+    // Unconditional loads (past the last block they repeat it) and a loop
+    // unrolled by four keep the compiler's count of outstanding loads exact.
+    // activations and weights both four K blocks ahead: block j sits in
+    // registers a(j%4) and w(j%4) until it is consumed
+    ALOAD(a0, 0);
+    ALOAD(a1, 1);
+    ALOAD(a2, 2);
+    ALOAD(a3, 3);
+    WLOAD(w0, 0);
+    WLOAD(w1, 1);
+    WLOAD(w2, 2);
+    WLOAD(w3, 3);
+    ASTORE(0, a0);
+    ALOAD(a0, 4);
     __syncthreads();
-    for (int idx = tid; idx < NT * MT * 256; idx += 256) {
-        const int tt = idx >> 8, mm = (idx >> 4) & 15, c = idx & 15;
-        const int nt = tt / MT, mt = tt % MT;
-        const int m = 16 * mt + mm, nn = n0 + 16 * nt + c;
-        if (m < M && nn < N)
-            C[(size_t)m * ldc + nn] = red[0][tt][mm][c] + red[1][tt][mm][c] + red[2][tt][mm][c] + red[3][tt][mm][c];
+#define STEP(j, wv, an, buf)                                                                \
+    MMA(wv, buf);                                                                           \
+    if (kb + (j) + 1 >= nk) break;                                                          \
+    ASTORE((buf) ^ 1, an);                                                                  \
+    ALOAD(an, kb + (j) + 5);                                                                \
+    WLOAD(wv, kb + (j) + 4);                                                                \
+    __syncthreads();
+    for (int kb = 0; kb < nk; kb += 4) {
+        STEP(0, w0, a1, 0)
+        STEP(1, w1, a2, 1)
+        STEP(2, w2, a3, 0)
+        STEP(3, w3, a0, 1)
     }
-}
-
-template <int MT>
-void launch_skinny(const uint16_t *A, int lda, const GemmW &W, int N, int K, float *C, int ldc, int M,
-                   hipStream_t s) {
-    if ((N + 15) / 16 >= 512)
-        hipLaunchKernelGGL((k_gemm_skinny<MT, 2>), dim3((N + 31) / 32), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
-    else
-        hipLaunchKernelGGL((k_gemm_skinny<MT, 1>), dim3((N + 15) / 16), dim3(256), 0, s, A, lda, W, N, K, C, ldc, M);
+#undef STEP
+#undef MMA
+#undef ASTORE
+#undef ALOAD
+#undef WLOAD
+    float *Cz = C + (size_t)blockIdx.y * pstride;
+    const int nn = n0 + r;
+    if (nn < N)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * mt + 4 * g + i;
+                if (m < M) Cz[(size_t)m * ldc + nn] = acc[mt][i];
+            }
 }
 
 }  // namespace
@@ -499,9 +512,10 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
     const GemmW W = Wb;
     if (wtype == kBF16 && Ab && lda % 8 == 0) {
         if (M <= 64 && K % 128 == 0) {
-            if (M <= 16) launch_skinny<1>(Ab, lda, W, N, K, C, ldc, M, s);
-            else if (M <= 32) launch_skinny<2>(Ab, lda, W, N, K, C, ldc, M, s);
-            else launch_skinny<4>(Ab, lda, W, N, K, C, ldc, M, s);
+            const dim3 grid((N + 63) / 64, kparts);
+            if (M <= 16) hipLaunchKernelGGL((k_gemm_skinny<1>), grid, dim3(256), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
+            else if (M <= 32) hipLaunchKernelGGL((k_gemm_skinny<2>), grid, dim3(256), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
+            else hipLaunchKernelGGL((k_gemm_skinny<4>), grid, dim3(256), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
             return hipGetLastError();
         }
         if (M > 64 && K % 64 == 0) {
@@ -533,11 +547,19 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
 }
 
 bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts) {
-    return wtype == kBF16 && have_bf16 && M > 64 && kparts <= kMaxKParts && K % (64 * kparts) == 0;
+    if (wtype != kBF16 || !have_bf16 || kparts > kMaxKParts) return false;
+    if (M <= 64) return K % 128 == 0 && K / 128 >= kparts;     // k_gemm_skinny: K blocks dealt out
+    return K % (64 * kparts) == 0;
 }
 
 int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K) {
     if (!gemm_splits_ok(wtype, have_bf16, M, K, 1)) return 1;
+    if (M <= 64) {  // about 256 workgroups of 64 weight rows, at least 4 K blocks each
+        const int tiles = (N + 63) / 64;
+        int S = 1;
+        while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K / 128 >= 4 * S * 2) S *= 2;
+        return S;
+    }
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
     int S = 1;
     while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K % (64 * S * 2) == 0 && K / (S * 2) >= 512) S *= 2;
