@@ -51,6 +51,7 @@ struct dory {
     int H = 0, F = 0, V = 0, Q = 0, KV = 0, nh = 0, nk = 0, hd = 0, ngk = 0, wt = 0, q8 = 0;
     int cap_s = 0, cap_f = 0;
     int split_pf = 256, ms_dec = 1, ms_pf = 1;
+    int split_bs = 64, split_bf = 64, ms_bs = 1, ms_bf = 1;  // decode splits of batches
     int split_ds = 64, split_df = 64, ms_ds = 1, ms_df = 1;  // one-row calls: sliding, full layers
     int64_t win_s = 0, win_f = 0;
     // device scratch
@@ -303,8 +304,13 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
                     fz = 1;
                 }
             }
-        aa.split = l.sliding ? h->split_ds : h->split_df;
-        aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
+        if (q.T == 1) {
+            aa.split = l.sliding ? h->split_ds : h->split_df;
+            aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
+        } else {
+            aa.split = l.sliding ? h->split_bs : h->split_bf;
+            aa.max_split = l.sliding ? h->ms_bs : h->ms_bf;
+        }
         aa.field = -1;
         LAUNCH(launch_attn_dec(aa, M, q.s));
     } else {
@@ -548,20 +554,28 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
                    : cfg->max_ctx;
     const int64_t wmax = std::min<int64_t>(std::max<int64_t>(h->win_s, std::min<int64_t>(h->win_f, cfg->max_ctx)),
                                            cfg->max_ctx);
-    // One-row calls: about 64 workgroups per kv head at the longest window, each
-    // taking a multiple of the keys a workgroup covers per step.
-    const int dmax = attn_dec_max_split(h->hd), kb = 256 / (h->hd / 4);
-    auto pick = [&](int64_t W) {
-        int sp = (int)std::min<int64_t>((W + 63) / 64, dmax);
+    // Decode splits.  One-row calls: about 64 workgroups per kv head at the
+    // longest window, 8 load steps each (the latency of one short workgroup
+    // sets the pace).  Batches: about 32 per kv head with 16 load steps (the
+    // grid is large anyway, and fewer splits mean less to merge).  Each takes a
+    // multiple of the keys a workgroup covers per step.
+    const int kb = 256 / (h->hd / 4);
+    auto pick = [&](int64_t W, int steps, int target, int lo) {
+        const int dmax = attn_dec_max_split(h->hd, steps);
+        int sp = (int)std::min<int64_t>(std::max<int64_t>(lo, (W + target - 1) / target), dmax);
         sp = std::max(kb, (sp + kb - 1) / kb * kb);
         return std::min(sp, dmax);
     };
     const int64_t wf = std::min<int64_t>(h->win_f, cfg->max_ctx), ws = std::min<int64_t>(h->win_s, cfg->max_ctx);
-    h->split_ds = pick(ws);
-    h->split_df = pick(wf);
+    h->split_ds = pick(ws, 8, 64, 1);
+    h->split_df = pick(wf, 8, 64, 1);
+    h->split_bs = pick(ws, 16, 32, 64);
+    h->split_bf = pick(wf, 16, 32, 64);
     h->ms_ds = (int)((ws + h->split_ds - 1) / h->split_ds);
     h->ms_df = (int)((wf + h->split_df - 1) / h->split_df);
-    h->ms_dec = std::max(h->ms_ds, h->ms_df);
+    h->ms_bs = (int)((ws + h->split_bs - 1) / h->split_bs);
+    h->ms_bf = (int)((wf + h->split_bf - 1) / h->split_bf);
+    h->ms_dec = std::max(std::max(h->ms_ds, h->ms_df), std::max(h->ms_bs, h->ms_bf));
     // multi-row calls: at least 256 keys per split over a block's key range,
     // which is at most wmax + 127 keys
     h->split_pf = 256;
@@ -974,8 +988,8 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_gemv(h->wt, kProResolve, kEpiStore, a, s);
             break;
         case 1:
-            aa.split = l->sliding ? h->split_ds : h->split_df;
-            aa.max_split = l->sliding ? h->ms_ds : h->ms_df;
+            aa.split = h->last_T == 1 ? (l->sliding ? h->split_ds : h->split_df) : (l->sliding ? h->split_bs : h->split_bf);
+            aa.max_split = h->last_T == 1 ? (l->sliding ? h->ms_ds : h->ms_df) : (l->sliding ? h->ms_bs : h->ms_bf);
             aa.field = -1;
             e = launch_attn_dec(aa, h->last_T, s);
             break;

@@ -383,13 +383,13 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 // LDS in place of the ring row it prefetched.
 //
 // Each thread owns key slot g = tid / (HD/4) and the 4 channels dq*4.. of it;
-// the workgroup takes KB = 256/(HD/4) keys per step and IT = 8 steps.  Load
+// the workgroup takes KB = 256/(HD/4) keys per step and IT steps.  Load
 // order: the projections, sq and the RoPE row first, then every K and V load
 // of the split; the prep waits only for the first group while the cache rows
 // are in flight.
-template <int HD, int REP, int Q8>
+template <int HD, int REP, int Q8, int IT>
 __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
-    constexpr int LPK = HD / 4, KB = 256 / LPK, IT = 8;
+    constexpr int LPK = HD / 4, KB = 256 / LPK;
     constexpr int SMAX = IT * KB < 256 ? IT * KB : 256;
     constexpr int NGK = (HD + kKGroup - 1) / kKGroup;
     constexpr int HALF = HD / 2;
@@ -875,8 +875,14 @@ template <int HD, int REP>
 hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     if (T < 0) {  // decode kernel: -T rows, each of its own sequence and position
         dim3 grid(a.max_split, a.nk, -T), block(256);
-        if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0>), grid, block, 0, s, a);
+        // 8 load steps per workgroup, or 16 when the split needs them
+        if (a.split <= 8 * (256 / (HD / 4))) {
+            if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1, 8>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0, 8>), grid, block, 0, s, a);
+        } else {
+            if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1, 16>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0, 16>), grid, block, 0, s, a);
+        }
     } else if (a.blk > 0) {
         if constexpr (HD == 128 && 128 % REP == 0) {
             if (a.blk != 128 / REP) return hipErrorInvalidValue;
@@ -947,13 +953,13 @@ hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
 
 int attn_chunk_block(int hd, int rep) { return hd == 128 && 128 % rep == 0 ? 128 / rep : 0; }
 
-int attn_dec_max_split(int hd) {
+int attn_dec_max_split(int hd, int steps) {
     const int kb = 256 / (hd / 4);
-    return 8 * kb < 256 ? 8 * kb : 256;
+    return steps * kb < 256 ? steps * kb : 256;
 }
 
 hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s) {
-    if (a.split <= 0 || a.split > attn_dec_max_split(a.hd) || T <= 0) return hipErrorInvalidValue;
+    if (a.split <= 0 || a.split > attn_dec_max_split(a.hd, 16) || T <= 0) return hipErrorInvalidValue;
     return launch_hd(a, -T, s);
 }
 

@@ -190,8 +190,9 @@ hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s);
 // Rows per block of the MFMA chunk attention for this geometry, or 0 when it
 // does not serve it (head dim other than 128).
 int attn_chunk_block(int hd, int rep);
-// Keys a one-row workgroup takes at most for head dim hd.
-int attn_dec_max_split(int hd);
+// Keys a decode workgroup takes at most for head dim hd with `steps` load
+// steps (8 or 16).
+int attn_dec_max_split(int hd, int steps);
 
 // q8_2f cache writes (kv_cache.rs `append` / `freeze_cols`).
 struct Q8WriteArgs {
