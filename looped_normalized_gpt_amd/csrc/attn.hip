@@ -689,12 +689,14 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
     }
 
     // ---- loaders.  K: thread (key tid/(HD/4) + KL*i, channels 4*(tid%(HD/4))).
-    // V: thread (slot chunk ci = tid / (HD/4) (+ 256/(HD/4) per pass), channels
-    // 4*(tid%(HD/4))); chunk ci holds keys 16(ci/2) + 4(ci%2) + {0..3} and
-    // 16(ci/2) + 8 + 4(ci%2) + {0..3} in slots 8ci .. 8ci+7.
+    // V: thread (slot chunk ci = tid % 8, channels 4*(tid/8)); chunk ci holds
+    // keys 16(ci/2) + 4(ci%2) + {0..3} and 16(ci/2) + 8 + 4(ci%2) + {0..3} in
+    // slots 8ci .. 8ci+7, so 8 consecutive lanes store one 128-byte run of a
+    // V^T row (and read 128-byte runs of 8 key rows).
     constexpr int KPASS = KT / KL;           // K rows per thread
-    constexpr int VPASS = (KT / 8) / KL;     // V slot chunks per thread
+    constexpr int VPASS = 1;                 // V slot chunks per thread (8 chunks x HD/4 channel groups = 256)
     const int lc = tid % (HD / 4), lk = tid / (HD / 4);
+    const int vci = tid & 7, vlc = tid >> 3;
     float4 kr[KPASS], vr[VPASS][8];
     float ksr[KPASS], vsr[VPASS][8];
     // Ring rows of a tile: one wave-uniform remainder per tile, then a wrap
@@ -721,16 +723,16 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < VPASS; ++i) {
-            const int ci = lk + KL * i;
+            const int ci = vci;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int kk = 16 * (ci >> 1) + 8 * (j >> 2) + 4 * (ci & 1) + (j & 3);
                 const size_t row = key_row(kk);
                 if (Q8) {
-                    vr[i][j] = gld_codes4(sd.vc + row * HD + 4 * lc);
+                    vr[i][j] = gld_codes4(sd.vc + row * HD + 4 * vlc);
                     vsr[i][j] = gld<float>(sd.vs + row);
                 } else {
-                    vr[i][j] = gld4(sd.v + row * HD + 4 * lc);
+                    vr[i][j] = gld4(sd.v + row * HD + 4 * vlc);
                 }
             }
         }
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < VPASS; ++i) {
-            const int ci = lk + KL * i;
+            const int ci = vci;
             bf16x8_t col[4];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -754,7 +756,7 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
                 col[0][j] = (__bf16)x.x; col[1][j] = (__bf16)x.y; col[2][j] = (__bf16)x.z; col[3][j] = (__bf16)x.w;
             }
 #pragma unroll
-            for (int c = 0; c < 4; ++c) *reinterpret_cast<bf16x8_t *>(&Vt[buf][4 * lc + c][8 * ci]) = col[c];
+            for (int c = 0; c < 4; ++c) *reinterpret_cast<bf16x8_t *>(&Vt[buf][4 * vlc + c][8 * ci]) = col[c];
         }
     };
 

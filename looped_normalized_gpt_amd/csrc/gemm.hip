@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
 // registers), STAGES deep: the loads of STAGES-1 K steps stay in flight while
 // one step is computed, which covers the memory latency that a one-step
 // register prefetch left exposed.  A tile row (64 bf16 = 8 chunks of 16 bytes)
-// is stored with chunk c at position c ^ (row % 8), so the 32 rows a wave
+// is stored with chunk c at position c ^ ((row / 2) % 8), so the rows a wave
 // reads for one MFMA operand fall in different banks.  One workgroup per CU
 // (STAGES x 32 KB of LDS).
 // LDS byte address of a shared-memory pointer
@@ -316,13 +316,16 @@ __global__ __launch_bounds__(512) void k_gemm_dma(const uint16_t *__restrict__ A
     const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
     const int Kp = K / S, kz = blockIdx.z * Kp;
     // DMA: load j (0..1) of wave w covers tile rows 16 w + 8 j .. +7; lane l
-    // reads row 16 w + 8 j + l/8, global chunk (l % 8) ^ (l / 8), and lands at
-    // chunk l % 8 of that row
-    const int crow = lane >> 3, csrc = (lane & 7) ^ crow;
+    // reads row r = 16 w + 8 j + l/8, global chunk (l % 8) ^ sw(r), and lands at
+    // chunk l % 8 of that row.  sw(r) = (r / 2) % 8: the 16 rows a group of 16
+    // lanes reads at one logical chunk then sit in 16 different bank groups
+    // (two 128-byte rows share a 256-byte bank line).
+    const int crow = lane >> 3;
     const uint16_t *asrc[2], *bsrc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int row = 16 * wave + 8 * j + crow;
+        const int csrc = (lane & 7) ^ ((row >> 1) & 7);
         const int gm = m0 + row < M ? m0 + row : M - 1;
         const int gn = n0 + row < N ? n0 + row : N - 1;
         asrc[j] = A + (size_t)gm * lda + kz + 8 * csrc;
@@ -375,8 +378,9 @@ __global__ __launch_bounds__(512) void k_gemm_dma(const uint16_t *__restrict__ A
                 "ds_read_b128 %2, %5\n\t"
                 "s_waitcnt lgkmcnt(0)"
                 : "=v"(a0), "=v"(a1), "=v"(b)
-                : "v"(As + 2 * (ra0 * BK + 8 * (ch ^ (ra0 & 7)))), "v"(As + 2 * (ra1 * BK + 8 * (ch ^ (ra1 & 7)))),
-                  "v"(Bs + 2 * (rb * BK + 8 * (ch ^ (rb & 7)))));
+                : "v"(As + 2 * (ra0 * BK + 8 * (ch ^ ((ra0 >> 1) & 7)))),
+                  "v"(As + 2 * (ra1 * BK + 8 * (ch ^ ((ra1 >> 1) & 7)))),
+                  "v"(Bs + 2 * (rb * BK + 8 * (ch ^ ((rb >> 1) & 7)))));
             acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
             acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
         }
