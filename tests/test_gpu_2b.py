@@ -146,3 +146,20 @@ def test_2b_q8_prompt_crosses_freeze_and_wrap(model2b, D):
     calls = [toks[:40], toks[40:70], toks[70:170], toks[170:200], toks[200:]]
     check_pair(run_pair(g, o, calls, 2, "last_loop"), COS, DLOGIT, "2b q8 prompt")
     g.close()
+
+
+def test_2b_full_chunk_past_the_window(model2b, D):
+    """The prefill benchmark's launch configuration: a 512-row call (the
+    512-row GEMM kernels with split K, 16 row blocks of the MFMA chunk
+    attention) on a loaded context of 700 rows, so the sliding layers' window
+    cuts through the chunk; loops 1 keeps the oracle's share to seconds."""
+    cfg, w = model2b
+    k, v = _rows(cfg, 700, 1, seed=15)
+    g = D.Dory(cfg, w, max_ctx=1300, max_chunk=512)
+    o = O.Oracle(cfg, w, max_ctx=1300)
+    g.kv_load(k, v, "last_loop", 1)
+    o.kv_load(k, v, "last_loop", 1)
+    toks = synth.make_tokens(513, cfg["vocab"], seq=16)
+    say("2b chunk of 512 at 700 + 1 decode, loops 1")
+    check_pair(run_pair(g, o, [toks[:512], toks[512:]], 1, "last_loop"), COS, DLOGIT, "2b full chunk")
+    g.close()

@@ -131,3 +131,47 @@ def test_batch_errors_change_nothing(D):
     torch.cuda.synchronize()
     assert [g.position(s) for s in range(4)] == [1, 4, 0, 0]
     g.close()
+
+
+def test_2b_batch_of_64_in_the_benchmark_shape(D):
+    """The batched benchmark's launch configuration: 64 rows in one call (skinny
+    GEMMs on four 16-row tiles with split K, the 16-step decode attention, the
+    multi-row merge) with loop counts drawn from 1..16, rows at different
+    contexts.  Every row is one sequence's next token; six sampled rows are
+    checked against the oracle run on that sequence alone."""
+    import torch
+    cfg = synth.config("2b")
+    w = synth.make_weights(cfg)
+    nseq = 64
+    rng = np.random.default_rng(21)
+    lens = rng.integers(40, 1300, nseq)            # some past the 1024-key window
+    g = D.Dory(cfg, w, max_ctx=1400, max_chunk=512, max_seqs=nseq)
+    n_ord = g.n_ord
+    rows = {}
+    for s in range(nseq):
+        k, v = synth.make_kv_rows(n_ord * int(lens[s]), cfg["nk"], cfg["hd"], cfg["hidden"], seed=200 + s)
+        shp = (n_ord, 1, int(lens[s]), cfg["nk"], cfg["hd"])
+        rows[s] = (k.reshape(shp), v.reshape(shp))
+        g.kv_load(rows[s][0], rows[s][1], "last_loop", 1, seq=s)
+    seqs = np.arange(nseq, dtype=np.int32)
+    toks = rng.integers(0, cfg["vocab"], nseq).astype(np.int32)
+    loops = synth.make_loops(nseq, seed=22)
+    say(f"2b batch of 64, loops {loops.min()}..{loops.max()}")
+    lg = g.forward_batch(seqs, toks, loops, "last_loop")
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy()
+    assert np.isfinite(lg).all()
+    sample = [int(np.argmax(loops)), int(np.argmin(loops)), int(np.argmax(lens)), 5, 33, 62]
+    worst = 0.0
+    for s in sample:
+        o = O.Oracle(cfg, w, max_ctx=1400)
+        o.kv_load(rows[s][0], rows[s][1], "last_loop", 1)
+        ol, _ = o.forward(toks[s:s + 1], int(loops[s]), "last_loop")
+        o.close()
+        d = float(np.abs(lg[s] - ol).max())
+        worst = max(worst, d)
+        assert d <= 5e-2, f"row {s} (context {lens[s]}, loops {loops[s]}): |dlogit| {d:.3e}"
+    for s in range(nseq):
+        assert g.position(s) == lens[s] + 1
+    say(f"2b batch of 64: worst |dlogit| over rows {sample}: {worst:.3e}")
+    g.close()
