@@ -100,7 +100,9 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
     if (Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup)))
         vcol = slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + dc];
     int nsplit;
-    if (a.blk > 0) {  // k_fattn: the splits of the row's block of a.blk rows
+    if (a.dec) {  // decode kernel: every slab of the grid, those past the row's keys hold max -inf
+        nsplit = a.max_split;
+    } else if (a.blk > 0) {  // k_fattn: the splits of the row's block of a.blk rows
         const int rb0 = r / a.blk * a.blk, rb1 = (rb0 + a.blk < a.rec->n ? rb0 + a.blk : a.rec->n) - 1;
         const int64_t pos0 = a.rec->rows[0].pos;
         const int64_t klo = pos0 + rb0 + 1 - a.window > 0 ? pos0 + rb0 + 1 - a.window : 0;
@@ -169,7 +171,9 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
     const int Q = a.nh * HD, ld = 2 * Q + 2 * a.nk * HD;
     const int64_t p = a.rec->rows[r].pos;
     int nsplit;
-    if (a.blk > 0) {
+    if (a.dec) {  // decode kernel: every slab of the grid, those past the row's keys hold max -inf
+        nsplit = a.max_split;
+    } else if (a.blk > 0) {
         const int rb0 = r / a.blk * a.blk, rb1 = (rb0 + a.blk < a.rec->n ? rb0 + a.blk : a.rec->n) - 1;
         const int64_t pos0 = a.rec->rows[0].pos;
         const int64_t klo = pos0 + rb0 + 1 - a.window > 0 ? pos0 + rb0 + 1 - a.window : 0;
@@ -410,7 +414,11 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int64_t nkeys = p - lo + 1;
     const int nsplit = (int)((nkeys + a.split - 1) / a.split);
-    if (s >= nsplit) return;
+    if (s >= nsplit) {  // no key here: the merge skips a slab whose max is -inf
+        if (tid < REP)
+            a.part[(((size_t)r * a.nk + kh) * a.max_split + s) * REP * (HD + 2) + (size_t)tid * (HD + 2)] = -INFINITY;
+        return;
+    }
     const int64_t e0 = lo + (int64_t)s * a.split;
     const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
     const bool tail = s == nsplit - 1;
@@ -876,6 +884,7 @@ __global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
 template <int HD, int REP>
 hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     if (T < 0) {  // decode kernel: -T rows, each of its own sequence and position
+        if (!a.dec) return hipErrorInvalidValue;
         dim3 grid(a.max_split, a.nk, -T), block(256);
         // 8 load steps per workgroup, or 16 when the split needs them
         if (a.split <= 8 * (256 / (HD / 4))) {
@@ -950,7 +959,9 @@ hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
     if (a.split <= 0 || T <= 0 || (a.blk == 0 && a.split > 256) || (a.blk > 0 && a.split % 64))
         return hipErrorInvalidValue;
-    return launch_hd(a, T, s);
+    AttnArgs b = a;
+    b.dec = 0;
+    return launch_hd(b, T, s);
 }
 
 int attn_chunk_block(int hd, int rep) { return hd == 128 && 128 % rep == 0 ? 128 / rep : 0; }
@@ -962,7 +973,9 @@ int attn_dec_max_split(int hd, int steps) {
 
 hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s) {
     if (a.split <= 0 || a.split > attn_dec_max_split(a.hd, 16) || T <= 0) return hipErrorInvalidValue;
-    return launch_hd(a, -T, s);
+    AttnArgs b = a;
+    b.dec = 1;
+    return launch_hd(b, -T, s);
 }
 
 }  // namespace dk

@@ -180,6 +180,8 @@ struct AttnArgs {
     // 64; 0: one row per workgroup (k_attn), split <= 256
     int32_t blk;
     int32_t nsplit;      // k_fattn: grid.x, the most splits a block has
+    int32_t dec;         // 1: the decode kernel (launch_attn_dec), whose merge reads all
+                         // max_split slabs of a row; 0: the multi-row kernels
 };
 // Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
