@@ -72,7 +72,7 @@ struct dory {
     bool stage_used[kStages]{};
     int stage_i = 0;
     hipStream_t cap_stream = nullptr;
-    std::map<std::tuple<int, int>, hipGraphExec_t> graphs;
+    std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;  // one-row calls by (loops, kv mode, sequence)
     float *tap = nullptr;
     int64_t tap_cap = 0;
     std::vector<SeqState> seqs;
@@ -82,6 +82,7 @@ struct dory {
     int last_T = 0, last_loops = 0, last_mode = -1;
     bool last_chunk = false;
     int64_t last_pos0 = 0;
+    int last_seq0 = 0;
 };
 
 namespace {
@@ -307,6 +308,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         if (q.T == 1) {
             aa.split = l.sliding ? h->split_ds : h->split_df;
             aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
+            aa.sd1 = h->tab + ((size_t)q.seq[0] * h->n_ord + l.ord) * kMaxLoops + slot;
         } else {
             aa.split = l.sliding ? h->split_bs : h->split_bf;
             aa.max_split = l.sliding ? h->ms_bs : h->ms_bf;
@@ -702,7 +704,7 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
     const bool graphable = n == 1 && (!h->q8 || st.pos >= kWarmup + 1);
     if (graphable) {
-        auto key = std::make_tuple(loops, kv_mode);
+        auto key = std::make_tuple(loops, kv_mode, seq);
         auto it = h->graphs.find(key);
         if (it == h->graphs.end()) {
             Enq cq = q;
@@ -732,6 +734,7 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     h->last_loops = loops;
     h->last_mode = kv_mode;
     h->last_pos0 = st.pos;
+    h->last_seq0 = seq;
     st.pos += n;
     st.mode = kv_mode;
     if (kv_mode == DORY_PER_LOOP) st.loops = loops;
@@ -794,6 +797,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
     rc = enqueue(q);
     if (rc) return rc;
     h->last_T = nseq;
+    h->last_seq0 = seqs[0];
     h->last_chunk = false;
     h->last_loops = lmax;
     h->last_mode = kv_mode;
@@ -990,6 +994,7 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
         case 1:
             aa.split = h->last_T == 1 ? (l->sliding ? h->split_ds : h->split_df) : (l->sliding ? h->split_bs : h->split_bf);
             aa.max_split = h->last_T == 1 ? (l->sliding ? h->ms_ds : h->ms_df) : (l->sliding ? h->ms_bs : h->ms_bf);
+            if (h->last_T == 1) aa.sd1 = h->tab + ((size_t)h->last_seq0 * h->n_ord + l->ord) * kMaxLoops + aa.slot;
             aa.field = -1;
             e = launch_attn_dec(aa, h->last_T, s);
             break;

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
     const int64_t p = a.rec->rows[r].pos;
     float vcol = 1.f;
     if (Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup)))
-        vcol = slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * hd + dc];
+        vcol = (a.sd1 ? *a.sd1 : slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot)).vcol[kh * hd + dc];
     int nsplit;
     if (a.dec) {  // decode kernel: every slab of the grid, those past the row's keys hold max -inf
         nsplit = a.max_split;
@@ -410,7 +410,15 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const CallRec *rec = a.rec;
+    // the slot's descriptor and the row's position, fetched together when the
+    // caller names the slot (pinned: else the compiler sinks the descriptor's
+    // load below the early exit, behind the position)
+    SlotDesc sd;
+    if (a.sd1) sd = *a.sd1;
+    else sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
     const int64_t p = rec->rows[r].pos;
+    if (Q8) asm volatile("" ::"s"(sd.cap), "s"(sd.kc), "s"(sd.vc), "s"(sd.ks), "s"(sd.vs));
+    else asm volatile("" ::"s"(sd.cap), "s"(sd.k), "s"(sd.v));
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int64_t nkeys = p - lo + 1;
     const int nsplit = (int)((nkeys + a.split - 1) / a.split);
@@ -423,7 +431,6 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
     const bool tail = s == nsplit - 1;
     const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
-    const SlotDesc &sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
     const int cap = sd.cap;
     const int Q = a.nh * HD, KV = a.nk * HD;
     const int g = tid / LPK, dq = tid % LPK;
@@ -617,6 +624,203 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     if (tid < REP) {
         mine[tid * (HD + 2)] = stat[0][tid];
         mine[tid * (HD + 2) + 1] = stat[1][tid];
+    }
+}
+
+// Decode attention of one row for head dim 128, 64 keys per workgroup: the
+// arithmetic of k_attn_dec with its steps laid out for short latency.
+//   0. Wave w loads vectors w, w+4, .. of the group's REP query heads and, as
+//      vector REP, the new key: lane j holds elements j and j+64, which are
+//      exactly the pairs RoPE rotates, so RoPE, the unit norm and the sq scale
+//      run in registers and one sync publishes them.  Every K and V load of the
+//      split is issued behind these loads, 16 bytes per lane, 8 keys a step.
+//   1. The split's K and V rows go to LDS in fp32 (q8_2f: codes times their
+//      scales; the key field and 1/sqrt(hd) are folded into the queries).
+//   2. Wave w takes heads w, w+4, ..: lane e scores key e against the head's
+//      query from LDS, and the softmax of the head's 64 keys stays in the wave.
+//   3. Lane l accumulates channels 2l, 2l+1 over the 64 keys, taking each
+//      key's weight from its lane (readlane), and stores the partial.
+template <int REP, int Q8>
+__global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
+    constexpr int HD = 128, HALF = 64, NK = 64, KP = HD + 4, IT = NK / 8;
+    constexpr int NGK = HD / kKGroup;
+    constexpr int VPW = (REP + 1 + 3) / 4;  // vectors a wave prepares
+    __shared__ float Ks[NK][KP], Vs[NK][KP];
+    __shared__ float qs[REP + 1][HD];  // queries (times the key field and 1/sqrt(hd)), then the new key
+    __shared__ float vn[HD];
+    __shared__ int8_t kcn[HD], vcn[HD];
+    __shared__ float ksn[NGK], vsn[1];
+    const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const CallRec *rec = a.rec;
+    SlotDesc sd;
+    if (a.sd1) sd = *a.sd1;
+    else sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
+    const int64_t p = rec->rows[r].pos;
+    if (Q8) asm volatile("" ::"s"(sd.cap), "s"(sd.kc), "s"(sd.vc), "s"(sd.ks), "s"(sd.vs));
+    else asm volatile("" ::"s"(sd.cap), "s"(sd.k), "s"(sd.v));
+    const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+    const int64_t nkeys = p - lo + 1;
+    const int nsplit = (int)((nkeys + a.split - 1) / a.split);
+    if (s >= nsplit) {  // no key here: the merge skips a slab whose max is -inf
+        if (tid < REP)
+            a.part[(((size_t)r * a.nk + kh) * a.max_split + s) * REP * (HD + 2) + (size_t)tid * (HD + 2)] = -INFINITY;
+        return;
+    }
+    const int64_t e0 = lo + (int64_t)s * a.split;
+    const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
+    const bool tail = s == nsplit - 1;
+    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    const int cap = sd.cap;
+    const int Q = a.nh * HD, KV = a.nk * HD;
+    const int g = tid >> 5, dq = tid & 31;
+
+    // ---- 0. the prologue's inputs, then every cache row of the split
+    const float *qrow = a.qkvg + (size_t)r * (2 * Q + 2 * KV);
+    float x0[VPW], x1[VPW], s0[VPW], s1[VPW];
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+        const int v = wave + 4 * i < REP + 1 ? wave + 4 * i : REP;
+        const float *src = v < REP ? qrow + (size_t)(kh * REP + v) * HD : qrow + Q + (size_t)kh * HD;
+        x0[i] = src[lane];
+        x1[i] = src[lane + HALF];
+        const int vq = v < REP ? v : 0;
+        s0[i] = a.sq[(size_t)(kh * REP + vq) * HD + lane];
+        s1[i] = a.sq[(size_t)(kh * REP + vq) * HD + lane + HALF];
+    }
+    const float vr0 = qrow[Q + KV + (size_t)kh * HD + lane], vr1 = qrow[Q + KV + (size_t)kh * HD + lane + HALF];
+    const float cs = a.rope[(size_t)p * HD + lane], sn = a.rope[(size_t)p * HD + HALF + lane];
+    const int rbase = (int)(e0 % cap);
+    float4 kr[IT], vr[IT];
+    float ksr[IT], vsr[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = g + 8 * it;
+        int rr = rbase + (e < len ? e : 0);
+        if (rr >= cap) rr -= cap;
+        const size_t row = (size_t)kh * cap + rr;
+        if (Q8) {
+            kr[it] = gld_codes4(sd.kc + row * HD + dq * 4);
+            vr[it] = gld_codes4(sd.vc + row * HD + dq * 4);
+            ksr[it] = gld<float>(sd.ks + row * NGK + (dq * 4) / kKGroup);
+            vsr[it] = gld<float>(sd.vs + row);
+        } else {
+            kr[it] = gld4(sd.k + row * HD + dq * 4);
+            vr[it] = gld4(sd.v + row * HD + dq * 4);
+        }
+    }
+    // the prologue waits only for its own loads (issued first)
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) asm volatile("" ::"v"(x0[i]), "v"(x1[i]), "v"(s0[i]), "v"(s1[i]));
+    asm volatile("" ::"v"(vr0), "v"(vr1), "v"(cs), "v"(sn));
+
+    // ---- RoPE, unit norm, sq (queries) in registers
+    float kc0 = 1.f, kc1 = 1.f;
+    if (field) {
+        kc0 = gld<float>(sd.kcol + kh * HD + lane);
+        kc1 = gld<float>(sd.kcol + kh * HD + lane + HALF);
+    }
+    const float scale = 1.0f / sqrtf((float)HD);
+#pragma unroll
+    for (int i = 0; i < VPW; ++i) {
+        const int v = wave + 4 * i;
+        if (v > REP) break;
+        const float y0 = x0[i] * cs - x1[i] * sn, y1 = x1[i] * cs + x0[i] * sn;
+        const float f = norm_factor(wave_sum(y0 * y0 + y1 * y1));
+        if (v < REP) {
+            qs[v][lane] = y0 * f * s0[i] * kc0 * scale;
+            qs[v][lane + HALF] = y1 * f * s1[i] * kc1 * scale;
+        } else {
+            qs[REP][lane] = y0 * f;
+            qs[REP][lane + HALF] = y1 * f;
+            vn[lane] = vr0;
+            vn[lane + HALF] = vr1;
+        }
+    }
+    __syncthreads();
+
+    // ---- the new row: into the cache, and in place of its prefetched copy
+    if (tail) {
+        const size_t row = (size_t)kh * cap + (size_t)(p % cap);
+        if (Q8) {
+            if (wave == 0) encode_row(qs[REP], field ? sd.kcol + kh * HD : nullptr, HD, kKGroup, kcn, ksn);
+            if (wave == 1) encode_row(vn, field ? sd.vcol + kh * HD : nullptr, HD, HD, vcn, vsn);
+            __syncthreads();
+            if (!a.no_write) {
+                if (tid < HD) {
+                    sd.kc[row * HD + tid] = kcn[tid];
+                    sd.vc[row * HD + tid] = vcn[tid];
+                }
+                if (tid < NGK) sd.ks[row * NGK + tid] = ksn[tid];
+                if (tid == 0) sd.vs[row] = vsn[0];
+            }
+        } else if (!a.no_write && tid < HD) {
+            sd.k[row * HD + tid] = qs[REP][tid];
+            sd.v[row * HD + tid] = vn[tid];
+        }
+        const int el = len - 1;
+        if (g == el % 8) {
+#pragma unroll
+            for (int it = 0; it < IT; ++it) {
+                if (it != el / 8) continue;
+                if (Q8) {
+                    const char4 kc = *reinterpret_cast<const char4 *>(kcn + dq * 4);
+                    const char4 vc = *reinterpret_cast<const char4 *>(vcn + dq * 4);
+                    kr[it] = make_float4((float)kc.x, (float)kc.y, (float)kc.z, (float)kc.w);
+                    vr[it] = make_float4((float)vc.x, (float)vc.y, (float)vc.z, (float)vc.w);
+                    ksr[it] = ksn[(dq * 4) / kKGroup];
+                    vsr[it] = vsn[0];
+                } else {
+                    kr[it] = *reinterpret_cast<const float4 *>(&qs[REP][dq * 4]);
+                    vr[it] = *reinterpret_cast<const float4 *>(&vn[dq * 4]);
+                }
+            }
+        }
+    }
+
+    // ---- 1. the split's rows to LDS
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+        const int e = g + 8 * it;
+        float4 k = kr[it], v = vr[it];
+        if (Q8) {
+            k.x *= ksr[it]; k.y *= ksr[it]; k.z *= ksr[it]; k.w *= ksr[it];
+            v.x *= vsr[it]; v.y *= vsr[it]; v.z *= vsr[it]; v.w *= vsr[it];
+        }
+        *reinterpret_cast<float4 *>(&Ks[e][dq * 4]) = k;
+        *reinterpret_cast<float4 *>(&Vs[e][dq * 4]) = v;
+    }
+    __syncthreads();
+
+    // ---- 2, 3. per head: scores of lane e's key, softmax, values
+    const size_t pstride = (size_t)REP * (HD + 2);
+    float *mine = a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride;
+    for (int h = wave; h < REP; h += 4) {
+        float d = 0.f;
+#pragma unroll
+        for (int c = 0; c < HD; c += 4) {
+            const float4 k = *reinterpret_cast<const float4 *>(&Ks[lane][c]);
+            const float4 q = *reinterpret_cast<const float4 *>(&qs[h][c]);
+            d += k.x * q.x + k.y * q.y + k.z * q.z + k.w * q.w;
+        }
+        const float sc = lane < len ? d : -INFINITY;
+        const float m = wave_max(sc);
+        const float pe = expf(sc - m);  // 0 past len
+        const float l = wave_sum(pe);
+        float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+        for (int e = 0; e < NK; ++e) {
+            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), e));
+            const float2 v = *reinterpret_cast<const float2 *>(&Vs[e][2 * lane]);
+            acc0 += w * v.x;
+            acc1 += w * v.y;
+        }
+        float *dst = mine + (size_t)h * (HD + 2);
+        *reinterpret_cast<float2 *>(dst + 2 + 2 * lane) = make_float2(acc0, acc1);
+        if (lane == 0) {
+            dst[0] = m;
+            dst[1] = l;
+        }
     }
 }
 
@@ -886,8 +1090,12 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     if (T < 0) {  // decode kernel: -T rows, each of its own sequence and position
         if (!a.dec) return hipErrorInvalidValue;
         dim3 grid(a.max_split, a.nk, -T), block(256);
-        // 8 load steps per workgroup, or 16 when the split needs them
-        if (a.split <= 8 * (256 / (HD / 4))) {
+        // one row, head dim 128, up to 64 keys a workgroup: the short-latency
+        // kernel; else 8 load steps per workgroup, or 16 when the split needs them
+        if (HD == 128 && T == -1 && a.split <= 64) {
+            if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_dec1<REP, 0>), grid, block, 0, s, a);
+        } else if (a.split <= 8 * (256 / (HD / 4))) {
             if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1, 8>), grid, block, 0, s, a);
             else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0, 8>), grid, block, 0, s, a);
         } else {

@@ -180,6 +180,9 @@ struct AttnArgs {
     // 64; 0: one row per workgroup (k_attn), split <= 256
     int32_t blk;
     int32_t nsplit;      // k_fattn: grid.x, the most splits a block has
+    // one-row calls: the row's slot table entry, read without waiting for the
+    // record's sequence; null: looked up by the record
+    const SlotDesc *sd1;
     int32_t dec;         // 1: the decode kernel (launch_attn_dec), whose merge reads all
                          // max_split slabs of a row; 0: the multi-row kernels
 };
