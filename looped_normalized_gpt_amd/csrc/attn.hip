@@ -77,17 +77,15 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
 
 // Merges the split partials of (row r, q head h) in log-sum-exp form, scales by
 // the V field (q8), applies the sigmoid gate (dory.rs `gate_body`) and writes z.
-// Grid (T, nh, ceil(hd/64)); lane d of every wave owns one channel, wave w takes
-// splits w, w + waves, ... with a running (max, sum, acc) merge, then wave 0
-// merges the waves' results.  A kernel of its own: the partials come from
-// workgroups on other XCDs, whose L2s are only coherent with this one at kernel
-// boundaries.
-template <int Q8>
-__global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
-    constexpr int U = 8;  // splits a wave holds in flight
-    __shared__ float sm[16][66];
+// Grid (T, nh, ceil(hd/64)), 4 waves; lane d owns one channel, wave w takes
+// splits w, w+4, .. with all U of its loads in flight before the running
+// (max, sum, acc) merge, then wave 0 merges the 4 waves' results.  A kernel of
+// its own: the partials come from workgroups on other XCDs, whose L2s are only
+// coherent with this one at kernel boundaries.
+template <int Q8, int U>
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
+    __shared__ float sm[4][66];
     const int r = blockIdx.x, hq = blockIdx.y, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
     const int d = blockIdx.z * 64 + lane;
     const int hd = a.hd, rep = a.nh / a.nk, kh = hq / rep, h = hq % rep;
     const int Q = a.nh * hd, ld = 2 * Q + 2 * a.nk * hd;
@@ -95,10 +93,6 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
     // what does not depend on the partials first
     const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * hd + hq * hd + dc];
     const float sgv = a.sg[hq * hd + dc];
-    const int64_t p = a.rec->rows[r].pos;
-    float vcol = 1.f;
-    if (Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup)))
-        vcol = (a.sd1 ? *a.sd1 : slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot)).vcol[kh * hd + dc];
     int nsplit;
     if (a.dec) {  // decode kernel: every slab of the grid, those past the row's keys hold max -inf
         nsplit = a.max_split;
@@ -108,25 +102,28 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
         const int64_t klo = pos0 + rb0 + 1 - a.window > 0 ? pos0 + rb0 + 1 - a.window : 0;
         nsplit = (int)((pos0 + rb1 - klo + a.split) / a.split);
     } else {
+        const int64_t p = a.rec->rows[r].pos;
         const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
         nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
     }
     const size_t pstride = (size_t)rep * (hd + 2);
     const float *all = a.part + ((size_t)r * a.nk + kh) * a.max_split * pstride + (size_t)h * (hd + 2);
     float M = -INFINITY, L = 0.f, acc = 0.f;
-    for (int base = wave; base < nsplit; base += nw * U) {
+    for (int base = wave; base < nsplit; base += 4 * U) {
         float m[U], l[U], v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int j = base + nw * u;
+            const int j = base + 4 * u;
             const float *pj = all + (size_t)(j < nsplit ? j : base) * pstride;
             m[u] = pj[0];
             l[u] = pj[1];
             v[u] = pj[2 + dc];
         }
 #pragma unroll
+        for (int u = 0; u < U; ++u) asm volatile("" ::"v"(m[u]), "v"(l[u]), "v"(v[u]));
+#pragma unroll
         for (int u = 0; u < U; ++u) {
-            if (base + nw * u >= nsplit) break;
+            if (base + 4 * u >= nsplit) break;
             if (m[u] == -INFINITY) continue;  // a split with no key this row sees
             const float Mn = fmaxf(M, m[u]);
             const float c0 = expf(M - Mn), c1 = expf(m[u] - Mn);
@@ -140,14 +137,22 @@ __global__ __launch_bounds__(1024) void k_attn_merge(AttnArgs a) {
         sm[wave][0] = M;
         sm[wave][1] = L;
     }
+    float vcol = 1.f;
+    if (Q8 && wave == 0) {
+        const int64_t p = a.rec->rows[r].pos;
+        if (a.field > 0 || (a.field < 0 && p >= kWarmup))
+            vcol = (a.sd1 ? *a.sd1 : slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot)).vcol[kh * hd + dc];
+    }
     __syncthreads();
     if (wave != 0 || d >= hd) return;
     float Mt = -INFINITY;
-    for (int w = 0; w < nw; ++w) Mt = fmaxf(Mt, sm[w][0]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) Mt = fmaxf(Mt, sm[w][0]);
     float Lt = 0.f, y = 0.f;
-    for (int w = 0; w < nw; ++w) {
-        if (sm[w][0] == -INFINITY) continue;  // a wave with no split
-        const float c = expf(sm[w][0] - Mt);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const float mw = sm[w][0];
+        const float c = mw == -INFINITY ? 0.f : expf(mw - Mt);  // a wave with no split adds nothing
         Lt += sm[w][1] * c;
         y += sm[w][2 + lane] * c;
     }
@@ -1119,13 +1124,23 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // one row: 16 waves per head channel block walk the splits in parallel;
+    // one row: 4 waves per head channel block walk the splits in parallel;
     // several rows: a workgroup per (row, kv head)
     const int rows = T < 0 ? -T : T;
     if (rows == 1) {
-        dim3 mgrid(1, a.nh, (HD + 63) / 64);
-        if (a.q8) hipLaunchKernelGGL((k_attn_merge<1>), mgrid, dim3(1024), 0, s, a);
-        else hipLaunchKernelGGL((k_attn_merge<0>), mgrid, dim3(1024), 0, s, a);
+        // each wave holds its splits' loads in flight at once (up to 68 splits)
+        dim3 mgrid(1, a.nh, (HD + 63) / 64), mblock(256);
+        const int per_wave = (a.max_split + 3) / 4;
+        if (per_wave <= 4) {
+            if (a.q8) hipLaunchKernelGGL((k_attn_merge<1, 4>), mgrid, mblock, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_merge<0, 4>), mgrid, mblock, 0, s, a);
+        } else if (per_wave <= 8) {
+            if (a.q8) hipLaunchKernelGGL((k_attn_merge<1, 8>), mgrid, mblock, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_merge<0, 8>), mgrid, mblock, 0, s, a);
+        } else {
+            if (a.q8) hipLaunchKernelGGL((k_attn_merge<1, 17>), mgrid, mblock, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_merge<0, 17>), mgrid, mblock, 0, s, a);
+        }
     } else {
         dim3 mgrid(rows, a.nk);
         if (a.q8) hipLaunchKernelGGL((k_attn_merge_rows<1, HD, REP>), mgrid, dim3(256), 0, s, a);
