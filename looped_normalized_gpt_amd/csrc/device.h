@@ -68,28 +68,54 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
-__device__ __forceinline__ float wave_max(float v) { return group_max<64>(v); }
 
-// Sums of two values over a 256-thread workgroup; red holds >= 8 floats.
-// Every thread gets both results.
-__device__ __forceinline__ void block_sum2(float &a, float &b, float *red) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    a = wave_sum(a);
-    b = wave_sum(b);
-    __syncthreads();  // red may still be read by a previous reduction
-    if (lane == 0) {
-        red[wave] = a;
-        red[4 + wave] = b;
-    }
-    __syncthreads();
-    a = red[0] + red[1] + red[2] + red[3];
-    b = red[4] + red[5] + red[6] + red[7];
+// The sum over the wave, complete in lane 63 only (the other lanes hold
+// partial sums): DPP row reductions, then the row broadcasts of lanes 15 and
+// 31; no LDS permutes, so it costs no LDS round trip.
+__device__ __forceinline__ float wave_sum63(float v) {
+    v = group_sum<16>(v);
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));  // row_bcast:15
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return v;
+}
+__device__ __forceinline__ float wave_max63(float v) {
+    v = group_max<16>(v);
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x142, 0xA, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), 0x143, 0xC, 0xF, false)));
+    return v;
+}
+// Every lane gets the wave's sum / maximum (lane 63's, read into a scalar).
+__device__ __forceinline__ float wave_sum(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_sum63(v)), 63));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wave_max63(v)), 63));
 }
 
-__device__ __forceinline__ float block_sum(float a, float *red) {
+// Sums of two values over a 256-thread workgroup; every thread gets both
+// results.  slot < 0: red[0..8), after a barrier (red may still be read by a
+// previous reduction).  slot 0 or 1: red[8*slot..8*slot+8) and no leading
+// barrier; the caller alternates the slots, so a reduction never overwrites
+// values another thread may still be reading.
+__device__ __forceinline__ void block_sum2(float &a, float &b, float *red, int slot = -1) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    a = wave_sum63(a);
+    b = wave_sum63(b);
+    float *r = red;
+    if (slot < 0) __syncthreads();
+    else r = red + 8 * slot;
+    if (lane == 63) {
+        r[wave] = a;
+        r[4 + wave] = b;
+    }
+    __syncthreads();
+    a = r[0] + r[1] + r[2] + r[3];
+    b = r[4] + r[5] + r[6] + r[7];
+}
+
+__device__ __forceinline__ float block_sum(float a, float *red, int slot = -1) {
     float b = 0.f;
-    block_sum2(a, b, red);
+    block_sum2(a, b, red, slot);
     return a;
 }
 
@@ -214,7 +240,7 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
             sx += h[j] * h[j];
             so += o[j] * o[j];
         }
-        block_sum2(sx, so, red);
+        block_sum2(sx, so, red, 0);
         const float rx = norm_factor(sx), ro = norm_factor(so);
         float se = 0.f;
 #pragma unroll
@@ -223,7 +249,7 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
             e[j] = xh + al[j] * (oh - xh);
             se += e[j] * e[j];
         }
-        const float re = norm_factor(block_sum(se, red));
+        const float re = norm_factor(block_sum(se, red, 1));
 #pragma unroll
         for (int j = 0; j < EPT; ++j) e[j] *= re;
     }
@@ -246,14 +272,14 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
             e[j] = e[j] + e[j];
             s += e[j] * e[j];
         }
-        const float f = norm_factor(block_sum(s, red));
+        const float f = norm_factor(block_sum(s, red, 0));
 #pragma unroll
         for (int j = 0; j < EPT; ++j) e[j] *= f;
     } else if (rs.loop_op != kLoopNone) {
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < EPT; ++j) s += e[j] * e[j];
-        const float fs = norm_factor(block_sum(s, red));
+        const float fs = norm_factor(block_sum(s, red, 0));
 #pragma unroll
         for (int j = 0; j < EPT; ++j) e[j] *= fs;
         if (rs.loop_op == kLoopNext) {
@@ -270,7 +296,7 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
                 e[j] = e[j] + in[j];
                 s2 += e[j] * e[j];
             }
-            const float f = norm_factor(block_sum(s2, red));
+            const float f = norm_factor(block_sum(s2, red, 1));
 #pragma unroll
             for (int j = 0; j < EPT; ++j) e[j] *= f;
         }

@@ -89,8 +89,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
     constexpr int EPT = 8 * MAXC;  // prologue elements per thread: K <= 2048 * MAXC
     float *xs = smem;              // [K]
-    float *red = smem + a.K;       // [8]
-    float *part = red + 8;         // [4][WR]
+    float *red = smem + a.K;       // [16]: two reduction slots
+    float *part = red + 16;        // [4][WR]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row0 = blockIdx.x * ROWS;
     const int K = a.K, N = a.N;
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
             for (int j = 0; j < EPT; ++j)
                 if (reg_index(j) < K) s += ph[j] * ph[j];
-            f = norm_factor(block_sum(s, red));
+            f = norm_factor(block_sum(s, red, 0));
         }
 #pragma unroll
         for (int jj = 0; jj < EPT / 4; ++jj) {
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < WR; ++j) {
-        float v = wave_sum(acc[j]);
-        if (lane == 0) part[wave * WR + j] = valid[j] ? v : 0.f;
+        const float v = wave_sum63(acc[j]);
+        if (lane == 63) part[wave * WR + j] = valid[j] ? v : 0.f;
     }
     __syncthreads();
     if (tid < ROWS) {
@@ -241,7 +241,7 @@ hipError_t launch_r(const GemvArgs &a, hipStream_t s) {
     const int nch = (a.K + 511) / 512;
     const int maxc = (nch + 3) / 4;
     dim3 grid((a.N + ROWS - 1) / ROWS), block(256);
-    const size_t lds = sizeof(float) * (a.K + 8 + 4 * 2 * ROWS);
+    const size_t lds = sizeof(float) * (a.K + 16 + 4 * 2 * ROWS);
     switch (maxc) {
         case 1: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 1, ROWS>), grid, block, lds, s, a); break;
         case 2: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 2, ROWS>), grid, block, lds, s, a); break;

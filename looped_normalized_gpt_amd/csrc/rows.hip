@@ -30,7 +30,7 @@ __global__ __launch_bounds__(256) void k_embed(const void *E, int V, int H, cons
 // arithmetic.
 template <int EPT>
 __global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const CallRec *rec) {
-    __shared__ float red[8];
+    __shared__ float red[16];  // resolve_regs' two reduction slots
     const int r = blockIdx.x, tid = threadIdx.x;
     const bool from_st = rs.loop_op == kLoopExit && r >= rs.n_prev;  // a batch row whose loops ended early
     const bool slerp = rs.slerp && !from_st;
