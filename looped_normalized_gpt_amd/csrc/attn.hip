@@ -121,14 +121,23 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) asm volatile("" ::"v"(m[u]), "v"(l[u]), "v"(v[u]));
+        // the group's maximum first, then independent weights; a split past
+        // the end or with no key (max -inf: its sums are stale) adds nothing
+        float Mn = M;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            if (base + 4 * u >= nsplit) break;
-            if (m[u] == -INFINITY) continue;  // a split with no key this row sees
-            const float Mn = fmaxf(M, m[u]);
-            const float c0 = expf(M - Mn), c1 = expf(m[u] - Mn);
-            L = L * c0 + l[u] * c1;
-            acc = acc * c0 + v[u] * c1;
+        for (int u = 0; u < U; ++u)
+            if (base + 4 * u < nsplit) Mn = fmaxf(Mn, m[u]);
+        if (Mn != -INFINITY) {
+            const float c0 = expf(M - Mn);
+            L *= c0;
+            acc *= c0;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const bool ok = base + 4 * u < nsplit && m[u] != -INFINITY;
+                const float c = expf((ok ? m[u] : Mn) - Mn);
+                L += ok ? l[u] * c : 0.f;
+                acc += ok ? v[u] * c : 0.f;
+            }
             M = Mn;
         }
     }
@@ -206,12 +215,29 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            if (j0 + 4 * u >= nsplit || m[u] == -INFINITY) continue;  // past the end, or no key seen
-            const float Mn = fmaxf(M, m[u]);
-            const float e0 = expf(M - Mn), e1 = expf(m[u] - Mn);
-            L = L * e0 + l[u] * e1;
+            asm volatile("" ::"v"(m[u]), "v"(l[u]));
 #pragma unroll
-            for (int i = 0; i < CPL; ++i) acc[i] = acc[i] * e0 + v[u][i] * e1;
+            for (int i = 0; i < CPL; ++i) asm volatile("" ::"v"(v[u][i]));
+        }
+        // the group's maximum first, then independent weights; a split past
+        // the end or with no key (max -inf: its sums are stale) adds nothing
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (j0 + 4 * u < nsplit) Mn = fmaxf(Mn, m[u]);
+        if (Mn != -INFINITY) {
+            const float e0 = expf(M - Mn);
+            L *= e0;
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc[i] *= e0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = j0 + 4 * u < nsplit && m[u] != -INFINITY;
+                const float e1 = expf((ok ? m[u] : Mn) - Mn);
+                L += ok ? l[u] * e1 : 0.f;
+#pragma unroll
+                for (int i = 0; i < CPL; ++i) acc[i] += ok ? v[u][i] * e1 : 0.f;
+            }
             M = Mn;
         }
     }
@@ -801,12 +827,21 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
     const size_t pstride = (size_t)REP * (HD + 2);
     float *mine = a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride;
     for (int h = wave; h < REP; h += 4) {
+        // LDS reads in batches, all issued before their first use (else the
+        // compiler keeps two in flight and waits on each pair)
         float d = 0.f;
 #pragma unroll
-        for (int c = 0; c < HD; c += 4) {
-            const float4 k = *reinterpret_cast<const float4 *>(&Ks[lane][c]);
-            const float4 q = *reinterpret_cast<const float4 *>(&qs[h][c]);
-            d += k.x * q.x + k.y * q.y + k.z * q.z + k.w * q.w;
+        for (int c0 = 0; c0 < HD; c0 += 32) {
+            float4 k[8], q[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                k[i] = *reinterpret_cast<const float4 *>(&Ks[lane][c0 + 4 * i]);
+                q[i] = *reinterpret_cast<const float4 *>(&qs[h][c0 + 4 * i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(k[i].x), "v"(k[i].w), "v"(q[i].x), "v"(q[i].w));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d += k[i].x * q[i].x + k[i].y * q[i].y + k[i].z * q[i].z + k[i].w * q[i].w;
         }
         const float sc = lane < len ? d : -INFINITY;
         const float m = wave_max(sc);
@@ -814,11 +849,20 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         const float l = wave_sum(pe);
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-        for (int e = 0; e < NK; ++e) {
-            const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), e));
-            const float2 v = *reinterpret_cast<const float2 *>(&Vs[e][2 * lane]);
-            acc0 += w * v.x;
-            acc1 += w * v.y;
+        for (int e0 = 0; e0 < NK; e0 += 16) {
+            float2 v[16];
+            float w[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const float2 *>(&Vs[e0 + i][2 * lane]);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) w[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), e0 + i));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y));
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc0 += w[i] * v[i].x;
+                acc1 += w[i] * v[i].y;
+            }
         }
         float *dst = mine + (size_t)h * (HD + 2);
         *reinterpret_cast<float2 *>(dst + 2 + 2 * lane) = make_float2(acc0, acc1);
