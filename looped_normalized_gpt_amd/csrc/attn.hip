@@ -128,13 +128,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
         for (int u = 0; u < U; ++u)
             if (base + 4 * u < nsplit) Mn = fmaxf(Mn, m[u]);
         if (Mn != -INFINITY) {
-            const float c0 = expf(M - Mn);
+            const float c0 = fexp(M - Mn);
             L *= c0;
             acc *= c0;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool ok = base + 4 * u < nsplit && m[u] != -INFINITY;
-                const float c = expf((ok ? m[u] : Mn) - Mn);
+                const float c = fexp((ok ? m[u] : Mn) - Mn);
                 L += ok ? l[u] * c : 0.f;
                 acc += ok ? v[u] * c : 0.f;
             }
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
         const float mw = sm[w][0];
-        const float c = mw == -INFINITY ? 0.f : expf(mw - Mt);  // a wave with no split adds nothing
+        const float c = mw == -INFINITY ? 0.f : fexp(mw - Mt);  // a wave with no split adds nothing
         Lt += sm[w][1] * c;
         y += sm[w][2 + lane] * c;
     }
@@ -226,14 +226,14 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
         for (int u = 0; u < 4; ++u)
             if (j0 + 4 * u < nsplit) Mn = fmaxf(Mn, m[u]);
         if (Mn != -INFINITY) {
-            const float e0 = expf(M - Mn);
+            const float e0 = fexp(M - Mn);
             L *= e0;
 #pragma unroll
             for (int i = 0; i < CPL; ++i) acc[i] *= e0;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const bool ok = j0 + 4 * u < nsplit && m[u] != -INFINITY;
-                const float e1 = expf((ok ? m[u] : Mn) - Mn);
+                const float e1 = fexp((ok ? m[u] : Mn) - Mn);
                 L += ok ? l[u] * e1 : 0.f;
 #pragma unroll
                 for (int i = 0; i < CPL; ++i) acc[i] += ok ? v[u][i] * e1 : 0.f;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             if (wm[w][ln] == -INFINITY) continue;  // a wave with no split
-            const float e = expf(wm[w][ln] - Mt);
+            const float e = fexp(wm[w][ln] - Mt);
             Lt += wl[w][ln] * e;
             y += wacc[w][c] * e;
         }
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
         m = wave_max(m);
         float l = 0.f;
         for (int e = lane; e < len; e += 64) {
-            const float pv = expf(sc[h][e] - m);
+            const float pv = fexp(sc[h][e] - m);
             sc[h][e] = pv;
             l += pv;
         }
@@ -845,7 +845,7 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         }
         const float sc = lane < len ? d : -INFINITY;
         const float m = wave_max(sc);
-        const float pe = expf(sc - m);  // 0 past len
+        const float pe = fexp(sc - m);  // 0 past len
         const float l = wave_sum(pe);
         float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll

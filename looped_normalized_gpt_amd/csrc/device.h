@@ -29,6 +29,11 @@ __device__ __forceinline__ float4 gld_codes4(const int8_t *p) {  // 4 int8 codes
                        (float)(int8_t)((u >> 24) & 0xff));
 }
 
+// e^x on the hardware exp2 (about 1 ulp of exp2, plus the rounding of
+// x*log2(e)): for softmax weights, where the libm expf's range reduction costs
+// a long dependent chain.  e^-inf = 0.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
 // fp32 -> bf16 bits, round to nearest even
 __device__ __forceinline__ uint16_t f2bf(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
