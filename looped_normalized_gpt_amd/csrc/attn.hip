@@ -897,7 +897,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // so the softmax rescale is one multiplier per lane.  Each workgroup writes
 // (max, sum, unnormalised sum of p*v) per (row, head) for k_attn_merge.
 template <int HD, int REP, int Q8>
-__global__ __launch_bounds__(256) void k_fattn(AttnArgs a) {
+__global__ __launch_bounds__(256, Q8 ? 1 : 2) void k_fattn(AttnArgs a) {
     static_assert(HD == 128, "the loaders assume 32 lanes per 128-channel row");
     constexpr int BQ = 128 / REP;        // rows per workgroup
     constexpr int KT = 64;               // keys per tile
