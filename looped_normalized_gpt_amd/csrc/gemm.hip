@@ -366,23 +366,42 @@ __global__ __launch_bounds__(512) void k_gemm_dma(const uint16_t *__restrict__ A
         __builtin_amdgcn_s_barrier();
         const uint32_t As = lds_addr(lds[ks % STAGES][0]), Bs = lds_addr(lds[ks % STAGES][1]);
         const int ra0 = wm * 64 + (lane & 31), ra1 = ra0 + 32, rb = wn * 32 + (lane & 31);
+        // the step's 12 operand fragments in one batch and one wait, then its
+        // 8 MFMAs back to back.  LDS reads in asm: the compiler cannot tell them
+        // from the DMA's destinations and would otherwise wait for every load
+        // in flight.  Early-clobber outputs: no output shares a register with
+        // an address still to be read.
+        bf16x8 a0[4], a1[4], b[4];
+        uint32_t ad0[4], ad1[4], bd[4];
 #pragma unroll
-        for (int kk = 0; kk < BK; kk += 16) {
-            const int ch = (kk >> 3) + (lane >> 5);   // the global 16-byte chunk this lane supplies
-            bf16x8 a0, a1, b;
-            // LDS reads in asm: the compiler cannot tell them from the DMA's
-            // destinations and would otherwise wait for every load in flight
-            asm volatile(
-                "ds_read_b128 %0, %3\n\t"
-                "ds_read_b128 %1, %4\n\t"
-                "ds_read_b128 %2, %5\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=v"(a0), "=v"(a1), "=v"(b)
-                : "v"(As + 2 * (ra0 * BK + 8 * (ch ^ ((ra0 >> 1) & 7)))),
-                  "v"(As + 2 * (ra1 * BK + 8 * (ch ^ ((ra1 >> 1) & 7)))),
-                  "v"(Bs + 2 * (rb * BK + 8 * (ch ^ ((rb >> 1) & 7)))));
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+        for (int q = 0; q < 4; ++q) {
+            const int ch = 2 * q + (lane >> 5);   // the global 16-byte chunk this lane supplies
+            ad0[q] = As + 2 * (ra0 * BK + 8 * (ch ^ ((ra0 >> 1) & 7)));
+            ad1[q] = As + 2 * (ra1 * BK + 8 * (ch ^ ((ra1 >> 1) & 7)));
+            bd[q] = Bs + 2 * (rb * BK + 8 * (ch ^ ((rb >> 1) & 7)));
+        }
+        asm volatile(
+            "ds_read_b128 %0, %12\n\t"
+            "ds_read_b128 %1, %13\n\t"
+            "ds_read_b128 %2, %14\n\t"
+            "ds_read_b128 %3, %15\n\t"
+            "ds_read_b128 %4, %16\n\t"
+            "ds_read_b128 %5, %17\n\t"
+            "ds_read_b128 %6, %18\n\t"
+            "ds_read_b128 %7, %19\n\t"
+            "ds_read_b128 %8, %20\n\t"
+            "ds_read_b128 %9, %21\n\t"
+            "ds_read_b128 %10, %22\n\t"
+            "ds_read_b128 %11, %23\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0[0]), "=&v"(a1[0]), "=&v"(b[0]), "=&v"(a0[1]), "=&v"(a1[1]), "=&v"(b[1]),
+              "=&v"(a0[2]), "=&v"(a1[2]), "=&v"(b[2]), "=&v"(a0[3]), "=&v"(a1[3]), "=&v"(b[3])
+            : "v"(ad0[0]), "v"(ad1[0]), "v"(bd[0]), "v"(ad0[1]), "v"(ad1[1]), "v"(bd[1]),
+              "v"(ad0[2]), "v"(ad1[2]), "v"(bd[2]), "v"(ad0[3]), "v"(ad1[3]), "v"(bd[3]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[q], b[q], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[q], b[q], acc[1], 0, 0, 0);
         }
         // every wave's reads of this buffer are done (lgkmcnt 0 above) before
         // the next iteration's loads refill it
