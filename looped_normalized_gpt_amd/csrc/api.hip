@@ -60,6 +60,7 @@ struct dory {
     int64_t o_stride = 0;   // elements between the split-K slabs of o
     uint16_t *xb = nullptr, *znb = nullptr, *unb = nullptr;  // bf16 copies of x, zn, un (GEMM operands)
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
+    float *zss = nullptr;  // multi-row attention: sums of squares of z per (row, kv head)
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
@@ -221,6 +222,8 @@ struct Enq {
     std::vector<int> seq;        // every row's sequence
     std::vector<uint8_t> froze;  // slots whose field this call froze: [max_seqs][n_ord][kMaxLoops]
     int o_parts = 1;             // split-K slabs of o the last output projection wrote
+    const float *o_ss = nullptr; // multi-row attention: per-row partial sums of |z|^2 scaling o
+    int o_ss_n = 0;
 };
 
 #define LAUNCH(call)                                            \
@@ -293,6 +296,10 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
     aa.window = l.sliding ? h->win_s : h->win_f;
     aa.q8 = h->q8; aa.rec = h->rec;
     aa.rope = l.sliding ? h->rope_s : h->rope_f; aa.sq = w.sq;
+    if (q.T > 1) {
+        aa.zb = h->znb;
+        aa.zss = h->zss;
+    }
     if (q.T == 1 || q.batch) {
         // One new row per sequence: prep and the cache write are fused into the
         // decode attention kernel.  kv_cache.rs `append`: a slot's field freezes
@@ -361,11 +368,14 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         a.src = h->z; a.y = h->o; a.rec = h->rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_rownorm(h->z, h->Q, h->zn, h->znb, h->Q, M, q.s));
+        // the projection runs on z as the merge left it (fp32 and bf16); the
+        // renorm before it is a per-row factor the next residual step applies
         const int S = gemm_pick_splits(h->wt, true, M, h->H, h->Q);
-        LAUNCH(launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s, S,
+        LAUNCH(launch_gemm(h->wt, h->z, h->znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s, S,
                            h->o_stride));
         q.o_parts = S;
+        q.o_ss = h->zss;
+        q.o_ss_n = h->nk;
     }
     return DORY_OK;
 }
@@ -390,6 +400,8 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
         LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s, S,
                            h->o_stride));
         q.o_parts = S;
+        q.o_ss = nullptr;
+        q.o_ss_n = 0;
     }
     return DORY_OK;
 }
@@ -430,6 +442,8 @@ int enqueue(Enq &q) {
         rs.loop_op = op;
         rs.o_parts = q.o_parts;
         rs.o_stride = h->o_stride;
+        rs.o_ss = q.o_ss;
+        rs.o_ss_n = q.o_ss_n;
         rs.st = q.batch ? h->st : nullptr;
         rs.n_next = M;
         if (k == 0) {
@@ -453,6 +467,8 @@ int enqueue(Enq &q) {
     Resolve rf{};
     rf.o_parts = q.o_parts;
     rf.o_stride = h->o_stride;
+    rf.o_ss = q.o_ss;
+    rf.o_ss_n = q.o_ss_n;
     rf.h = h->hb[(P - 1) % 2]; rf.o = h->o; rf.alpha = h->L[prev_li].w.alpha; rf.slerp = 1;
     rf.loop_op = kLoopNone; rf.inp = h->inp; rf.tap_pass = P - 1; rf.n_prev = rf.n_next = T;
     GemvArgs a{};
@@ -616,6 +632,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->un, (size_t)chunk * h->F));
     CREATE_CHECK(dmalloc(h, &h->xb, (size_t)chunk * h->H));
     CREATE_CHECK(dmalloc(h, &h->znb, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->zss, (size_t)chunk * h->nk));
     CREATE_CHECK(dmalloc(h, &h->unb, (size_t)chunk * h->F));
     CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
     constexpr int CH = REP * HD, CPL = CH >= 64 ? CH / 64 : 1;
     static_assert(CH % 64 == 0 || CH < 64, "channels split evenly over the lanes");
     static_assert(HD % CPL == 0, "a lane's channels lie in one head");
-    __shared__ float wm[4][64], wl[4][64], wacc[4][CH];
+    __shared__ float wm[4][64], wl[4][64], wacc[4][CH], red[8];
     const int r = blockIdx.x, kh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Q = a.nh * HD, ld = 2 * Q + 2 * a.nk * HD;
@@ -248,6 +248,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
         for (int i = 0; i < CPL; ++i) wacc[wave][c0 + i] = acc[i];
     __syncthreads();
     const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    float ss = 0.f;
     for (int c = tid; c < CH; c += 256) {
         const int ln = c / CPL, hh = c / HD, d = c % HD, hq = kh * REP + hh;
         float Mt = -INFINITY;
@@ -264,7 +265,14 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
         const float vcol = field ? slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * HD + d] : 1.f;
         const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * HD + hq * HD + d];
         y = y / Lt * vcol;
-        a.z[(size_t)r * Q + hq * HD + d] = y / (1.0f + expf(-(gate * a.sg[hq * HD + d])));
+        const float zv = y / (1.0f + expf(-(gate * a.sg[hq * HD + d])));
+        a.z[(size_t)r * Q + hq * HD + d] = zv;
+        if (a.zb) a.zb[(size_t)r * Q + hq * HD + d] = f2bf(zv);
+        ss += zv * zv;
+    }
+    if (a.zss) {
+        ss = block_sum(ss, red);
+        if (tid == 0) a.zss[(size_t)r * a.nk + kh] = ss;
     }
 }
 
@@ -1171,7 +1179,7 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
     // one row: 4 waves per head channel block walk the splits in parallel;
     // several rows: a workgroup per (row, kv head)
     const int rows = T < 0 ? -T : T;
-    if (rows == 1) {
+    if (rows == 1 && !a.zss) {  // (a row of a multi-row call needs zb and zss: the merge below)
         // each wave holds its splits' loads in flight at once (up to 68 splits)
         dim3 mgrid(1, a.nh, (HD + 63) / 64), mblock(256);
         const int per_wave = (a.max_split + 3) / 4;

@@ -71,6 +71,11 @@ struct Resolve {
     uint16_t *hb_out;    // the same rows rounded to bf16 (the GEMMs' operand), or null
     int32_t o_parts;     // multi-row calls: o is the sum of o_parts slabs o + s * o_stride
     int64_t o_stride;
+    // multi-row calls after an attention sub-layer: its output projection ran
+    // on the un-normalised gated output z, so row r of o is scaled by
+    // justnorm's factor of |z_r|^2 = the sum of o_ss[r*o_ss_n .. +o_ss_n); null: none
+    const float *o_ss;
+    int32_t o_ss_n;
     float *inp;          // the loop's input [T][H]
     float *st;           // the loop state of every row [T][H] (batches), or null
     int32_t slerp;       // 1: e = slerp(h, o, alpha); 0: e = h
@@ -180,6 +185,10 @@ struct AttnArgs {
     // 64; 0: one row per workgroup (k_attn), split <= 256
     int32_t blk;
     int32_t nsplit;      // k_fattn: grid.x, the most splits a block has
+    // multi-row merges: z also rounded to bf16 [T][Q], and the sum of squares
+    // of z over each (row, kv head) group of channels [T][nk]; null: not written
+    uint16_t *zb;
+    float *zss;
     // one-row calls: the row's slot table entry, read without waiting for the
     // record's sequence; null: looked up by the record
     const SlotDesc *sd1;

@@ -35,6 +35,14 @@ __global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const C
     const bool from_st = rs.loop_op == kLoopExit && r >= rs.n_prev;  // a batch row whose loops ended early
     const bool slerp = rs.slerp && !from_st;
     const float *hs = (from_st ? rs.st : rs.h) + (size_t)r * H;
+    // the renorm of the attention output before its projection, applied here
+    // (the projection is linear): o times justnorm's factor of |z|^2
+    float oc = 1.f;
+    if (slerp && rs.o_ss) {
+        float t = 0.f;
+        for (int k = 0; k < rs.o_ss_n; ++k) t += rs.o_ss[(size_t)r * rs.o_ss_n + k];
+        oc = norm_factor(t);
+    }
     float h[EPT], o[EPT], al[EPT], in[EPT];
 #pragma unroll
     for (int jj = 0; jj < EPT / 4; ++jj) {
@@ -52,7 +60,8 @@ __global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const C
         if (rs.loop_op == kLoopNext) vi = *reinterpret_cast<const float4 *>(rs.inp + (size_t)r * H + ic);
         const bool ok = i < H;
         h[4 * jj] = ok ? vh.x : 0.f; h[4 * jj + 1] = ok ? vh.y : 0.f; h[4 * jj + 2] = ok ? vh.z : 0.f; h[4 * jj + 3] = ok ? vh.w : 0.f;
-        o[4 * jj] = ok ? vo.x : 0.f; o[4 * jj + 1] = ok ? vo.y : 0.f; o[4 * jj + 2] = ok ? vo.z : 0.f; o[4 * jj + 3] = ok ? vo.w : 0.f;
+        o[4 * jj] = ok ? vo.x * oc : 0.f; o[4 * jj + 1] = ok ? vo.y * oc : 0.f;
+        o[4 * jj + 2] = ok ? vo.z * oc : 0.f; o[4 * jj + 3] = ok ? vo.w * oc : 0.f;
         al[4 * jj] = va.x; al[4 * jj + 1] = va.y; al[4 * jj + 2] = va.z; al[4 * jj + 3] = va.w;
         in[4 * jj] = ok ? vi.x : 0.f; in[4 * jj + 1] = ok ? vi.y : 0.f; in[4 * jj + 2] = ok ? vi.z : 0.f; in[4 * jj + 3] = ok ? vi.w : 0.f;
     }
