@@ -61,6 +61,7 @@ struct dory {
     uint16_t *xb = nullptr, *znb = nullptr, *unb = nullptr;  // bf16 copies of x, zn, un (GEMM operands)
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     float *zss = nullptr;  // multi-row attention: sums of squares of z per (row, kv head)
+    float *uss = nullptr;  // multi-row MLP: sums of squares of the SwiGLU rows
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
@@ -395,13 +396,16 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
     } else {
         LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
-        LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, h->un, h->unb, h->F, M, q.s));
+        // the renorm before the down projection becomes a per-row factor the
+        // next residual step applies (the projection is linear)
+        float *un = gemm_reads_fp32_a(h->wt, true, M, h->F, h->F) ? h->un : nullptr;
+        LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, un, h->unb, h->F, M, q.s, h->uss));
         const int S = gemm_pick_splits(h->wt, true, M, h->H, h->F);
         LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s, S,
                            h->o_stride));
         q.o_parts = S;
-        q.o_ss = nullptr;
-        q.o_ss_n = 0;
+        q.o_ss = h->uss;
+        q.o_ss_n = 1;
     }
     return DORY_OK;
 }
@@ -633,6 +637,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->xb, (size_t)chunk * h->H));
     CREATE_CHECK(dmalloc(h, &h->znb, (size_t)chunk * h->Q));
     CREATE_CHECK(dmalloc(h, &h->zss, (size_t)chunk * h->nk));
+    CREATE_CHECK(dmalloc(h, &h->uss, (size_t)chunk));
     CREATE_CHECK(dmalloc(h, &h->unb, (size_t)chunk * h->F));
     CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));

@@ -528,6 +528,11 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict_
 
 }  // namespace
 
+bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda) {
+    if (wtype != kBF16 || !have_bf16 || lda % 8) return true;
+    return !((M <= 64 && K % 128 == 0) || (M > 64 && K % 64 == 0) || (M >= 32 && K % 8 == 0));
+}
+
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &Wb, int N, int K,
                        float *C, int ldc, int M, hipStream_t s, int kparts, size_t pstride) {
     if (kparts < 1 || (kparts > 1 && !gemm_splits_ok(wtype, Ab != nullptr, M, K, kparts))) return hipErrorInvalidValue;

@@ -118,9 +118,11 @@ hipError_t launch_embed(int wtype, const void *embed, int V, int H, const CallRe
                         float *h, uint16_t *hb, hipStream_t s);
 hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s);
 hipError_t launch_rownorm(const float *src, int ld_src, float *dst, uint16_t *dstb, int N, int T, hipStream_t s);
-// a and b rows have stride ld; dst rows stride F.
+// a and b rows have stride ld; dst rows stride F.  dst or dstb may be null.
+// With ss: the un-normalised rows are stored and ss[r] = their |z|^2 (the
+// renorm is then a per-row factor its consumer applies).
 hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su,
-                              float *dst, uint16_t *dstb, int F, int T, hipStream_t s);
+                              float *dst, uint16_t *dstb, int F, int T, hipStream_t s, float *ss = nullptr);
 
 // Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
 hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,
@@ -143,6 +145,8 @@ inline GemmW gemm_w(const void *w, int N) { return GemmW{{w, w, w, w}, {N, N, N,
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &W, int N, int K,
                        float *C, int ldc, int T, hipStream_t s, int kparts = 1, size_t pstride = 0);
 bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts);
+// Whether launch_gemm reads the fp32 A for this shape (else only the bf16 Ab).
+bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda);
 // Split-K count that fills the chip with 128 x 128 tiles (1 where it does not apply).
 int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K);
 

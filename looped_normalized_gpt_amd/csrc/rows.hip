@@ -99,9 +99,11 @@ __global__ __launch_bounds__(256) void k_rownorm(const float *src, int ld, float
     }
 }
 
-// dory.rs `mlp_layer`: z = silu(a*sg) * (b*su), then justnorm over F.
+// dory.rs `mlp_layer`: z = silu(a*sg) * (b*su), then justnorm over F.  With
+// ss: z itself is stored and ss[row] = |z|^2 (the consumer of the projection
+// applies the renorm's factor).  dst (fp32) or dstb (bf16) may be null.
 __global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float *b, int ld, const float *sg,
-                                                     const float *su, float *dst, uint16_t *dstb, int F) {
+                                                     const float *su, float *dst, uint16_t *dstb, int F, float *ss) {
     extern __shared__ float smem[];
     float *red = smem, *z = smem + 8;
     const size_t off = (size_t)blockIdx.x * F, offi = (size_t)blockIdx.x * ld;
@@ -112,10 +114,12 @@ __global__ __launch_bounds__(256) void k_swiglu_norm(const float *a, const float
         z[i] = v;
         s += v * v;
     }
-    const float f = norm_factor(block_sum(s, red));
+    s = block_sum(s, red);
+    const float f = ss ? 1.f : norm_factor(s);
+    if (ss && threadIdx.x == 0) ss[blockIdx.x] = s;
     for (int i = threadIdx.x; i < F; i += 256) {
         const float v = z[i] * f;
-        dst[off + i] = v;
+        if (dst) dst[off + i] = v;
         if (dstb) dstb[off + i] = f2bf(v);
     }
 }
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(256) void k_rownorm_v(const float *src, int ld, flo
 
 template <int G>
 __global__ __launch_bounds__(256) void k_swiglu_norm_v(const float *a, const float *b, int ld, const float *sg,
-                                                       const float *su, float *dst, uint16_t *dstb, int F) {
+                                                       const float *su, float *dst, uint16_t *dstb, int F, float *ss) {
     __shared__ float red[8];
     const size_t offi = (size_t)blockIdx.x * ld, off = (size_t)blockIdx.x * F;
     float4 z[G];
@@ -171,17 +175,24 @@ __global__ __launch_bounds__(256) void k_swiglu_norm_v(const float *a, const flo
         z[j] = make_float4(zz[0], zz[1], zz[2], zz[3]);
         s += zz[0] * zz[0] + zz[1] * zz[1] + zz[2] * zz[2] + zz[3] * zz[3];
     }
-    const float f = norm_factor(block_sum(s, red));
+    // with ss the stores need not wait for the row's sum
+    float f = 1.f;
+    if (!ss) f = norm_factor(block_sum(s, red));
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const int i = 4 * (threadIdx.x + 256 * j);
         if (i >= F) continue;
         const float4 y = make_float4(z[j].x * f, z[j].y * f, z[j].z * f, z[j].w * f);
-        *reinterpret_cast<float4 *>(dst + off + i) = y;
+        if (dst) *reinterpret_cast<float4 *>(dst + off + i) = y;
         if (dstb) {
-            uint16_t *q = dstb + off + i;
-            q[0] = f2bf(y.x); q[1] = f2bf(y.y); q[2] = f2bf(y.z); q[3] = f2bf(y.w);
+            const uint32_t lo = (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16);
+            const uint32_t hi = (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16);
+            *reinterpret_cast<uint2 *>(dstb + off + i) = make_uint2(lo, hi);
         }
+    }
+    if (ss) {
+        s = block_sum(s, red);
+        if (threadIdx.x == 0) ss[blockIdx.x] = s;
     }
 }
 
@@ -237,13 +248,14 @@ hipError_t launch_rownorm(const float *src, int ld, float *dst, uint16_t *dstb, 
 }
 
 hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su, float *dst,
-                              uint16_t *dstb, int F, int T, hipStream_t s) {
+                              uint16_t *dstb, int F, int T, hipStream_t s, float *ss) {
     const int G = (F / 4 + 255) / 256;
     if (F % 4 == 0 && ld % 4 == 0 && G <= 8) {
-        DK_G_SWITCH(G, k_swiglu_norm_v, dim3(T), dim3(256), 0, s, a, b, ld, sg, su, dst, dstb, F)
+        DK_G_SWITCH(G, k_swiglu_norm_v, dim3(T), dim3(256), 0, s, a, b, ld, sg, su, dst, dstb, F, ss)
         return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_swiglu_norm, dim3(T), dim3(256), sizeof(float) * (F + 8), s, a, b, ld, sg, su, dst, dstb, F);
+    hipLaunchKernelGGL(k_swiglu_norm, dim3(T), dim3(256), sizeof(float) * (F + 8), s, a, b, ld, sg, su, dst, dstb, F,
+                       ss);
     return hipGetLastError();
 }
 
