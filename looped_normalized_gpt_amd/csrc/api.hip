@@ -576,9 +576,10 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
                    : cfg->max_ctx;
     const int64_t wmax = std::min<int64_t>(std::max<int64_t>(h->win_s, std::min<int64_t>(h->win_f, cfg->max_ctx)),
                                            cfg->max_ctx);
-    // Decode splits.  One-row calls: about 64 workgroups per kv head at the
-    // longest window, 8 load steps each (the latency of one short workgroup
-    // sets the pace).  Batches: about 32 per kv head with 16 load steps (the
+    // Decode splits.  One-row calls: full layers about 64 workgroups per kv
+    // head at the longest window, 8 load steps each (the latency of one short
+    // workgroup sets the pace); sliding layers about 16 (64 keys each, the
+    // one-row kernel's full width: fewer splits to merge).  Batches: about 32 per kv head with 16 load steps (the
     // grid is large anyway, and fewer splits mean less to merge).  Each takes a
     // multiple of the keys a workgroup covers per step.
     const int kb = 256 / (h->hd / 4);
@@ -589,7 +590,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
         return std::min(sp, dmax);
     };
     const int64_t wf = std::min<int64_t>(h->win_f, cfg->max_ctx), ws = std::min<int64_t>(h->win_s, cfg->max_ctx);
-    h->split_ds = pick(ws, 8, 64, 1);
+    h->split_ds = pick(ws, 8, 16, 1);
     h->split_df = pick(wf, 8, 64, 1);
     h->split_bs = pick(ws, 16, 32, 64);
     h->split_bf = pick(wf, 16, 32, 64);
