@@ -403,6 +403,19 @@ int ora_reset(ora_model *m, int32_t seq) {
     return ORA_OK;
 }
 
+/* [dory] `DoryState::rollback`: every slot forgets its rows from position n on
+ * and the position becomes min(pos, n).  [kv] `truncate_last` drops rows only:
+ * a frozen q8 field stays frozen (it froze once per conversation), and an
+ * unfrozen one freezes at the next append with 64 or more rows stored. */
+int ora_rollback(ora_model *m, int32_t seq, int64_t n) {
+    if (!m || seq < 0 || seq >= m->c.max_seqs || n < 0) return ORA_EINVAL;
+    seq_t *q = &m->seqs[seq];
+    for (int i = 0; i < m->n_ord * ORA_MAX_LOOPS; i++)
+        if (q->slots[i].rows > n) q->slots[i].rows = n;
+    if (q->pos > n) q->pos = n;
+    return ORA_OK;
+}
+
 int64_t ora_pos(const ora_model *m, int32_t seq) { return m->seqs[seq].pos; }
 
 int ora_passes(const ora_model *m, int32_t loops) {

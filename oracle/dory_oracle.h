@@ -62,6 +62,8 @@ void ora_destroy(ora_model *m);
 int  ora_forward(ora_model *m, int32_t seq, const int32_t *tokens, int32_t n,
                  int32_t loops, int32_t kv_mode, float *logits, float *tap);
 int  ora_reset(ora_model *m, int32_t seq);
+/* Forget the rows from position n on (dory.rs `DoryState::rollback`). */
+int  ora_rollback(ora_model *m, int32_t seq, int64_t n);
 int64_t ora_pos(const ora_model *m, int32_t seq);
 int  ora_passes(const ora_model *m, int32_t loops);
 /* Rows stored in a slot (attention ordinal, slot). */

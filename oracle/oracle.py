@@ -61,6 +61,7 @@ def lib():
         L.ora_forward.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
                                   C.c_int32, C.c_void_p, C.c_void_p]
         L.ora_reset.argtypes = [C.c_void_p, C.c_int32]
+        L.ora_rollback.argtypes = [C.c_void_p, C.c_int32, C.c_int64]
         L.ora_pos.argtypes = [C.c_void_p, C.c_int32]
         L.ora_pos.restype = C.c_int64
         L.ora_passes.argtypes = [C.c_void_p, C.c_int32]
@@ -173,6 +174,10 @@ class Oracle:
 
     def reset(self, seq: int = -1):
         _check(lib().ora_reset(self.h, seq))
+
+    def rollback(self, n: int, seq: int = 0):
+        """Forget the rows from position n on (dory.rs `DoryState::rollback`)."""
+        _check(lib().ora_rollback(self.h, seq, n))
 
     def pos(self, seq: int = 0) -> int:
         return lib().ora_pos(self.h, seq)

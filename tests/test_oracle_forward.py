@@ -212,3 +212,82 @@ def test_attention_output_is_renormed_before_o(pages):
     lg, tap = o.forward(ids, 2, "per_loop", tap=True)
     rl, rt = ref.forward(ids, 2, "per_loop")
     assert np.allclose(tap, rt, atol=2e-5) and np.allclose(lg, rl, atol=1e-4)
+
+
+def test_rollback_keeps_the_prefix_a_new_turn_extends_pages_case(pages):
+    """dory.rs test `rollback_keeps_the_prefix_a_new_turn_extends`: 9 tokens in
+    one call, back to position 5, the rest from there: the logits of one token
+    per call over all 12."""
+    g = golden("pages_fixture.json")["rollback"]
+    cfg, w = pages
+    cfg = dict(cfg, window=g["window"])
+    ids = np.array([i * 3 % 11 for i in range(12)], np.int32)
+    want = _run(cfg, w, ids, g["reference_chunk"], g["loops"], g["kv"])[0]
+    o = O.Oracle(cfg, w, max_ctx=64)
+    o.forward(ids[:g["first_call"]], g["loops"], g["kv"])
+    o.rollback(g["rollback_to"])
+    assert o.pos() == g["rollback_to"]
+    got, _ = o.forward(ids[g["rollback_to"]:], g["loops"], g["kv"])
+    assert np.abs(got - want).max() < g["abs_tol"]
+
+
+def test_rollback_equals_a_run_that_never_went_there(tiny):
+    """Back to position 80 after 100 rows (q8_2f, last_loop, past the freeze),
+    then other tokens: bit for bit the run that took the same calls up to 80
+    and the new tokens next (the field froze from the same 64 rows)."""
+    cfg, w = tiny
+    ids = synth.make_tokens(100, cfg["vocab"])
+    new = synth.make_tokens(12, cfg["vocab"], seq=3)
+    a = O.Oracle(cfg, w, max_ctx=256, kv_q8=True)
+    for s, e in ((0, 40), (40, 80), (80, 100)):
+        a.forward(ids[s:e], 2, "last_loop", logits=False)
+    a.rollback(80)
+    assert a.pos() == 80 and all(a.slot_rows(od, 0) == 80 for od in range(a.n_ord))
+    ga, _ = a.forward(new, 2, "last_loop")
+    b = O.Oracle(cfg, w, max_ctx=256, kv_q8=True)
+    for s, e in ((0, 40), (40, 80)):
+        b.forward(ids[s:e], 2, "last_loop", logits=False)
+    gb, _ = b.forward(new, 2, "last_loop")
+    assert np.array_equal(ga, gb)
+    for od in range(a.n_ord):
+        for p in (79, 85, 91):
+            for x, y in zip(a.kv_read(od, 0, p), b.kv_read(od, 0, p)):
+                assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+
+
+def test_rollback_below_the_freeze_keeps_the_field(tiny):
+    """kv_cache.rs `truncate_last` drops rows only and `append` freezes only
+    while the field is empty: back to position 30 after the freeze, the field
+    stays as it was, and the rows appended again past position 64 do not
+    freeze it a second time."""
+    cfg, w = tiny
+    ids = synth.make_tokens(100, cfg["vocab"])
+    o = O.Oracle(cfg, w, max_ctx=256, kv_q8=True)
+    o.forward(ids[:50], 1, "last_loop", logits=False)
+    o.forward(ids[50:100], 1, "last_loop", logits=False)
+    before = [o.kv_field(od) for od in range(o.n_ord)]
+    assert all(f[0] for f in before)
+    o.rollback(30)
+    assert o.pos() == 30 and o.slot_rows(0, 0) == 30
+    new = synth.make_tokens(70, cfg["vocab"], seq=4)
+    o.forward(new[:40], 1, "last_loop", logits=False)
+    o.forward(new[40:], 1, "last_loop", logits=False)
+    for od in range(o.n_ord):
+        fr, kcol, vcol = o.kv_field(od)
+        assert fr
+        assert np.array_equal(kcol.view(np.uint32), before[od][1].view(np.uint32))
+        assert np.array_equal(vcol.view(np.uint32), before[od][2].view(np.uint32))
+
+
+def test_rollback_bounds(tiny):
+    cfg, w = tiny
+    o = O.Oracle(cfg, w, max_ctx=64)
+    ids = synth.make_tokens(8, cfg["vocab"])
+    o.forward(ids, 2, "per_loop")
+    o.rollback(20)               # past the position: nothing to forget
+    assert o.pos() == 8 and o.slot_rows(1, 1) == 8   # the recurrent layer's second loop slot
+    with pytest.raises(Exception):
+        o.rollback(-1)
+    o.rollback(3)
+    assert o.pos() == 3 and o.slot_rows(0, 0) == 3 and o.slot_rows(1, 1) == 3
+    assert o.forward_rc(ids, 3, "per_loop") == -2    # the per_loop loop count stays fixed

@@ -39,6 +39,9 @@ MUTANTS = {
     "one_slot_per_loop": ("int si = (sq->mode == ORA_PER_LOOP && rec) ? loop_i : 0;", "int si = 0;"),
     "v_unscaled": ("acc += s[e] * (double)vs[row] * (double)vc[row * hd + i];", "acc += s[e] * (double)vc[row * hd + i];"),
     "k_group_scale_index": ("d += dg * (double)ks[row * ngk + g];", "d += dg * (double)ks[row * ngk];"),
+    "rollback_keeps_rows": ("if (q->slots[i].rows > n) q->slots[i].rows = n;", ";"),
+    "rollback_unfreezes": ("if (q->slots[i].rows > n) q->slots[i].rows = n;",
+                           "if (q->slots[i].rows > n) { q->slots[i].rows = n; q->slots[i].frozen = 0; }"),
 }
 # Not planted: `state = justnorm(h)` after a loop acts on a vector a slerp has just
 # normalised, so dropping it changes results only at the 1e-7 level of eps.
