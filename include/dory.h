@@ -137,6 +137,18 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
  * kv mode and loop count free again, q8 fields unfrozen.  seq == -1: all. */
 int dory_kv_reset(dory_t *h, int32_t seq);
 
+/* Forget the rows of a sequence from position n on (dory.rs
+ * `DoryState::rollback`, e.g. a chat turn that rewrites the last answer): its
+ * next call starts at position min(pos, n); kv mode, per_loop loop count and
+ * frozen q8_2f fields stay as they are (kv_cache.rs `truncate_last` drops rows
+ * only).  The windowed rings keep cap - W + 1 >= max_chunk rows of slack, so a
+ * rollback may go back that far on them (the pages' Metal rings keep 448 rows,
+ * dory.rs `REWIND`); deeper, DORY_ERANGE and nothing changes.  DORY_EINVAL for a
+ * bad seq or n < 0.  Host bookkeeping only: it enqueues nothing, and the rows
+ * past n are overwritten by the next call before any row reads them.  Must
+ * not run while a call on the sequence is still being enqueued. */
+int dory_rollback(dory_t *h, int32_t seq, int64_t n);
+
 /* Next position of a sequence (rows held), or a negative status. */
 int64_t dory_position(const dory_t *h, int32_t seq);
 

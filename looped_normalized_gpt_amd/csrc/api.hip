@@ -32,6 +32,11 @@ struct SeqState {
     int64_t pos = 0;
     int mode = -1;   // fixed from the first call until a reset
     int loops = 0;   // per_loop: fixed from the first call until a reset
+    // q8_2f: the fields of the sequence's slots froze (a row was appended with
+    // 64 rows stored; every slot of a sequence holds the same positions, so
+    // they freeze in the same call).  kv_cache.rs `truncate_last` drops rows
+    // only: a rollback keeps them frozen.  Cleared by a reset.
+    bool q8_frozen = false;
 };
 
 constexpr int kStages = 32;
@@ -222,6 +227,7 @@ struct Enq {
     std::vector<int64_t> pos;    // every row's position (host copy, for the q8 freeze)
     std::vector<int> seq;        // every row's sequence
     std::vector<uint8_t> froze;  // slots whose field this call froze: [max_seqs][n_ord][kMaxLoops]
+    std::vector<uint8_t> q8f;    // per row: its sequence's fields were frozen before this call
     int o_parts = 1;             // split-K slabs of o the last output projection wrote
     const float *o_ss = nullptr; // multi-row attention: per-row partial sums of |z|^2 scaling o
     int o_ss_n = 0;
@@ -308,7 +314,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         if (h->q8)
             for (int r = 0; r < M; ++r) {
                 uint8_t &fz = froze_at(q, q.seq[r], l.ord, slot);
-                if (q.pos[r] == kWarmup && !fz) {
+                if (q.pos[r] >= kWarmup && !q.q8f[r] && !fz) {
                     LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, r, q.s));
                     fz = 1;
                 }
@@ -337,7 +343,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
             // is appended; rows before it were encoded without a field, rows after
             // against it.  A later loop's rewrite of the same rows finds it frozen.
             uint8_t &fz = froze_at(q, q.seq[0], l.ord, slot);
-            const bool frozen = pos0 >= kWarmup + 1 || fz;
+            const bool frozen = q.q8f[0] || fz;
             Q8WriteArgs wa{};
             wa.ksrc = h->kstage; wa.kld = h->KV; wa.vsrc = h->qkvg + h->Q + h->KV; wa.vld = ld;
             wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = slot; wa.nk = h->nk; wa.hd = h->hd;
@@ -357,7 +363,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
                 LAUNCH(launch_q8_write(wa, q.s));
                 fz = 1;
             }
-            field = pos0 >= kWarmup + 1 || fz;
+            field = q.q8f[0] || fz;
         }
         chunk_split(h, pos0, M, aa);
         aa.field = field;
@@ -514,9 +520,9 @@ int put_record(dory_t *h, const std::vector<RowRec> &rows, float *logits, hipStr
 }
 
 // Rows of a chunk of one sequence: positions pos0.., logits (if any) of the last.
-std::vector<RowRec> chunk_rows(int seq, int64_t pos0, int n, const int32_t *tokens) {
+std::vector<RowRec> chunk_rows(int seq, int64_t pos0, int n, const int32_t *tokens, bool q8f = false) {
     std::vector<RowRec> rows(n);
-    for (int r = 0; r < n; ++r) rows[r] = RowRec{pos0 + r, seq, tokens ? tokens[r] : 0, 0, 0};
+    for (int r = 0; r < n; ++r) rows[r] = RowRec{pos0 + r, seq, tokens ? tokens[r] : 0, 0, q8f ? 1 : 0};
     return rows;
 }
 
@@ -527,6 +533,7 @@ Enq make_enq(dory_t *h, hipStream_t s, int T, int loops, int mode, bool batch, b
     for (const RowRec &r : rows) {
         q.pos.push_back(r.pos);
         q.seq.push_back(r.seq);
+        q.q8f.push_back((uint8_t)r.q8f);
     }
     q.froze.assign((size_t)h->cfg.max_seqs * h->n_ord * kMaxLoops, 0);
     return q;
@@ -721,11 +728,12 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     int rc = ensure_slots(h, seq, kv_mode, loops);
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens);
+    const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens, st.q8_frozen);
     rc = put_record(h, rows, logits, s);
     if (rc) return rc;
     Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
-    const bool graphable = n == 1 && (!h->q8 || st.pos >= kWarmup + 1);
+    // (q8_2f: once the fields froze, a one-row call launches no freeze)
+    const bool graphable = n == 1 && (!h->q8 || st.q8_frozen);
     if (graphable) {
         auto key = std::make_tuple(loops, kv_mode, seq);
         auto it = h->graphs.find(key);
@@ -758,6 +766,7 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     h->last_mode = kv_mode;
     h->last_pos0 = st.pos;
     h->last_seq0 = seq;
+    if (h->q8 && st.pos + n > kWarmup) st.q8_frozen = true;
     st.pos += n;
     st.mode = kv_mode;
     if (kv_mode == DORY_PER_LOOP) st.loops = loops;
@@ -805,7 +814,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
     std::vector<RowRec> rows(nseq);
     for (int r = 0; r < nseq; ++r) {
         const int i = order[r];
-        rows[r] = RowRec{h->seqs[seqs[i]].pos, seqs[i], tokens[i], i, 0};
+        rows[r] = RowRec{h->seqs[seqs[i]].pos, seqs[i], tokens[i], i, h->seqs[seqs[i]].q8_frozen ? 1 : 0};
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     int rc = put_record(h, rows, logits, s);
@@ -826,6 +835,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
     h->last_mode = kv_mode;
     for (int i = 0; i < nseq; ++i) {
         SeqState &st = h->seqs[seqs[i]];
+        if (h->q8 && st.pos >= kWarmup) st.q8_frozen = true;
         st.pos += 1;
         st.mode = kv_mode;
         if (kv_mode == DORY_PER_LOOP) st.loops = loops[i];
@@ -838,6 +848,24 @@ int dory_kv_reset(dory_t *h, int32_t seq) {
     if (seq < -1 || seq >= h->cfg.max_seqs) return fail(h, DORY_EINVAL, "dory_kv_reset: seq out of range");
     for (int s = 0; s < h->cfg.max_seqs; ++s)
         if (seq < 0 || s == seq) h->seqs[s] = SeqState{};
+    return DORY_OK;
+}
+
+int dory_rollback(dory_t *h, int32_t seq, int64_t n) {
+    if (!h) return DORY_EINVAL;
+    if (seq < 0 || seq >= h->cfg.max_seqs) return fail(h, DORY_EINVAL, "dory_rollback: seq out of range");
+    if (n < 0) return fail(h, DORY_EINVAL, "dory_rollback: n must be >= 0");
+    SeqState &st = h->seqs[seq];
+    if (n >= st.pos) return DORY_OK;
+    // The next row, at position n, reads keys max(0, n - W + 1) .. n - 1; a
+    // ring of cap rows still holds positions pos - cap .. pos - 1.
+    auto keeps = [&](int64_t W, int64_t cap) {
+        return cap >= h->cfg.max_ctx || std::max<int64_t>(0, n - W + 1) >= st.pos - cap;
+    };
+    if (!keeps(h->win_s, h->cap_s) || !keeps(h->win_f, h->cap_f))
+        return fail(h, DORY_ERANGE, "dory_rollback: from position " + std::to_string(st.pos) + " to " +
+                                        std::to_string(n) + " is deeper than the windowed rings keep");
+    st.pos = n;
     return DORY_OK;
 }
 
@@ -899,8 +927,7 @@ int dory_kv_field(dory_t *h, int32_t seq, int32_t ord, int32_t slot, float *kcol
     int rc = slot_check(h, seq, ord, slot, &d);
     if (rc) return rc;
     if (!h->q8) return fail(h, DORY_EINVAL, "dory_kv_field: the cache is not q8_2f");
-    const bool frozen = h->seqs[seq].pos >= kWarmup + 1;
-    if (!frozen) return 0;
+    if (!h->seqs[seq].q8_frozen) return 0;
     HIPCHECK(h, hipSetDevice(h->device));
     HIPCHECK(h, hipDeviceSynchronize());
     if (kcol) HIPCHECK(h, hipMemcpy(kcol, d->kcol, sizeof(float) * h->KV, hipMemcpyDeviceToHost));
@@ -968,6 +995,7 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
     st.pos = npos;
     st.mode = kv_mode;
     st.loops = kv_mode == DORY_PER_LOOP ? loops : 0;
+    st.q8_frozen = h->q8 && npos > kWarmup;
     return DORY_OK;
 }
 

@@ -7,6 +7,13 @@ namespace dk {
 
 namespace {
 
+// Whether the cache rows of call row `row` use the frozen q8_2f field (see
+// AttnArgs::field): kv_cache.rs `append` freezes the field at the first append
+// with 64 rows stored, and it stays frozen from then on.
+__device__ __forceinline__ bool field_on(const AttnArgs &a, const RowRec &row) {
+    return a.field > 0 || (a.field < 0 && (row.pos >= kWarmup || row.q8f));
+}
+
 // dory.rs `attn_layer` (rotate, justnorm per head, q times sq), with the RoPE
 // table row of the position (dory.rs `stack`: cos half, sin half).  One wave
 // per (row, head); lane j owns the pairs (j, j + hd/2), (j + 64, j + 64 + hd/2).
@@ -148,8 +155,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
     }
     float vcol = 1.f;
     if (Q8 && wave == 0) {
-        const int64_t p = a.rec->rows[r].pos;
-        if (a.field > 0 || (a.field < 0 && p >= kWarmup))
+        if (field_on(a, a.rec->rows[r]))
             vcol = (a.sd1 ? *a.sd1 : slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot)).vcol[kh * hd + dc];
     }
     __syncthreads();
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < CPL; ++i) wacc[wave][c0 + i] = acc[i];
     __syncthreads();
-    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    const bool field = Q8 && field_on(a, a.rec->rows[r]);
     float ss = 0.f;
     for (int c = tid; c < CH; c += 256) {
         const int ln = c / CPL, hh = c / HD, d = c % HD, hq = kh * REP + hh;
@@ -469,7 +475,7 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
     const int64_t e0 = lo + (int64_t)s * a.split;
     const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
     const bool tail = s == nsplit - 1;
-    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    const bool field = Q8 && field_on(a, a.rec->rows[r]);
     const int cap = sd.cap;
     const int Q = a.nh * HD, KV = a.nk * HD;
     const int g = tid / LPK, dq = tid % LPK;
@@ -709,7 +715,7 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
     const int64_t e0 = lo + (int64_t)s * a.split;
     const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
     const bool tail = s == nsplit - 1;
-    const bool field = Q8 && (a.field > 0 || (a.field < 0 && p >= kWarmup));
+    const bool field = Q8 && field_on(a, a.rec->rows[r]);
     const int cap = sd.cap;
     const int Q = a.nh * HD, KV = a.nk * HD;
     const int g = tid >> 5, dq = tid & 31;

@@ -19,7 +19,9 @@ struct RowRec {
     int32_t seq;
     int32_t token;
     int32_t out;       // logits row (rows of one sequence's chunk: only the last, at 0)
-    int32_t pad;
+    int32_t q8f;       // 1: the sequence's q8_2f fields were frozen before this call
+                       // (kv_cache.rs `append`: once frozen, they stay frozen, also
+                       // across a rollback to fewer than 64 rows)
 };
 
 // The per-call record: written by the host into pinned memory and copied to the
@@ -178,7 +180,8 @@ struct AttnArgs {
     int32_t max_split;   // grid.x; partial stride
     int32_t q8;          // cache encoding
     int32_t field;       // q8: 1 the field is frozen (apply kcol / vcol), 0 not, -1 by
-                         // each row's position (frozen from position 64 on)
+                         // each row: frozen before its call (RowRec::q8f), or frozen
+                         // as its call appends position 64 or later
     const CallRec *rec;
     // one-row calls: the RoPE, norms and cache write of the new row are fused in
     const float *rope;   // [max_ctx][hd] RoPE table of the layer's kind: cos half, sin half

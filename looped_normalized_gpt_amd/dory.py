@@ -59,6 +59,7 @@ def _load():
     L.dory_forward_chunk.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
     L.dory_forward_batch.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp]
     L.dory_kv_reset.argtypes = [vp, i32]
+    L.dory_rollback.argtypes = [vp, i32, i64]
     L.dory_position.argtypes = [vp, i32]
     L.dory_position.restype = i64
     L.dory_debug_tap.argtypes = [vp, vp, i64]
@@ -206,6 +207,10 @@ class Dory:
 
     def reset(self, seq: int = -1):
         self._check(lib.dory_kv_reset(self.h, seq))
+
+    def rollback(self, n: int, seq: int = 0):
+        """Forget the sequence's rows from position n on (dory_rollback)."""
+        self._check(lib.dory_rollback(self.h, seq, n))
 
     def position(self, seq: int = 0) -> int:
         return lib.dory_position(self.h, seq)

@@ -81,6 +81,7 @@ def test_null_handles_and_encoder_arguments_are_rejected():
     from looped_normalized_gpt_amd.dory import lib, EINVAL
     assert lib.dory_forward_chunk(None, 0, None, 1, 1, 0, None, None) == EINVAL
     assert lib.dory_kv_reset(None, 0) == EINVAL
+    assert lib.dory_rollback(None, 0, 0) == EINVAL
     assert lib.dory_debug_tap(None, None, 0) == EINVAL
     assert lib.dory_q8_encode_rows(None, None, 1, 128, 32, None, None, None) == EINVAL
     x = C.c_void_p(16)
