@@ -55,6 +55,7 @@ struct ora_model {
     int *ord_layer;      /* per attention ordinal: its sub-layer index */
     float *inv_s, *inv_f;
     seq_t *seqs;
+    int prompt_loops;    /* [dory] `prompt_loops`: 0 = as many passes as any chunk */
 };
 
 /* ------------------------------------------------------------------ primitives */
@@ -527,11 +528,27 @@ static int check_call(ora_model *m, int32_t seq, int32_t n, int32_t loops, int32
 
 /* [dory] `forward_host` for one chunk, `stack` for the walk through the three
  * blocks, `head` for the logits of the last row. */
+int ora_set_prompt_loops(ora_model *m, int32_t n) {
+    if (!m || n < 0 || n > ORA_MAX_LOOPS) return ORA_EINVAL;
+    m->prompt_loops = n;
+    return ORA_OK;
+}
+
 int ora_forward(ora_model *m, int32_t seq, const int32_t *tokens, int32_t t, int32_t loops,
                 int32_t kv_mode, float *logits, float *tap) {
+    return ora_forward_want(m, seq, tokens, t, loops, kv_mode, logits ? ORA_WANT_LAST : ORA_WANT_NONE, logits, tap);
+}
+
+int ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t t, int32_t loops,
+                     int32_t kv_mode, int32_t want, float *logits, float *tap) {
     int rc = check_call(m, seq, t, loops, kv_mode);
     if (rc) return rc;
-    if (!tokens) return ORA_EINVAL;
+    if (!tokens || want < ORA_WANT_NONE || want > ORA_WANT_ALL || (want != ORA_WANT_NONE && !logits))
+        return ORA_EINVAL;
+    /* [dory] `chunk_loops`: a last_loop chunk whose logits nobody reads keeps
+     * only its cache rows, and runs at most prompt_loops passes. */
+    if (want == ORA_WANT_NONE && m->prompt_loops > 0 && kv_mode == ORA_LAST_LOOP && loops > m->prompt_loops)
+        loops = m->prompt_loops;
     const ora_cfg *c = &m->c;
     seq_t *sq = &m->seqs[seq];
     int H = c->hidden;
@@ -574,10 +591,11 @@ int ora_forward(ora_model *m, int32_t seq, const int32_t *tokens, int32_t t, int
     memcpy(h, state, rowsz);
     for (int li = c->n_in + c->n_rec; li < m->n_layers; li++) SUB(li, 0);
 #undef SUB
-    if (logits) {
-        const float *x = h + (size_t)(t - 1) * H;
-        matvec(m->w.head, x, c->vocab, H, logits);
-        for (int i = 0; i < c->vocab; i++) logits[i] *= m->w.logit_scale[i];
+    /* [dory] `head`: the last row (`Want::Last`) or every row (`Want::All`). */
+    for (int r = want == ORA_WANT_ALL ? 0 : t - 1; want != ORA_WANT_NONE && r < t; r++) {
+        float *lg = logits + (want == ORA_WANT_ALL ? (size_t)r * c->vocab : 0);
+        matvec(m->w.head, h + (size_t)r * H, c->vocab, H, lg);
+        for (int i = 0; i < c->vocab; i++) lg[i] *= m->w.logit_scale[i];
     }
     sq->pos = pos0 + t;
     free(h); free(input); free(state);

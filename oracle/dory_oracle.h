@@ -61,6 +61,17 @@ void ora_destroy(ora_model *m);
  * state after every sub-layer pass) may be NULL. */
 int  ora_forward(ora_model *m, int32_t seq, const int32_t *tokens, int32_t n,
                  int32_t loops, int32_t kv_mode, float *logits, float *tap);
+/* The same call with the rows whose logits are wanted ([dory] `Want`):
+ * ORA_WANT_NONE (logits NULL), ORA_WANT_LAST (logits [vocab], row n-1) or
+ * ORA_WANT_ALL (logits [n][vocab]). */
+#define ORA_WANT_NONE 0
+#define ORA_WANT_LAST 1
+#define ORA_WANT_ALL 2
+int  ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t n,
+                      int32_t loops, int32_t kv_mode, int32_t want, float *logits, float *tap);
+/* [dory] `prompt_loops` (0..16, 0 = off): a last_loop call that wants no
+ * logits runs min(loops, prompt_loops) passes of the recurrent block. */
+int  ora_set_prompt_loops(ora_model *m, int32_t n);
 int  ora_reset(ora_model *m, int32_t seq);
 /* Forget the rows from position n on (dory.rs `DoryState::rollback`). */
 int  ora_rollback(ora_model *m, int32_t seq, int64_t n);

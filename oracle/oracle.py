@@ -60,6 +60,9 @@ def lib():
         L.ora_destroy.argtypes = [C.c_void_p]
         L.ora_forward.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
                                   C.c_int32, C.c_void_p, C.c_void_p]
+        L.ora_forward_want.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
+                                       C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+        L.ora_set_prompt_loops.argtypes = [C.c_void_p, C.c_int32]
         L.ora_reset.argtypes = [C.c_void_p, C.c_int32]
         L.ora_rollback.argtypes = [C.c_void_p, C.c_int32, C.c_int64]
         L.ora_pos.argtypes = [C.c_void_p, C.c_int32]
@@ -165,6 +168,20 @@ class Oracle:
         tp = np.zeros((self.passes(loops), n, self.cfg["hidden"]), np.float32) if tap else None
         _check(lib().ora_forward(self.h, seq, _p(tok), n, loops, mode, _p(lg), _p(tp)))
         return lg, tp
+
+    def forward_all(self, tokens, loops: int, kv_mode="last_loop", seq: int = 0):
+        """One call whose logits are wanted for every row (dory.rs `Want::All`):
+        returns logits [n][vocab]."""
+        mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        n = int(tok.shape[0])
+        lg = np.zeros((n, self.cfg["vocab"]), np.float32)
+        _check(lib().ora_forward_want(self.h, seq, _p(tok), n, loops, mode, 2, _p(lg), None))
+        return lg
+
+    def set_prompt_loops(self, n: int):
+        """dory.rs `prompt_loops`: passes of a logits-free last_loop call (0: off)."""
+        _check(lib().ora_set_prompt_loops(self.h, n))
 
     def forward_rc(self, tokens, loops, kv_mode, seq=0):
         """Raw status of a call (for the error-path tests)."""

@@ -291,3 +291,47 @@ def test_rollback_bounds(tiny):
     o.rollback(3)
     assert o.pos() == 3 and o.slot_rows(0, 0) == 3 and o.slot_rows(1, 1) == 3
     assert o.forward_rc(ids, 3, "per_loop") == -2    # the per_loop loop count stays fixed
+
+
+def test_want_all_rows_pages_case(pages):
+    """dory.rs `Want::All`: the head over every row of the call.  Its last row is
+    the `Want::Last` logits bit for bit, and under per_loop (chunk invariant, the
+    pages' test) row r equals the last logits of a call that ends at row r."""
+    cfg, w = pages
+    cfg = dict(cfg, window=5)
+    ids = np.array([i * 7 % 11 for i in range(23)], np.int32)
+    o = O.Oracle(cfg, w, max_ctx=64)
+    allv = o.forward_all(ids, 2, "per_loop")
+    o2 = O.Oracle(cfg, w, max_ctx=64)
+    last, _ = o2.forward(ids, 2, "per_loop")
+    assert np.array_equal(allv[-1], last)
+    for r in (0, 4, 11, 17):
+        o3 = O.Oracle(cfg, w, max_ctx=64)
+        lr, _ = o3.forward(ids[:r + 1], 2, "per_loop")
+        assert np.abs(allv[r] - lr).max() < 2e-4, r
+
+
+def test_prompt_loops_caps_logits_free_last_loop_calls(tiny):
+    """dory.rs `chunk_loops`: with prompt_loops 1, a last_loop call that wants no
+    logits runs one pass (its cache rows equal a loops-1 call's); a call that
+    wants logits, and per_loop, run every pass."""
+    cfg, w = tiny
+    ids = synth.make_tokens(40, cfg["vocab"])
+    a = O.Oracle(cfg, w, max_ctx=128)
+    a.set_prompt_loops(1)
+    a.forward(ids[:30], 4, "last_loop", logits=False)
+    b = O.Oracle(cfg, w, max_ctx=128)
+    b.forward(ids[:30], 1, "last_loop", logits=False)
+    c = O.Oracle(cfg, w, max_ctx=128)
+    c.forward(ids[:30], 4, "last_loop", logits=False)
+    for od in range(a.n_ord):
+        for p in (0, 17, 29):
+            ra, rb, rc = a.kv_read(od, 0, p), b.kv_read(od, 0, p), c.kv_read(od, 0, p)
+            assert all(np.array_equal(x, y) for x, y in zip(ra, rb))
+    assert not all(np.array_equal(x, y) for x, y in zip(a.kv_read(1, 0, 29), c.kv_read(1, 0, 29)))
+    la, _ = a.forward(ids[30:], 4, "last_loop")       # logits wanted: four passes
+    lc, _ = c.forward(ids[30:], 4, "last_loop")
+    lb, _ = b.forward(ids[30:], 4, "last_loop")
+    assert np.array_equal(la, lb) and not np.array_equal(la, lc)
+    with pytest.raises(Exception):
+        a.set_prompt_loops(17)

@@ -40,6 +40,9 @@ MUTANTS = {
     "v_unscaled": ("acc += s[e] * (double)vs[row] * (double)vc[row * hd + i];", "acc += s[e] * (double)vc[row * hd + i];"),
     "k_group_scale_index": ("d += dg * (double)ks[row * ngk + g];", "d += dg * (double)ks[row * ngk];"),
     "rollback_keeps_rows": ("if (q->slots[i].rows > n) q->slots[i].rows = n;", ";"),
+    "all_rows_read_the_last": ("matvec(m->w.head, h + (size_t)r * H, c->vocab, H, lg);",
+                               "matvec(m->w.head, h + (size_t)(t - 1) * H, c->vocab, H, lg);"),
+    "prompt_loops_ignored": ("        loops = m->prompt_loops;", "        ;"),
     "rollback_unfreezes": ("if (q->slots[i].rows > n) q->slots[i].rows = n;",
                            "if (q->slots[i].rows > n) { q->slots[i].rows = n; q->slots[i].frozen = 0; }"),
 }
