@@ -122,6 +122,21 @@ const char *dory_last_error(const dory_t *h);
 int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
                        int32_t loops, int32_t kv_mode, dory_stream_t stream, float *logits);
 
+/* dory_forward_chunk with the logits of every row (dory.rs `Want::All`):
+ * logits is device fp32 [n][vocab], row r for the token at position pos + r,
+ * and must not be NULL (DORY_EINVAL).  Rows of a multi-row call go through the
+ * head as one GEMM (bf16 weights: bf16 operands, fp32 accumulation, as the
+ * other projections of such a call); the handle allocates a [max_chunk][vocab]
+ * fp32 buffer for it on the first such call.  Otherwise as dory_forward_chunk. */
+int dory_forward_chunk_all(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
+                           int32_t loops, int32_t kv_mode, dory_stream_t stream, float *logits);
+
+/* dory.rs `prompt_loops` (0..16; 0, the default, turns it off): a last_loop
+ * call that wants no logits (logits NULL; a batch with logits NULL, row by row)
+ * runs min(loops, n) passes of the recurrent block, since only its cache rows
+ * stay (dory.rs `chunk_loops`).  per_loop calls are not affected. */
+int dory_set_prompt_loops(dory_t *h, int32_t n);
+
 /* One decode step of nseq sequences at once: row i is the next token of
  * sequence seqs[i] (distinct, 0 <= seqs[i] < max_seqs), run with loops[i] passes
  * of the recurrent block (1..16; per_loop sequences need their fixed count).

@@ -68,6 +68,8 @@ struct dory {
     float *zss = nullptr;  // multi-row attention: sums of squares of z per (row, kv head)
     float *uss = nullptr;  // multi-row MLP: sums of squares of the SwiGLU rows
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
+    float *hlog_all = nullptr;  // every row's head output of a chunk [max_chunk][vocab] (allocated on first use)
+    int prompt_loops = 0;       // dory.rs `prompt_loops`: 0 = off
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
     std::vector<SlotDesc> tab_host;
@@ -228,6 +230,7 @@ struct Enq {
     std::vector<int> seq;        // every row's sequence
     std::vector<uint8_t> froze;  // slots whose field this call froze: [max_seqs][n_ord][kMaxLoops]
     std::vector<uint8_t> q8f;    // per row: its sequence's fields were frozen before this call
+    bool want_all = false;       // a chunk whose every row's logits are wanted (dory.rs `Want::All`)
     int o_parts = 1;             // split-K slabs of o the last output projection wrote
     const float *o_ss = nullptr; // multi-row attention: per-row partial sums of |z|^2 scaling o
     int o_ss_n = 0;
@@ -492,12 +495,15 @@ int enqueue(Enq &q) {
         rf.h_out = h->hb[P % 2];
         rf.hb_out = h->xb;
         LAUNCH(launch_resolve_rows(rf, h->H, T, h->rec, q.s));
-        if (q.want_logits && !q.batch) {
+        if (q.want_logits && !q.batch && !q.want_all) {
             a.row = T - 1; a.src = h->hb[P % 2];
             LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));
         } else if (q.want_logits) {
-            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->xb, h->H, gemm_w(h->w.head, h->V), h->V, h->H, h->hlog, h->V, T, q.s));
-            LAUNCH(launch_logits_rows(h->hlog, h->w.logit_scale, h->V, T, h->rec, q.s));
+            // every row: the head as a GEMM, then the logit scale into each
+            // row's logits row (the record's `out`)
+            float *hl = q.want_all ? h->hlog_all : h->hlog;
+            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->xb, h->H, gemm_w(h->w.head, h->V), h->V, h->H, hl, h->V, T, q.s));
+            LAUNCH(launch_logits_rows(hl, h->w.logit_scale, h->V, T, h->rec, q.s));
         }
     }
     return DORY_OK;
@@ -520,9 +526,10 @@ int put_record(dory_t *h, const std::vector<RowRec> &rows, float *logits, hipStr
 }
 
 // Rows of a chunk of one sequence: positions pos0.., logits (if any) of the last.
-std::vector<RowRec> chunk_rows(int seq, int64_t pos0, int n, const int32_t *tokens, bool q8f = false) {
+std::vector<RowRec> chunk_rows(int seq, int64_t pos0, int n, const int32_t *tokens, bool q8f = false,
+                               bool all = false) {
     std::vector<RowRec> rows(n);
-    for (int r = 0; r < n; ++r) rows[r] = RowRec{pos0 + r, seq, tokens ? tokens[r] : 0, 0, q8f ? 1 : 0};
+    for (int r = 0; r < n; ++r) rows[r] = RowRec{pos0 + r, seq, tokens ? tokens[r] : 0, all ? r : 0, q8f ? 1 : 0};
     return rows;
 }
 
@@ -705,8 +712,12 @@ void dory_destroy(dory_t *h) {
 
 const char *dory_last_error(const dory_t *h) { return h ? h->err.c_str() : g_create_error.c_str(); }
 
-int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
-                       dory_stream_t stream, float *logits) {
+namespace {
+
+// dory_forward_chunk (all = false: logits of the last row, or none) and
+// dory_forward_chunk_all (every row's logits).
+int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
+                  dory_stream_t stream, float *logits, bool all) {
     if (!h) return DORY_EINVAL;
     const dory_config &c = h->cfg;
     if (seq < 0 || seq >= c.max_seqs) return fail(h, DORY_EINVAL, "dory_forward_chunk: seq out of range");
@@ -722,16 +733,23 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     if (kv_mode == DORY_PER_LOOP && st.loops > 0 && st.loops != loops)
         return fail(h, DORY_ESTATE, "dory_forward_chunk: per_loop needs the same loop count on every call");
     if (st.pos + n > c.max_ctx) return fail(h, DORY_ERANGE, "dory_forward_chunk: position past max_ctx");
+    if (all && !logits) return fail(h, DORY_EINVAL, "dory_forward_chunk_all: logits must not be null");
+    // dory.rs `chunk_loops`: a last_loop call whose logits nobody reads keeps
+    // only its cache rows and runs at most prompt_loops passes
+    if (!logits && kv_mode == DORY_LAST_LOOP && h->prompt_loops > 0) loops = std::min(loops, h->prompt_loops);
     if (h->tap && (int64_t)passes(h, loops) * n * h->H > h->tap_cap)
         return fail(h, DORY_EINVAL, "dory_forward_chunk: the tap buffer is too small for this call");
     HIPCHECK(h, hipSetDevice(h->device));
+    all = all && n > 1;  // one row: its logits are the last row's
+    if (all && !h->hlog_all) HIPCHECK(h, dmalloc(h, &h->hlog_all, (size_t)c.max_chunk * h->V));
     int rc = ensure_slots(h, seq, kv_mode, loops);
     if (rc) return rc;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens, st.q8_frozen);
+    const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens, st.q8_frozen, all);
     rc = put_record(h, rows, logits, s);
     if (rc) return rc;
     Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
+    q.want_all = all;
     // (q8_2f: once the fields froze, a one-row call launches no freeze)
     const bool graphable = n == 1 && (!h->q8 || st.q8_frozen);
     if (graphable) {
@@ -773,6 +791,25 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
     return DORY_OK;
 }
 
+}  // namespace
+
+int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
+                       dory_stream_t stream, float *logits) {
+    return forward_chunk(h, seq, tokens, n, loops, kv_mode, stream, logits, false);
+}
+
+int dory_forward_chunk_all(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
+                           dory_stream_t stream, float *logits) {
+    return forward_chunk(h, seq, tokens, n, loops, kv_mode, stream, logits, true);
+}
+
+int dory_set_prompt_loops(dory_t *h, int32_t n) {
+    if (!h) return DORY_EINVAL;
+    if (n < 0 || n > DORY_MAX_LOOPS) return fail(h, DORY_EINVAL, "dory_set_prompt_loops: n must be in 0..16");
+    h->prompt_loops = n;
+    return DORY_OK;
+}
+
 int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32_t *tokens, const int32_t *loops,
                        int32_t kv_mode, dory_stream_t stream, float *logits) {
     if (!h) return DORY_EINVAL;
@@ -795,6 +832,12 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
             return fail(h, DORY_ESTATE, "dory_forward_batch: per_loop needs the same loop count on every call");
         if (st.pos + 1 > c.max_ctx) return fail(h, DORY_ERANGE, "dory_forward_batch: position past max_ctx");
     }
+    // dory.rs `chunk_loops` for rows whose logits nobody reads (each row is a
+    // one-row call of its sequence)
+    std::vector<int32_t> lp(loops, loops + nseq);
+    if (!logits && kv_mode == DORY_LAST_LOOP && h->prompt_loops > 0)
+        for (int32_t &x : lp) x = std::min(x, (int32_t)h->prompt_loops);
+    loops = lp.data();
     if (h->tap) {
         int lmax = 0;
         for (int i = 0; i < nseq; ++i) lmax = std::max(lmax, (int)loops[i]);

@@ -60,6 +60,8 @@ def _load():
     L.dory_forward_batch.argtypes = [vp, i32, vp, vp, vp, i32, vp, vp]
     L.dory_kv_reset.argtypes = [vp, i32]
     L.dory_rollback.argtypes = [vp, i32, i64]
+    L.dory_forward_chunk_all.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
+    L.dory_set_prompt_loops.argtypes = [vp, i32]
     L.dory_position.argtypes = [vp, i32]
     L.dory_position.restype = i64
     L.dory_debug_tap.argtypes = [vp, vp, i64]
@@ -179,6 +181,21 @@ class Dory:
                                     mode, _stream(stream), _ptr(out))
         self._check(rc)
         return out
+
+    def forward_all(self, tokens, loops: int, kv_mode="last_loop", seq: int = 0, stream=None):
+        """One call with the logits of every row (dory_forward_chunk_all):
+        returns a device fp32 tensor [n][vocab]."""
+        import torch
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        out = torch.empty((int(tok.shape[0]), self.cfg["vocab"]), dtype=torch.float32, device=self.device)
+        mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
+        self._check(lib.dory_forward_chunk_all(self.h, seq, tok.ctypes.data_as(C.c_void_p), int(tok.shape[0]),
+                                               loops, mode, _stream(stream), _ptr(out)))
+        return out
+
+    def set_prompt_loops(self, n: int):
+        """dory_set_prompt_loops: passes of a logits-free last_loop call (0: off)."""
+        self._check(lib.dory_set_prompt_loops(self.h, n))
 
     def forward_batch(self, seqs, tokens, loops, kv_mode="last_loop", logits=True, stream=None):
         """One decode step of several sequences: row i = next token of seqs[i] with

@@ -32,7 +32,7 @@ MUTANTS = {
                   "return (float)(x / (1.0 + exp(x)) * ((double)b * (double)su));"),
     "no_q_scale": ("for (int i = 0; i < hd; i++) row[i] *= L->sq[hh * hd + i];", ";"),
     "no_renorm_before_o": ("        ora_justnorm(yr, Q);\n", "\n"),
-    "no_logit_scale": ("logits[i] *= m->w.logit_scale[i];", ";"),
+    "no_logit_scale": ("lg[i] *= m->w.logit_scale[i];", ";"),
     "field_without_sqrt": ("float c = sqrtf(col[d] / (float)rows);", "float c = col[d] / (float)rows;"),
     "key_not_normed": ("            ora_rope_rotate(row, hd, inv, pos0 + r);\n            ora_justnorm(row, hd);\n        }\n    }",
                        "            ora_rope_rotate(row, hd, inv, pos0 + r);\n        }\n    }"),
