@@ -40,6 +40,10 @@ typedef struct {
 
 typedef struct {
     int64_t pos;
+    float exit_rate;     /* [dory] `ExitRate`: rate of early exits (starts at 1) */
+    uint32_t exit_tokens;
+    uint64_t gate_tokens, gate_one;   /* gated tokens, and those that left after one pass */
+    float last_top;      /* the top probability of the last read-out (-1: none yet) */
     int mode;            /* -1: not fixed yet */
     int loops;           /* per_loop: the loop count fixed at the first call; 0 unset */
     slot_t *slots;       /* [n_ord][ORA_MAX_LOOPS] */
@@ -56,6 +60,8 @@ struct ora_model {
     float *inv_s, *inv_f;
     seq_t *seqs;
     int prompt_loops;    /* [dory] `prompt_loops`: 0 = as many passes as any chunk */
+    int gate_on;         /* [dory] `Gate::Conf(th)` for one-row calls */
+    float gate_th;
 };
 
 /* ------------------------------------------------------------------ primitives */
@@ -371,6 +377,8 @@ int ora_create(const ora_cfg *cfg, const ora_weights *w, ora_model **out) {
     m->seqs = (seq_t *)calloc((size_t)c->max_seqs, sizeof(seq_t));
     for (int s = 0; s < c->max_seqs; s++) {
         m->seqs[s].mode = -1;
+        m->seqs[s].exit_rate = 1.0f;
+        m->seqs[s].last_top = -1.0f;
         m->seqs[s].slots = (slot_t *)calloc((size_t)(m->n_ord * ORA_MAX_LOOPS), sizeof(slot_t));
     }
     *out = m;
@@ -400,6 +408,10 @@ int ora_reset(ora_model *m, int32_t seq) {
         q->pos = 0;
         q->mode = -1;
         q->loops = 0;
+        q->exit_rate = 1.0f;
+        q->exit_tokens = 0;
+        q->gate_tokens = q->gate_one = 0;
+        q->last_top = -1.0f;
     }
     return ORA_OK;
 }
@@ -437,8 +449,10 @@ static void attn_sub(ora_model *m, seq_t *sq, int li, int loop_i, float *h, int 
     int rec = is_recurrent(m, li);
     /* [dory] `slot_loop`: per_loop keeps a slot per loop for recurrent layers. */
     int si = (sq->mode == ORA_PER_LOOP && rec) ? loop_i : 0;
-    /* [dory] `stack`: under last_loop a later loop rewrites this chunk's rows. */
-    int overwrite = sq->mode == ORA_LAST_LOOP && rec && loop_i > 0;
+    /* [dory] `stack`: under last_loop a later loop rewrites this chunk's rows
+     * (in the output block, only the early exit's second read-out runs at a
+     * later loop: it replaces the first read-out's rows). */
+    int overwrite = sq->mode == ORA_LAST_LOOP && li >= c->n_in && loop_i > 0;
     slot_t *s = &sq->slots[m->ordinal[li] * ORA_MAX_LOOPS + si];
     const float *inv = sliding ? m->inv_s : m->inv_f;
 
@@ -528,6 +542,49 @@ static int check_call(ora_model *m, int32_t seq, int32_t n, int32_t loops, int32
 
 /* [dory] `forward_host` for one chunk, `stack` for the walk through the three
  * blocks, `head` for the logits of the last row. */
+/* [dory] `top_prob`: the softmax probability of the largest logit, with the
+ * terms more than 20 below it left out of the sum (f64 sum, f32 result). */
+float ora_top_prob(const float *lg, int32_t n) {
+    float top = -INFINITY;
+    for (int32_t i = 0; i < n; i++) top = lg[i] > top ? lg[i] : top;
+    double den = 0.0;
+    for (int32_t i = 0; i < n; i++) {
+        float t = lg[i] - top;
+        if (t > -20.0f) den += exp((double)t);
+    }
+    return (float)(1.0 / den);
+}
+
+/* [dory] `ExitRate::probe`: is this token worth a read-out after its first
+ * pass?  Always while early exits are frequent (rate >= 0.35), else one token
+ * in eight. */
+static int exit_probe(seq_t *q) {
+    q->exit_tokens += 1u;
+    return q->exit_rate >= 0.35f || q->exit_tokens % 8u == 0u;
+}
+
+/* [dory] `ExitRate::note`: a running mean of the exits, weight 0.1 (f32). */
+static void exit_note(seq_t *q, int exited) {
+    q->exit_rate += 0.1f * ((float)(exited ? 1 : 0) - q->exit_rate);
+}
+
+int ora_set_gate(ora_model *m, int32_t on, float th) {
+    if (!m || (on && !(th >= 0.0f))) return ORA_EINVAL;
+    m->gate_on = on ? 1 : 0;
+    m->gate_th = th;
+    return ORA_OK;
+}
+
+int ora_gate_stats(const ora_model *m, int32_t seq, int64_t *tokens, int64_t *one, float *last_top, float *rate) {
+    if (!m || seq < 0 || seq >= m->c.max_seqs) return ORA_EINVAL;
+    const seq_t *q = &m->seqs[seq];
+    if (tokens) *tokens = (int64_t)q->gate_tokens;
+    if (one) *one = (int64_t)q->gate_one;
+    if (last_top) *last_top = q->last_top;
+    if (rate) *rate = q->exit_rate;
+    return ORA_OK;
+}
+
 int ora_set_prompt_loops(ora_model *m, int32_t n) {
     if (!m || n < 0 || n > ORA_MAX_LOOPS) return ORA_EINVAL;
     m->prompt_loops = n;
@@ -545,6 +602,11 @@ int ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t t
     if (rc) return rc;
     if (!tokens || want < ORA_WANT_NONE || want > ORA_WANT_ALL || (want != ORA_WANT_NONE && !logits))
         return ORA_EINVAL;
+    /* [dory] `stack`: under the gate a one-row call runs its first pass, and a
+     * second one only if the gate asks for it, on the last-loop cache (a
+     * per_loop cache would take the read-out's rows twice) */
+    const int early = t == 1 && m->gate_on;
+    if (early && (kv_mode != ORA_LAST_LOOP || tap)) return ORA_EINVAL;
     /* [dory] `chunk_loops`: a last_loop chunk whose logits nobody reads keeps
      * only its cache rows, and runs at most prompt_loops passes. */
     if (want == ORA_WANT_NONE && m->prompt_loops > 0 && kv_mode == ORA_LAST_LOOP && loops > m->prompt_loops)
@@ -581,7 +643,7 @@ int ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t t
      * the recurrent block, state = justnorm(h). */
     memcpy(input, h, rowsz);
     memcpy(state, input, rowsz);
-    for (int i = 0; i < loops; i++) {
+    for (int i = 0; i < (early ? 1 : loops); i++) {
         for (size_t j = 0; j < (size_t)t * H; j++) h[j] = state[j] + input[j];
         for (int r = 0; r < t; r++) ora_justnorm(h + (size_t)r * H, H);
         for (int li = c->n_in; li < c->n_in + c->n_rec; li++) SUB(li, i);
@@ -589,8 +651,44 @@ int ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t t
         for (int r = 0; r < t; r++) ora_justnorm(state + (size_t)r * H, H);
     }
     memcpy(h, state, rowsz);
-    for (int li = c->n_in + c->n_rec; li < m->n_layers; li++) SUB(li, 0);
+    float *exit_lg = NULL;
+    if (early) {
+        /* [dory] `stack`, the early exit (`Gate::Conf`): a read-out through the
+         * output block and the head when the exit rate says it is worth one;
+         * the token leaves if its top probability reaches the threshold.
+         * Otherwise a second pass from the first one's state rewrites this
+         * position (and the read-out's rows, at loop 1) and reads out again. */
+        int stay = 1, readout = 0;
+        if (exit_probe(sq)) {
+            readout = 1;
+            for (int li = c->n_in + c->n_rec; li < m->n_layers; li++) SUB(li, 0);
+            exit_lg = (float *)malloc(sizeof(float) * (size_t)c->vocab);
+            matvec(m->w.head, h, c->vocab, H, exit_lg);
+            for (int i = 0; i < c->vocab; i++) exit_lg[i] *= m->w.logit_scale[i];
+            sq->last_top = ora_top_prob(exit_lg, c->vocab);
+            stay = sq->last_top < m->gate_th;
+            exit_note(sq, !stay);
+        }
+        if (stay) {
+            for (int j = 0; j < H; j++) h[j] = state[j] + input[j];
+            ora_justnorm(h, H);
+            for (int li = c->n_in; li < c->n_in + c->n_rec; li++) SUB(li, 1);
+            ora_justnorm(h, H);
+            for (int li = c->n_in + c->n_rec; li < m->n_layers; li++) SUB(li, readout);
+            free(exit_lg);
+            exit_lg = NULL;
+        }
+        sq->gate_tokens += 1;
+        sq->gate_one += stay ? 0 : 1;
+    } else {
+        for (int li = c->n_in + c->n_rec; li < m->n_layers; li++) SUB(li, 0);
+    }
 #undef SUB
+    if (exit_lg) {   /* the token left after one pass: the read-out's logits */
+        if (want != ORA_WANT_NONE) memcpy(logits, exit_lg, sizeof(float) * (size_t)c->vocab);
+        free(exit_lg);
+        want = ORA_WANT_NONE;
+    }
     /* [dory] `head`: the last row (`Want::Last`) or every row (`Want::All`). */
     for (int r = want == ORA_WANT_ALL ? 0 : t - 1; want != ORA_WANT_NONE && r < t; r++) {
         float *lg = logits + (want == ORA_WANT_ALL ? (size_t)r * c->vocab : 0);

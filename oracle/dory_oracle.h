@@ -72,6 +72,17 @@ int  ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t 
 /* [dory] `prompt_loops` (0..16, 0 = off): a last_loop call that wants no
  * logits runs min(loops, prompt_loops) passes of the recurrent block. */
 int  ora_set_prompt_loops(ora_model *m, int32_t n);
+/* [dory] `Gate::Conf(th)` (on = 0: no gate): a one-row last_loop call runs one
+ * pass of the recurrent block, a read-out when the exit rate asks for one, and
+ * a second pass unless the read-out's top probability reaches th.  Gated calls
+ * take no tap. */
+int  ora_set_gate(ora_model *m, int32_t on, float th);
+/* Per sequence: gated tokens, tokens that left after one pass, the last
+ * read-out's top probability (-1 before any) and the exit rate. */
+int  ora_gate_stats(const ora_model *m, int32_t seq, int64_t *tokens, int64_t *one, float *last_top,
+                    float *rate);
+/* [dory] `top_prob`. */
+float ora_top_prob(const float *lg, int32_t n);
 int  ora_reset(ora_model *m, int32_t seq);
 /* Forget the rows from position n on (dory.rs `DoryState::rollback`). */
 int  ora_rollback(ora_model *m, int32_t seq, int64_t n);

@@ -63,6 +63,10 @@ def lib():
         L.ora_forward_want.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
                                        C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
         L.ora_set_prompt_loops.argtypes = [C.c_void_p, C.c_int32]
+        L.ora_set_gate.argtypes = [C.c_void_p, C.c_int32, C.c_float]
+        L.ora_gate_stats.argtypes = [C.c_void_p, C.c_int32] + [C.c_void_p] * 4
+        L.ora_top_prob.argtypes = [C.c_void_p, C.c_int32]
+        L.ora_top_prob.restype = C.c_float
         L.ora_reset.argtypes = [C.c_void_p, C.c_int32]
         L.ora_rollback.argtypes = [C.c_void_p, C.c_int32, C.c_int64]
         L.ora_pos.argtypes = [C.c_void_p, C.c_int32]
@@ -178,6 +182,18 @@ class Oracle:
         lg = np.zeros((n, self.cfg["vocab"]), np.float32)
         _check(lib().ora_forward_want(self.h, seq, _p(tok), n, loops, mode, 2, _p(lg), None))
         return lg
+
+    def set_gate(self, th):
+        """dory.rs `Gate::Conf(th)` for one-row calls; None turns it off."""
+        _check(lib().ora_set_gate(self.h, 0 if th is None else 1, 0.0 if th is None else float(th)))
+
+    def gate_stats(self, seq: int = 0):
+        """(gated tokens, tokens out after one pass, last read-out's top
+        probability, exit rate)."""
+        t, o = C.c_int64(), C.c_int64()
+        lt, r = C.c_float(), C.c_float()
+        _check(lib().ora_gate_stats(self.h, seq, C.byref(t), C.byref(o), C.byref(lt), C.byref(r)))
+        return t.value, o.value, lt.value, r.value
 
     def set_prompt_loops(self, n: int):
         """dory.rs `prompt_loops`: passes of a logits-free last_loop call (0: off)."""
@@ -322,3 +338,9 @@ def silu_gate(a, sg, b, su):
 
 def sigmoid_gate(y, g, sg):
     return lib().ora_sigmoid_gate(y, g, sg)
+
+
+def top_prob(lg) -> float:
+    """dory.rs `top_prob` on a row of logits."""
+    a = np.ascontiguousarray(lg, dtype=np.float32)
+    return float(lib().ora_top_prob(_p(a), int(a.shape[0])))

@@ -335,3 +335,79 @@ def test_prompt_loops_caps_logits_free_last_loop_calls(tiny):
     assert np.array_equal(la, lb) and not np.array_equal(la, lc)
     with pytest.raises(Exception):
         a.set_prompt_loops(17)
+
+
+# ---------------------------------------------------------------- the early exit (Gate::Conf)
+
+def test_top_prob_pages_case():
+    """dory.rs test `top_prob_of_a_sure_row`, and the softmax maximum in fp64
+    where no term is dropped (every logit within 20 of the top)."""
+    lg = np.full(100, -30.0, np.float32)
+    lg[7] = 30.0
+    assert O.top_prob(lg) > 0.999
+    assert abs(O.top_prob(np.array([1.0, 1.0], np.float32)) - 0.5) < 1e-5
+    x = np.random.default_rng(3).uniform(-5, 5, 1000).astype(np.float32)
+    e = np.exp(x.astype(np.float64) - x.max())
+    assert abs(O.top_prob(x) - 1.0 / e.sum()) < 1e-7
+
+
+def _gate_run(cfg, w, ids, th, loops=2):
+    o = O.Oracle(cfg, w, max_ctx=256)
+    o.set_gate(th)
+    o.forward(ids[:8], loops, "last_loop")            # a multi-row call: no gate
+    out = [o.forward(ids[i:i + 1], loops, "last_loop")[0] for i in range(8, len(ids))]
+    return o, out
+
+
+def test_gate_that_never_exits_equals_two_loops(tiny):
+    """Threshold above 1: every token takes the second pass, read out or not,
+    and rewrites the first read-out's rows: bit for bit a forward of loops 2
+    (logits and cache rows).  The probes follow `ExitRate`: the rate falls by a
+    tenth per read-out, so tokens 1..10 read out, then every eighth."""
+    cfg, w = tiny
+    ids = synth.make_tokens(28, cfg["vocab"], seq=6)
+    g, got = _gate_run(cfg, w, ids, 2.0, loops=7)
+    r = O.Oracle(cfg, w, max_ctx=256)
+    r.forward(ids[:8], 7, "last_loop")
+    want = [r.forward(ids[i:i + 1], 2, "last_loop")[0] for i in range(8, 28)]
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+    for od in range(g.n_ord):
+        assert g.slot_rows(od, 0) == r.slot_rows(od, 0) == 28
+        for p in (8, 19, 27):
+            assert all(np.array_equal(x, y) for x, y in zip(g.kv_read(od, 0, p), r.kv_read(od, 0, p)))
+    rate = np.float32(1.0)
+    for _ in range(11):       # read-outs at tokens 1..10 and 16 of the 20
+        rate = np.float32(rate + np.float32(0.1) * (np.float32(0.0) - rate))
+    tokens, one, last, got_rate = g.gate_stats()
+    assert (tokens, one) == (20, 0) and got_rate == rate and 0 < last < 1
+
+
+def test_gate_that_always_exits_equals_one_loop(tiny):
+    """Threshold 0: every token leaves after its read-out (the rate stays 1, so
+    every token reads out): bit for bit a forward of loops 1."""
+    cfg, w = tiny
+    ids = synth.make_tokens(20, cfg["vocab"], seq=7)
+    g, got = _gate_run(cfg, w, ids, 0.0, loops=5)
+    r = O.Oracle(cfg, w, max_ctx=256)
+    r.forward(ids[:8], 5, "last_loop")
+    want = [r.forward(ids[i:i + 1], 1, "last_loop")[0] for i in range(8, 20)]
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+    assert g.gate_stats()[:2] == (12, 12) and g.gate_stats()[3] == 1.0
+
+
+def test_gate_rules(tiny):
+    cfg, w = tiny
+    ids = synth.make_tokens(10, cfg["vocab"], seq=8)
+    o = O.Oracle(cfg, w, max_ctx=64)
+    o.set_gate(0.5)
+    assert o.forward_rc(ids[:1], 2, "per_loop") == -1    # the gate works on the last-loop cache
+    with pytest.raises(Exception):
+        o.forward(ids[:1], 2, "last_loop", tap=True)      # gated calls take no tap
+    with pytest.raises(Exception):
+        o.set_gate(-0.1)
+    # multi-row calls are not gated
+    a, _ = o.forward(ids[:6], 3, "last_loop")
+    b, _ = O.Oracle(cfg, w, max_ctx=64).forward(ids[:6], 3, "last_loop")
+    assert np.array_equal(a, b) and o.gate_stats()[0] == 0

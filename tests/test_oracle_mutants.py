@@ -43,6 +43,11 @@ MUTANTS = {
     "all_rows_read_the_last": ("matvec(m->w.head, h + (size_t)r * H, c->vocab, H, lg);",
                                "matvec(m->w.head, h + (size_t)(t - 1) * H, c->vocab, H, lg);"),
     "prompt_loops_ignored": ("        loops = m->prompt_loops;", "        ;"),
+    "readout_rows_appended": ("int overwrite = sq->mode == ORA_LAST_LOOP && li >= c->n_in && loop_i > 0;",
+                              "int overwrite = sq->mode == ORA_LAST_LOOP && rec && loop_i > 0;"),
+    "probe_every_token": ("return q->exit_rate >= 0.35f || q->exit_tokens % 8u == 0u;", "return 1;"),
+    "second_pass_from_readout": ("for (int j = 0; j < H; j++) h[j] = state[j] + input[j];",
+                                 "for (int j = 0; j < H; j++) h[j] = h[j] + input[j];"),
     "rollback_unfreezes": ("if (q->slots[i].rows > n) q->slots[i].rows = n;",
                            "if (q->slots[i].rows > n) { q->slots[i].rows = n; q->slots[i].frozen = 0; }"),
 }
