@@ -15,6 +15,11 @@ seeded tokens:
 * ``batch``: 64 sequences, each prefilled to 8192 tokens (last_loop, loops 4);
   a step is one batched decode call with one token per sequence and a loop
   count per (sequence, step) drawn uniformly from 1..16.
+* ``gate``: the ``decode`` workload with the confidence-gated early exit on
+  (dory.rs ``Gate::Conf``, threshold ``--gate``, 0.7 by default): every token
+  runs one or two passes as the gate decides; a token that reads out waits for
+  its read-out on the host, so the host clock times the steps.  No CPU
+  baseline (the oracle's decode sample is not gated).
 
 Timed: ``--steps`` steps after ``--warmup`` untimed ones, bracketed by device
 synchronisation and HIP events on the stream the library launches on.  One JSON
@@ -208,7 +213,7 @@ def prompt(g, cfg, n, loops, mode, seq=0, chunk=512, tok_seed=None, last_logits=
         g.forward(toks[c:c + chunk], loops, mode, seq=seq, logits=(last_logits and c + chunk >= n))
 
 
-def run_decode(args, q8):
+def run_decode(args, q8, gate=None):
     import numpy as np
     import torch
 
@@ -232,6 +237,10 @@ def run_decode(args, q8):
     prefill_s = time.perf_counter() - t0
 
     logits = torch.empty(cfg["vocab"], dtype=torch.float32, device="cuda")
+    if gate is not None:
+        # the confidence-gated early exit on every one-row call (its passes
+        # replace `loops`); a call with a read-out waits for it on the host
+        g.set_gate(gate)
     for i in range(W):
         g.forward(toks[ctx + i:ctx + i + 1], loops, "last_loop", logits=logits)
     torch.cuda.synchronize()
@@ -245,6 +254,9 @@ def run_decode(args, q8):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms = ev0.elapsed_time(ev1) / K
+    if gate is not None:
+        ms = wall_ms / K   # the read-outs wait on the host: the host clock is the one that counts
+        gstats = g.gate_stats()
     assert torch.isfinite(logits).all().item(), "non-finite logits"
     tok_s = 1000.0 / ms
     bytes_tok = float(np.mean([token_bytes(cfg, ctx + i, loops) for i in range(W, W + K)]))
@@ -267,7 +279,11 @@ def run_decode(args, q8):
         cctx = 8200 if q8 else ctx
         cpu = cpu_decode(cfg, w, cctx, lambda i: loops, 20.0,
                          f"decode tokens of Dory-2B (loops {loops}, last_loop{', q8_2f' if q8 else ''})")
-    if q8:
+    if gate is not None:
+        metric = f"gated decode tokens/s (confidence gate {gate}), 1×MI355X, Dory-2B ctx {ctx}"
+        workload = (f"Dory-2B decode, batch 1, context {ctx}, confidence-gated early exit at top probability "
+                    f"{gate} (one or two passes), last_loop, fp32 KV cache, bf16 weights with fp32 arithmetic")
+    elif q8:
         metric = "q8_2f long-context decode tokens/s (all loops) + achieved HBM GB/s, 1×MI355X, Dory-2B ctx 32768"
         workload = (f"Dory-2B decode, batch 1, context {ctx}, loops 4, last_loop, q8_2f KV cache "
                     f"(full_window 8192), bf16 weights with fp32 arithmetic")
@@ -275,7 +291,7 @@ def run_decode(args, q8):
         metric = METRIC
         workload = (f"Dory-2B decode, batch 1, context {ctx}, loops 4, last_loop, fp32 KV cache, "
                     f"bf16 weights with fp32 arithmetic")
-    return {
+    out = {
         "metric": metric, "value": round(tok_s, 2), "unit": "tokens/s", "steps": K, "warmup": W,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
@@ -290,6 +306,17 @@ def run_decode(args, q8):
                      "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3)},
         "cpu_baseline": cpu,
     }
+    if gate is not None:
+        # passes per token follow the gate's decisions, not `loops`: the byte
+        # count above assumes 4 loops and is not reported for this workload
+        tokens, one, _, rate = gstats
+        for k in ("hbm_gbps_algorithmic", "bytes_per_token", "hbm_frac_of_peak"):
+            out.pop(k)
+        out["config"]["loops"] = "1 or 2 (gated)"
+        out["gate"] = {"threshold": gate, "tokens": tokens, "one_pass": one, "exit_rate": round(rate, 4),
+                       "note": "synthetic weights: top probabilities stay far below the threshold, so no token "
+                               "exits; the exit rate falls and 1 token in 8 reads out after its first pass"}
+    return out
 
 
 def run_prefill(args):
@@ -440,7 +467,9 @@ def run_batch(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--config", choices=("decode", "q8", "prefill", "batch"), default="decode")
+    ap.add_argument("--config", choices=("decode", "q8", "prefill", "batch", "gate"), default="decode")
+    ap.add_argument("--gate", type=float, default=0.7,
+                    help="gate workload: the top-probability threshold (dory.rs `--loops auto` default 0.7)")
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--context", type=int, default=None, help="decode context / prompt length")
@@ -467,6 +496,9 @@ def main():
         del src, dst
     if args.config in ("decode", "q8"):
         out = run_decode(args, args.config == "q8")
+    elif args.config == "gate":
+        args.no_cpu_baseline = True   # the oracle's decode sample is not gated
+        out = run_decode(args, False, gate=args.gate)
     elif args.config == "prefill":
         out = run_prefill(args)
     else:

@@ -137,6 +137,26 @@ int dory_forward_chunk_all(dory_t *h, int32_t seq, const int32_t *tokens, int32_
  * stay (dory.rs `chunk_loops`).  per_loop calls are not affected. */
 int dory_set_prompt_loops(dory_t *h, int32_t n);
 
+/* dory.rs `Gate::Conf(threshold)`, the confidence-gated early exit (on = 0
+ * turns it off; threshold >= 0, else DORY_EINVAL).  While on, every one-row
+ * call (a call of one token) runs one pass of the recurrent block instead of
+ * `loops`; if its sequence's exit rate asks for a read-out (dory.rs `ExitRate`:
+ * while at least 0.35 of the recent read-outs exited, else one token in eight)
+ * it runs the output block and the head, and the token leaves with those
+ * logits when their top probability (dory.rs `top_prob`) reaches the
+ * threshold.  Otherwise a second pass from the first one's state rewrites the
+ * position (and the read-out's rows) and the output block and head run again.
+ * A call with a read-out waits for it on the host (it synchronises its
+ * stream); one without is a plain two-pass call.  Gated calls need the
+ * last_loop cache and no tap (DORY_EINVAL); batches of several sequences are
+ * refused while the gate is on.  The first call allocates a few buffers. */
+int dory_set_gate(dory_t *h, int32_t on, float threshold);
+
+/* The gate's counters of a sequence: gated tokens, tokens that left after one
+ * pass, the last read-out's top probability (-1 before any), the exit rate
+ * (any pointer may be NULL).  Cleared by dory_kv_reset. */
+int dory_gate_stats(const dory_t *h, int32_t seq, int64_t *tokens, int64_t *one, float *last_top, float *rate);
+
 /* One decode step of nseq sequences at once: row i is the next token of
  * sequence seqs[i] (distinct, 0 <= seqs[i] < max_seqs), run with loops[i] passes
  * of the recurrent block (1..16; per_loop sequences need their fixed count).

@@ -37,6 +37,11 @@ struct SeqState {
     // they freeze in the same call).  kv_cache.rs `truncate_last` drops rows
     // only: a rollback keeps them frozen.  Cleared by a reset.
     bool q8_frozen = false;
+    // dory.rs `ExitRate` and the gate's counters (the early exit)
+    float exit_rate = 1.0f;
+    uint32_t exit_tokens = 0;
+    int64_t gate_tokens = 0, gate_one = 0;
+    float last_top = -1.0f;
 };
 
 constexpr int kStages = 32;
@@ -70,6 +75,14 @@ struct dory {
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     float *hlog_all = nullptr;  // every row's head output of a chunk [max_chunk][vocab] (allocated on first use)
     int prompt_loops = 0;       // dory.rs `prompt_loops`: 0 = off
+    // dory.rs `Gate::Conf(th)`: one-row last_loop calls leave after one pass
+    // when the read-out's top probability reaches gate_th
+    bool gate_on = false;
+    float gate_th = 0.f;
+    float *gst = nullptr;       // the first pass's e at the loop exit, before its norm [H]
+    float *glog = nullptr;      // read-out logits of a call that wants none [V]
+    float *gtop = nullptr;      // the read-out's top probability (device)
+    float *gtop_host = nullptr; // ... copied to pinned host memory
     CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
     std::vector<SlotDesc> tab_host;
@@ -167,6 +180,7 @@ void free_all(dory_t *h) {
     for (int i = 0; i < kStages; ++i)
         if (h->stage_ev[i]) (void)hipEventDestroy(h->stage_ev[i]);
     if (h->stage) (void)hipHostFree(h->stage);
+    if (h->gtop_host) (void)hipHostFree(h->gtop_host);
     if (h->cap_stream) (void)hipStreamDestroy(h->cap_stream);
 }
 
@@ -231,6 +245,11 @@ struct Enq {
     std::vector<uint8_t> froze;  // slots whose field this call froze: [max_seqs][n_ord][kMaxLoops]
     std::vector<uint8_t> q8f;    // per row: its sequence's fields were frozen before this call
     bool want_all = false;       // a chunk whose every row's logits are wanted (dory.rs `Want::All`)
+    // the early exit: the loop exit also stores e before its norm (gate_save);
+    // a second pass starts at pass k0 from e0 (one row) instead of the embedding
+    bool gate_save = false;
+    int k0 = 0;
+    const float *e0 = nullptr;
     int o_parts = 1;             // split-K slabs of o the last output projection wrote
     const float *o_ss = nullptr; // multi-row attention: per-row partial sums of |z|^2 scaling o
     int o_ss_n = 0;
@@ -428,14 +447,15 @@ int enqueue(Enq &q) {
     dory_t *h = q.h;
     const dory_config &c = h->cfg;
     const int T = q.T;
-    LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], T > 1 ? h->xb : nullptr, q.s));
+    if (q.k0 == 0)
+        LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], T > 1 ? h->xb : nullptr, q.s));
     const int P = passes(h, q.loops);
     auto rows_of = [&](int k) {
         if (k < c.n_in || k >= c.n_in + c.n_rec * q.loops) return T;
         return q.act[(k - c.n_in) / c.n_rec];
     };
     int prev_li = -1;
-    for (int k = 0; k < P; ++k) {
+    for (int k = q.k0; k < P; ++k) {
         int li, loop_i = 0, op = kLoopNone;
         if (k < c.n_in) {
             li = k;
@@ -465,12 +485,18 @@ int enqueue(Enq &q) {
             rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0; rs.h_out = nullptr;
             rs.tap_pass = -1;
             rs.n_prev = T;
+        } else if (k == q.k0) {
+            // the early exit's second pass: e is the first pass's, as saved
+            rs.h = q.e0; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0;
+            rs.h_out = h->hb[k % 2]; rs.hb_out = h->xb; rs.tap_pass = -1;
+            rs.n_prev = T;
         } else {
             rs.h = h->hb[(k - 1) % 2]; rs.o = h->o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
             rs.h_out = h->hb[k % 2]; rs.hb_out = h->xb; rs.tap_pass = k - 1;
             rs.n_prev = rows_of(k - 1);
             if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, h->rec, q.s));
         }
+        if (op == kLoopExit && q.gate_save) rs.e_out = h->gst;
         const LayerInfo &l = h->L[li];
         const float *x = h->hb[k % 2];
         int rc = l.attn ? enq_attn(q, l, loop_i, rs, x, M) : enq_mlp(q, l, rs, x, M);
@@ -714,6 +740,65 @@ const char *dory_last_error(const dory_t *h) { return h ? h->err.c_str() : g_cre
 
 namespace {
 
+// dory.rs `ExitRate::probe`: a read-out after the first pass while early exits
+// are frequent (rate >= 0.35), else for one token in eight.
+bool exit_probe(SeqState &st) {
+    st.exit_tokens += 1u;
+    return st.exit_rate >= 0.35f || st.exit_tokens % 8u == 0u;
+}
+
+// dory.rs `ExitRate::note`: running mean of the exits, weight 0.1.
+void exit_note(SeqState &st, bool exited) { st.exit_rate += 0.1f * ((exited ? 1.0f : 0.0f) - st.exit_rate); }
+
+// A gated one-row call whose token reads out after its first pass (dory.rs
+// `stack`, `Gate::Conf`): the first pass, the output block and the head
+// (saving the loop exit's e), the top probability back on the host; then,
+// unless it reaches the threshold, a second pass from the saved e that
+// rewrites this position (the read-out's rows too: one-row writes go to the
+// position's ring row) and reads out again.  Synchronous: it waits for the
+// read-out.
+int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, float *logits) {
+    const dory_config &c = h->cfg;
+    SeqState &st = h->seqs[seq];
+    const std::vector<RowRec> rows = chunk_rows(seq, st.pos, 1, tokens, st.q8_frozen);
+    float *lg = logits ? logits : h->glog;
+    int rc = put_record(h, rows, lg, s);
+    if (rc) return rc;
+    Enq q = make_enq(h, s, 1, 1, DORY_LAST_LOOP, false, true, rows);
+    q.gate_save = true;
+    rc = enqueue(q);
+    if (rc) return rc;
+    HIPCHECK(h, launch_top_prob(lg, h->V, h->gtop, s));
+    HIPCHECK(h, hipMemcpyAsync(h->gtop_host, h->gtop, sizeof(float), hipMemcpyDeviceToHost, s));
+    HIPCHECK(h, hipStreamSynchronize(s));
+    const float tp = *h->gtop_host;
+    const bool stay = tp < h->gate_th;
+    st.last_top = tp;
+    exit_note(st, !stay);
+    if (stay) {
+        Enq q2 = q;  // the same record and the freezes the first pass made
+        q2.loops = 2;
+        q2.act.assign(2, 1);
+        q2.gate_save = false;
+        q2.k0 = c.n_in + c.n_rec;
+        q2.e0 = h->gst;
+        rc = enqueue(q2);
+        if (rc) return rc;
+    }
+    st.gate_tokens += 1;
+    st.gate_one += stay ? 0 : 1;
+    h->last_T = 1;
+    h->last_chunk = false;
+    h->last_loops = stay ? 2 : 1;
+    h->last_mode = DORY_LAST_LOOP;
+    h->last_pos0 = st.pos;
+    h->last_seq0 = seq;
+    if (h->q8 && st.pos + 1 > kWarmup) st.q8_frozen = true;
+    st.pos += 1;
+    st.mode = DORY_LAST_LOOP;
+    return DORY_OK;
+}
+
 // dory_forward_chunk (all = false: logits of the last row, or none) and
 // dory_forward_chunk_all (every row's logits).
 int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
@@ -734,12 +819,24 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
         return fail(h, DORY_ESTATE, "dory_forward_chunk: per_loop needs the same loop count on every call");
     if (st.pos + n > c.max_ctx) return fail(h, DORY_ERANGE, "dory_forward_chunk: position past max_ctx");
     if (all && !logits) return fail(h, DORY_EINVAL, "dory_forward_chunk_all: logits must not be null");
+    // dory.rs `stack`: under the gate a one-row call runs one pass, a read-out
+    // when the exit rate asks for one, and a second pass unless it exits
+    const bool gated = n == 1 && h->gate_on;
+    if (gated && kv_mode != DORY_LAST_LOOP)
+        return fail(h, DORY_EINVAL, "dory_forward_chunk: the exit gate works on the last_loop cache");
+    if (gated && h->tap) return fail(h, DORY_EINVAL, "dory_forward_chunk: gated calls take no tap");
     // dory.rs `chunk_loops`: a last_loop call whose logits nobody reads keeps
     // only its cache rows and runs at most prompt_loops passes
     if (!logits && kv_mode == DORY_LAST_LOOP && h->prompt_loops > 0) loops = std::min(loops, h->prompt_loops);
     if (h->tap && (int64_t)passes(h, loops) * n * h->H > h->tap_cap)
         return fail(h, DORY_EINVAL, "dory_forward_chunk: the tap buffer is too small for this call");
     HIPCHECK(h, hipSetDevice(h->device));
+    if (gated) {
+        int rc0 = ensure_slots(h, seq, kv_mode, 2);
+        if (rc0) return rc0;
+        if (exit_probe(st)) return gated_readout(h, seq, tokens, reinterpret_cast<hipStream_t>(stream), logits);
+        loops = 2;  // no read-out: both passes, then the output block once
+    }
     all = all && n > 1;  // one row: its logits are the last row's
     if (all && !h->hlog_all) HIPCHECK(h, dmalloc(h, &h->hlog_all, (size_t)c.max_chunk * h->V));
     int rc = ensure_slots(h, seq, kv_mode, loops);
@@ -785,6 +882,7 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
     h->last_pos0 = st.pos;
     h->last_seq0 = seq;
     if (h->q8 && st.pos + n > kWarmup) st.q8_frozen = true;
+    if (gated) st.gate_tokens += 1;
     st.pos += n;
     st.mode = kv_mode;
     if (kv_mode == DORY_PER_LOOP) st.loops = loops;
@@ -803,6 +901,31 @@ int dory_forward_chunk_all(dory_t *h, int32_t seq, const int32_t *tokens, int32_
     return forward_chunk(h, seq, tokens, n, loops, kv_mode, stream, logits, true);
 }
 
+int dory_set_gate(dory_t *h, int32_t on, float threshold) {
+    if (!h) return DORY_EINVAL;
+    if (on && !(threshold >= 0.0f)) return fail(h, DORY_EINVAL, "dory_set_gate: the threshold must be >= 0");
+    if (on && !h->gst) {
+        HIPCHECK(h, hipSetDevice(h->device));
+        HIPCHECK(h, dmalloc(h, &h->gst, (size_t)h->H));
+        HIPCHECK(h, dmalloc(h, &h->glog, (size_t)h->V));
+        HIPCHECK(h, dmalloc(h, &h->gtop, (size_t)1));
+        HIPCHECK(h, hipHostMalloc((void **)&h->gtop_host, sizeof(float), hipHostMallocDefault));
+    }
+    h->gate_on = on != 0;
+    h->gate_th = on ? threshold : 0.f;
+    return DORY_OK;
+}
+
+int dory_gate_stats(const dory_t *h, int32_t seq, int64_t *tokens, int64_t *one, float *last_top, float *rate) {
+    if (!h || seq < 0 || seq >= h->cfg.max_seqs) return DORY_EINVAL;
+    const SeqState &st = h->seqs[seq];
+    if (tokens) *tokens = st.gate_tokens;
+    if (one) *one = st.gate_one;
+    if (last_top) *last_top = st.last_top;
+    if (rate) *rate = st.exit_rate;
+    return DORY_OK;
+}
+
 int dory_set_prompt_loops(dory_t *h, int32_t n) {
     if (!h) return DORY_EINVAL;
     if (n < 0 || n > DORY_MAX_LOOPS) return fail(h, DORY_EINVAL, "dory_set_prompt_loops: n must be in 0..16");
@@ -818,6 +941,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
     if (nseq > c.max_chunk || nseq > c.max_seqs) return fail(h, DORY_ERANGE, "dory_forward_batch: nseq > max_chunk or max_seqs");
     if (kv_mode != DORY_PER_LOOP && kv_mode != DORY_LAST_LOOP)
         return fail(h, DORY_EINVAL, "dory_forward_batch: kv_mode must be per_loop or last_loop");
+    if (h->gate_on && nseq > 1) return fail(h, DORY_EINVAL, "dory_forward_batch: the exit gate takes one-row calls");
     std::vector<uint8_t> seen(c.max_seqs, 0);
     for (int i = 0; i < nseq; ++i) {
         const int sq = seqs[i];

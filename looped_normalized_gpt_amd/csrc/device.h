@@ -281,6 +281,12 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
 #pragma unroll
         for (int j = 0; j < EPT; ++j) e[j] *= f;
     } else if (rs.loop_op != kLoopNone) {
+        if (rs.loop_op == kLoopExit && writer && rs.e_out)
+#pragma unroll
+            for (int j = 0; j < EPT; j += 4)
+                if (reg_index(j) < H)
+                    *reinterpret_cast<float4 *>(rs.e_out + (size_t)r * H + reg_index(j)) =
+                        make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < EPT; ++j) s += e[j] * e[j];

@@ -83,6 +83,7 @@ struct Resolve {
     int32_t slerp;       // 1: e = slerp(h, o, alpha); 0: e = h
     int32_t loop_op;
     int32_t tap_pass;    // pass index of e for the tap, or -1
+    float *e_out;        // kLoopExit: e before its norm (the early exit's second pass starts from it), or null
     int32_t n_prev, n_next;
     int32_t pad;
 };
@@ -125,6 +126,9 @@ hipError_t launch_rownorm(const float *src, int ld_src, float *dst, uint16_t *ds
 // renorm is then a per-row factor its consumer applies).
 hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su,
                               float *dst, uint16_t *dstb, int F, int T, hipStream_t s, float *ss = nullptr);
+
+// dory.rs `top_prob` of one row of logits lg[V] into *out (one workgroup).
+hipError_t launch_top_prob(const float *lg, int V, float *out, hipStream_t s);
 
 // Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
 hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,

@@ -205,7 +205,45 @@ __global__ __launch_bounds__(256) void k_logits_rows(const float *hlog, const fl
     rec->logits[(size_t)rec->rows[r].out * V + v] = hlog[(size_t)r * V + v] * ls[v];
 }
 
+// dory.rs `top_prob`: the softmax probability of the largest logit, the terms
+// more than 20 below it left out, the sum in f64.  One workgroup of 1024
+// threads: the maximum, then the sum, each reduced through LDS.
+__global__ __launch_bounds__(1024) void k_top_prob(const float *__restrict__ lg, int V, float *__restrict__ out) {
+    __shared__ float mx[16];
+    __shared__ double sm[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float m = -INFINITY;
+    for (int i = tid; i < V; i += 1024) m = fmaxf(m, lg[i]);
+    m = wave_max(m);
+    if (lane == 0) mx[wave] = m;
+    __syncthreads();
+    float top = mx[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) top = fmaxf(top, mx[w]);
+    double d = 0.0;
+    for (int i = tid; i < V; i += 1024) {
+        const float t = lg[i] - top;
+        if (t > -20.0f) d += exp((double)t);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) d += __shfl_xor(d, off);
+    if (lane == 0) sm[wave] = d;
+    __syncthreads();
+    if (tid == 0) {
+        double den = 0.0;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) den += sm[w];
+        *out = (float)(1.0 / den);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_top_prob(const float *lg, int V, float *out, hipStream_t s) {
+    if (V <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_top_prob, dim3(1), dim3(1024), 0, s, lg, V, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_logits_rows(const float *hlog, const float *ls, int V, int T, const CallRec *rec, hipStream_t s) {
     hipLaunchKernelGGL(k_logits_rows, dim3((V + 255) / 256, T), dim3(256), 0, s, hlog, ls, V, rec);

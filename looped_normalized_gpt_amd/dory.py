@@ -62,6 +62,8 @@ def _load():
     L.dory_rollback.argtypes = [vp, i32, i64]
     L.dory_forward_chunk_all.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
     L.dory_set_prompt_loops.argtypes = [vp, i32]
+    L.dory_set_gate.argtypes = [vp, i32, C.c_float]
+    L.dory_gate_stats.argtypes = [vp, i32, vp, vp, vp, vp]
     L.dory_position.argtypes = [vp, i32]
     L.dory_position.restype = i64
     L.dory_debug_tap.argtypes = [vp, vp, i64]
@@ -192,6 +194,18 @@ class Dory:
         self._check(lib.dory_forward_chunk_all(self.h, seq, tok.ctypes.data_as(C.c_void_p), int(tok.shape[0]),
                                                loops, mode, _stream(stream), _ptr(out)))
         return out
+
+    def set_gate(self, th):
+        """dory_set_gate: the confidence-gated early exit (None: off)."""
+        self._check(lib.dory_set_gate(self.h, 0 if th is None else 1, 0.0 if th is None else float(th)))
+
+    def gate_stats(self, seq: int = 0):
+        """(gated tokens, tokens out after one pass, last read-out's top
+        probability, exit rate)."""
+        t, o = C.c_int64(), C.c_int64()
+        lt, r = C.c_float(), C.c_float()
+        self._check(lib.dory_gate_stats(self.h, seq, C.byref(t), C.byref(o), C.byref(lt), C.byref(r)))
+        return t.value, o.value, lt.value, r.value
 
     def set_prompt_loops(self, n: int):
         """dory_set_prompt_loops: passes of a logits-free last_loop call (0: off)."""

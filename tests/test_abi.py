@@ -83,6 +83,8 @@ def test_null_handles_and_encoder_arguments_are_rejected():
     assert lib.dory_kv_reset(None, 0) == EINVAL
     assert lib.dory_rollback(None, 0, 0) == EINVAL
     assert lib.dory_set_prompt_loops(None, 1) == EINVAL
+    assert lib.dory_set_gate(None, 1, C.c_float(0.5)) == EINVAL
+    assert lib.dory_gate_stats(None, 0, None, None, None, None) == EINVAL
     assert lib.dory_forward_chunk_all(None, 0, None, 1, 1, 0, None, None) == EINVAL
     assert lib.dory_debug_tap(None, None, 0) == EINVAL
     assert lib.dory_q8_encode_rows(None, None, 1, 128, 32, None, None, None) == EINVAL

@@ -27,12 +27,13 @@ MUTANTS = {
     "window_off_by_one": ("int64_t first = p + 1 - win > 0 ? p + 1 - win : 0;", "int64_t first = p - win > 0 ? p - win : 0;"),
     "round_half_even": ("float c = roundf(r[d] / s);", "float c = rintf(r[d] / s);"),
     "freeze_one_row_early": ("if (s->rows >= ORA_WARMUP && !s->frozen)", "if (s->rows >= ORA_WARMUP - 1 && !s->frozen)"),
-    "mix_drops_input": ("h[j] = state[j] + input[j];", "h[j] = state[j];"),
+    "mix_drops_input": ("for (size_t j = 0; j < (size_t)t * H; j++) h[j] = state[j] + input[j];",
+                        "for (size_t j = 0; j < (size_t)t * H; j++) h[j] = state[j];"),
     "silu_sign": ("return (float)(x / (1.0 + exp(-x)) * ((double)b * (double)su));",
                   "return (float)(x / (1.0 + exp(x)) * ((double)b * (double)su));"),
     "no_q_scale": ("for (int i = 0; i < hd; i++) row[i] *= L->sq[hh * hd + i];", ";"),
     "no_renorm_before_o": ("        ora_justnorm(yr, Q);\n", "\n"),
-    "no_logit_scale": ("lg[i] *= m->w.logit_scale[i];", ";"),
+    "no_logit_scale": ("i++) lg[i] *= m->w.logit_scale[i];", "i++) ;"),
     "field_without_sqrt": ("float c = sqrtf(col[d] / (float)rows);", "float c = col[d] / (float)rows;"),
     "key_not_normed": ("            ora_rope_rotate(row, hd, inv, pos0 + r);\n            ora_justnorm(row, hd);\n        }\n    }",
                        "            ora_rope_rotate(row, hd, inv, pos0 + r);\n        }\n    }"),
