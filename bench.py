@@ -148,6 +148,25 @@ def traffic_entry(mode):
     return t.get("bytes_per_launch")
 
 
+def vendor_gemm_tflops(M, N, K, reps=100):
+    """Reference point, not part of the path: torch.mm (hipBLASLt) on an
+    M x N x K bf16 product with a contiguous [K][N] right operand, rotating over
+    8 weight copies so they stream from HBM as the library's weights do."""
+    import torch
+    A = torch.randn(M, K, device="cuda", dtype=torch.bfloat16)
+    Ws = [torch.randn(K, N, device="cuda", dtype=torch.bfloat16) for _ in range(8)]
+    for i in range(16):
+        torch.mm(A, Ws[i % 8])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        torch.mm(A, Ws[i % 8])
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * M * N * K / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e12
+
+
 def time_stage(dory, g, stage, reps, stream):
     import torch
     dory.stage_bench(g, stage, min(reps, 40), stream)   # warm
@@ -358,6 +377,8 @@ def run_prefill(args):
         tflops[st] = round(2 * chunk * N * Kd / (us * 1e-6) / 1e12, 1)
     stages["attn_chunk"] = round(time_stage(dory, g, "attn_chunk", 32, stream), 2)
     g.close()
+    log("bench: the vendor GEMM on the same shapes (reference only)")
+    vendor = {st: round(vendor_gemm_tflops(chunk, N, Kd), 1) for st, (N, Kd) in shapes.items()}
     gu_flops = 2 * chunk * 2 * F * H
     gu_tf = tflops["gemm_gateup"]
 
@@ -374,7 +395,7 @@ def run_prefill(args):
                    "prompt": n, "chunk": chunk, "loops": loops, "kv_mode": "per_loop", "weights": "bf16",
                    "parallelism": "none (one GPU)"},
         "projection_tflops_overall": round(gemm_tflops, 1), "wall_ms_per_step": round(wall_ms / K, 3),
-        "stage_us": stages, "stage_tflops": tflops,
+        "stage_us": stages, "stage_tflops": tflops, "vendor_gemm_tflops_same_shapes": vendor,
         "roofline": {"kernel": "k_gemm_mfma gate|up (512 x 11264 x 2048, bf16)", "bound": "mfma",
                      "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry("prefill"),
