@@ -45,12 +45,21 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "decode tokens/s (all loops) + achieved HBM GB/s, 1×MI355X, Dory-2B ctx 4096"
 CSRC = os.path.join(ROOT, "looped_normalized_gpt_amd", "csrc")
-TRAFFIC = {  # committed counter runs: file, kernel source it was taken on
+TRAFFIC = {  # committed counter runs: file, kernel source it was taken on (with the shared headers)
     "decode": ("gemv_gateup_2b_traffic.json", "gemv.hip"),
     "q8": ("gemv_gateup_2b_traffic.json", "gemv.hip"),
     "prefill": ("gemm_gateup_2b_traffic.json", "gemm.hip"),
     "batch": ("attn_dec_batch64_traffic.json", "attn.hip"),
 }
+TRAFFIC_HEADERS = ("device.h", "internal.h")
+
+
+def sources_digest(src):
+    """sha256 over a kernel source and the headers every kernel includes."""
+    h = hashlib.sha256()
+    for f in (src,) + TRAFFIC_HEADERS:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -135,15 +144,15 @@ def prefill_flops(cfg, T, loops):
 
 def traffic_entry(mode):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    runs, or None when there are none or the kernel source changed since."""
+    runs, or None when there are none or the kernel source or the headers it
+    includes changed since."""
     fname, src = TRAFFIC[mode]
     path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    digest = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
-    if t.get("source_sha256") != digest:
+    if t.get("sources_sha256") != sources_digest(src):
         return None
     return t.get("bytes_per_launch")
 
