@@ -176,6 +176,27 @@ def vendor_gemm_tflops(M, N, K, reps=100):
     return 2 * M * N * K / (e0.elapsed_time(e1) * 1e-3 / reps) / 1e12
 
 
+def vendor_gemv_us(N, K, reps=200):
+    """Reference point, not part of the path: torch.mv (the vendor GEMV) of a
+    bf16 [N][K] matrix by a bf16 vector, rotating over 8 matrices so each launch
+    streams its weights from HBM."""
+    import torch
+    x = torch.randn(K, device="cuda", dtype=torch.bfloat16)
+    Ws = [torch.randn(N, K, device="cuda", dtype=torch.bfloat16) for _ in range(8)]
+    for i in range(16):
+        torch.mv(Ws[i % 8], x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(reps):
+        torch.mv(Ws[i % 8], x)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del Ws
+    return us
+
+
 def time_stage(dory, g, stage, reps, stream):
     import torch
     dory.stage_bench(g, stage, min(reps, 40), stream)   # warm
@@ -298,6 +319,10 @@ def run_decode(args, q8, gate=None):
     stages["gateup"] = round(gu_us, 2)
     g.close()
     gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
+    log("bench: the vendor GEMV on the gate|up shape (reference only)")
+    v_us = vendor_gemv_us(2 * F, H)
+    vendor = {"us": round(v_us, 2), "gbps": round(2 * F * H * 2 / (v_us * 1e-6) / 1e9, 1),
+              "what": "torch.mv, bf16 [11264][2048] x bf16 vector (no SwiGLU)"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -327,7 +352,7 @@ def run_decode(args, q8, gate=None):
                    "kv_encoding": cfg["kv_encoding"], "weights": "bf16", "parallelism": "none (one GPU)"},
         "hbm_gbps_algorithmic": round(gbs, 1), "bytes_per_token": int(bytes_tok),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "wall_ms_per_step": round(wall_ms / K, 4),
-        "prefill_tokens_per_s": round(ctx / prefill_s, 1), "stage_us": stages,
+        "prefill_tokens_per_s": round(ctx / prefill_s, 1), "stage_us": stages, "vendor_gemv_same_shape": vendor,
         "roofline": {"kernel": "k_gemv gate|up + SwiGLU (bf16 [2x5632][2048])", "bound": "hbm",
                      "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_entry("q8" if q8 else "decode"),
