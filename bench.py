@@ -430,7 +430,8 @@ def run_prefill(args):
                    "parallelism": "none (one GPU)"},
         "projection_tflops_overall": round(gemm_tflops, 1), "wall_ms_per_step": round(wall_ms / K, 3),
         "stage_us": stages, "stage_tflops": tflops, "vendor_gemm_tflops_same_shapes": vendor,
-        "roofline": {"kernel": "k_gemm_mfma gate|up (512 x 11264 x 2048, bf16)", "bound": "mfma",
+        "roofline": {"kernel": "k_gemm_mfma2<SwiGLU> gate|up with the SwiGLU epilogue (512 x 11264 x 2048, bf16)",
+                     "bound": "mfma",
                      "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry("prefill"),
                      "flops_per_launch": gu_flops, "us_per_launch": stages["gemm_gateup"]},

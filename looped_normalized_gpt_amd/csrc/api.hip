@@ -72,6 +72,7 @@ struct dory {
     float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     float *zss = nullptr;  // multi-row attention: sums of squares of z per (row, kv head)
     float *uss = nullptr;  // multi-row MLP: sums of squares of the SwiGLU rows
+    float *ussp = nullptr; // ... per 64 ffn indices, from the fused gate|up GEMM [max_chunk][ffn/64]
     float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
     float *hlog_all = nullptr;  // every row's head output of a chunk [max_chunk][vocab] (allocated on first use)
     int prompt_loops = 0;       // dory.rs `prompt_loops`: 0 = off
@@ -423,17 +424,23 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
         d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
         // the renorm before the down projection becomes a per-row factor the
         // next residual step applies (the projection is linear)
-        float *un = gemm_reads_fp32_a(h->wt, true, M, h->F, h->F) ? h->un : nullptr;
-        LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, un, h->unb, h->F, M, q.s, h->uss));
+        const bool fused = h->ussp && gemm_swiglu_ok(h->wt, M, h->F, h->H, h->H) &&
+                           !gemm_reads_fp32_a(h->wt, true, M, h->F, h->F);
+        if (fused) {  // SwiGLU in the GEMM's epilogue: z in bf16, sums of squares per 64 indices
+            LAUNCH(launch_gemm_swiglu(h->xb, h->H, w.wgate, w.wup, h->F, h->H, w.sg, w.su, h->unb, h->ussp, M, q.s));
+        } else {
+            LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
+            float *un = gemm_reads_fp32_a(h->wt, true, M, h->F, h->F) ? h->un : nullptr;
+            LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, un, h->unb, h->F, M, q.s, h->uss));
+        }
         const int S = gemm_pick_splits(h->wt, true, M, h->H, h->F);
         LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s, S,
                            h->o_stride));
         q.o_parts = S;
-        q.o_ss = h->uss;
-        q.o_ss_n = 1;
+        q.o_ss = fused ? h->ussp : h->uss;
+        q.o_ss_n = fused ? h->F / 64 : 1;
     }
     return DORY_OK;
 }
@@ -679,6 +686,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(dmalloc(h, &h->znb, (size_t)chunk * h->Q));
     CREATE_CHECK(dmalloc(h, &h->zss, (size_t)chunk * h->nk));
     CREATE_CHECK(dmalloc(h, &h->uss, (size_t)chunk));
+    if (h->F % 64 == 0) CREATE_CHECK(dmalloc(h, &h->ussp, (size_t)chunk * (h->F / 64)));
     CREATE_CHECK(dmalloc(h, &h->unb, (size_t)chunk * h->F));
     CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));
@@ -1242,7 +1250,11 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
                             gemm_pick_splits(h->wt, true, MC, h->H, h->Q), h->o_stride);
             break;
         case 8:
-            e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
+            if (h->ussp && gemm_swiglu_ok(h->wt, MC, h->F, h->H, h->H))
+                e = launch_gemm_swiglu(h->xb, h->H, l->w.wgate, l->w.wup, h->F, h->H, l->w.sg, l->w.su, h->unb,
+                                       h->ussp, MC, s);
+            else
+                e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
             break;
         case 9:
             e = launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s,

@@ -198,9 +198,20 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(const uint16_t *__restrict__ 
 // accumulator j).  73.7 KB of LDS: two workgroups per CU.
 // Split K: workgroup z takes K range [z K/S, (z+1) K/S) and writes its partial
 // C to C + z * pstride; the caller's consumer adds the S slabs.
+// SWIGLU (the MLP's gate | up projection, dory.rs `mlp_layer`): tile x pairs
+// gate rows 64x .. 64x+63 (columns 0..63, W.w[0]) with the same up rows
+// (columns 64..127, W.w[1]); the waves holding the up half hand their
+// accumulators to the gate waves through LDS (same lane layout, so the same
+// element is the same (row, ffn index)), which store z = silu(a sg) (b su)
+// rounded to bf16 at zb[row][64x + c] (row stride N/2 = ffn) and the row's sum
+// of z^2 over the tile's 64 indices at ssp[row][x] (the renorm before the down
+// projection is then a per-row factor its consumer applies).  No C is written.
+template <bool SWIGLU>
 __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restrict__ A, int lda, const GemmW W, int N,
                                                        int K, float *__restrict__ C, int ldc, int M, int S,
-                                                       size_t pstride) {
+                                                       size_t pstride, const float *__restrict__ sg,
+                                                       const float *__restrict__ su, uint16_t *__restrict__ zb,
+                                                       float *__restrict__ ssp) {
     constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;
     __shared__ __bf16 As[2][BM][LDK];
     __shared__ __bf16 Bs[2][BN][LDK];
@@ -215,9 +226,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int am = m0 + 32 * i + lr < M ? m0 + 32 * i + lr : M - 1;
-        const int bn = n0 + 32 * i + lr < N ? n0 + 32 * i + lr : N - 1;
         arow[i] = A + (size_t)am * lda + kz + lc;
-        brow[i] = seg_row<uint16_t>(W, bn, K) + kz + lc;
+        if (SWIGLU) {  // tile column c: gate row 64x + c, or up row 64x + c - 64
+            const int c = 32 * i + lr;
+            brow[i] = reinterpret_cast<const uint16_t *>(W.w[c < 64 ? 0 : 1]) +
+                      (size_t)(blockIdx.x * 64 + (c & 63)) * K + kz + lc;
+        } else {
+            const int bn = n0 + 32 * i + lr < N ? n0 + 32 * i + lr : N - 1;
+            brow[i] = seg_row<uint16_t>(W, bn, K) + kz + lc;
+        }
     }
     u32x4_t ra0[4], rb0[4];
     // (macros rather than lambdas over array references: the latter left the
@@ -277,6 +294,56 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
 #undef GLOAD
 #undef SSTORE
 #undef COMPUTE
+    if constexpr (SWIGLU) {
+        // The two waves of a 64-row block hold the gate (wn 0) and up (wn 1)
+        // halves of the same (row, ffn index) elements in the same lanes.  Each
+        // hands the other its accumulators of one 32-row tile through LDS (the
+        // operand tiles are free after the loop's last barrier) and finishes
+        // the other tile: wn 0 rows 0..31 of the block, wn 1 rows 32..63.
+        float *ex = reinterpret_cast<float *>(&As[0][0][0]);
+        float *mine = ex + (wn * 2 + wm) * (2 * 16 * 64);          // [j][e][lane]
+        const float *other = ex + ((1 - wn) * 2 + wm) * (2 * 16 * 64);
+        if (wn == 0) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[(j * 16 + e) * 64 + lane] = acc[1][j][e];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) mine[(j * 16 + e) * 64 + lane] = acc[0][j][e];
+        }
+        __syncthreads();
+        const int F = N / 2, x = blockIdx.x;
+        float sgv[2], suv[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sgv[j] = sg[x * 64 + j * 32 + (lane & 31)];
+            suv[j] = su[x * 64 + j * 32 + (lane & 31)];
+        }
+        const int i = wn;  // the 32-row tile this wave finishes
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const float a = wn == 0 ? acc[0][j][e] : other[(j * 16 + e) * 64 + lane];
+                const float b = wn == 0 ? other[(j * 16 + e) * 64 + lane] : acc[1][j][e];
+                const float g = a * sgv[j];
+                const float z = g / (1.0f + expf(-g)) * (b * suv[j]);
+                ss += z * z;
+                if (row < M) zb[(size_t)row * F + x * 64 + j * 32 + (lane & 31)] = f2bf(z);
+            }
+            // the row's 64 indices lie in the 32 lanes of this lane's half: DPP
+            // row sums, then row 0's sum into row 1 and row 2's into row 3
+            ss = group_sum<16>(ss);
+            ss += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(ss), 0x142, 0xA, 0xF, false));
+            if ((lane & 31) == 31 && row < M) ssp[(size_t)row * (F / 64) + x] = ss;
+        }
+        return;
+    }
     float *Cz = C + (size_t)blockIdx.z * pstride;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -553,7 +620,8 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
             if ((long)grid.x * grid.y * grid.z <= 256)
                 hipLaunchKernelGGL(k_gemm_dma<4>, grid, dim3(512), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
             else
-                hipLaunchKernelGGL(k_gemm_mfma2, grid, dim3(256), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts, pstride);
+                hipLaunchKernelGGL(k_gemm_mfma2<false>, grid, dim3(256), 0, s, Ab, lda, W, N, K, C, ldc, M, kparts,
+                                   pstride, nullptr, nullptr, nullptr, nullptr);
             return hipGetLastError();
         }
         if (M >= 32 && K % 8 == 0) {
@@ -571,6 +639,20 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
     dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM), block(256);
     if (wtype == kBF16) hipLaunchKernelGGL((k_gemm_tiled<kBF16>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);
     else hipLaunchKernelGGL((k_gemm_tiled<kF32>), grid, block, 0, s, A, lda, W, N, K, C, ldc, M);
+    return hipGetLastError();
+}
+
+bool gemm_swiglu_ok(int wtype, int M, int F, int K, int lda) {
+    return wtype == kBF16 && M > 64 && F % 64 == 0 && K % 64 == 0 && lda % 8 == 0;
+}
+
+hipError_t launch_gemm_swiglu(const uint16_t *Ab, int lda, const void *wgate, const void *wup, int F, int K,
+                              const float *sg, const float *su, uint16_t *zb, float *ssp, int M, hipStream_t s) {
+    if (!gemm_swiglu_ok(kBF16, M, F, K, lda) || !Ab || !zb || !ssp) return hipErrorInvalidValue;
+    const GemmW W{{wgate, wup, wup, wup}, {F, 2 * F, 2 * F, 2 * F}, 2};
+    const dim3 grid(F / 64, (M + 127) / 128, 1);
+    hipLaunchKernelGGL(k_gemm_mfma2<true>, grid, dim3(256), 0, s, Ab, lda, W, 2 * F, K, nullptr, 0, M, 1, (size_t)0,
+                       sg, su, zb, ssp);
     return hipGetLastError();
 }
 

@@ -151,6 +151,12 @@ inline GemmW gemm_w(const void *w, int N) { return GemmW{{w, w, w, w}, {N, N, N,
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &W, int N, int K,
                        float *C, int ldc, int T, hipStream_t s, int kparts = 1, size_t pstride = 0);
 bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts);
+// The MLP's gate | up projection of a multi-row call with SwiGLU in its
+// epilogue (bf16 weights, more than 64 rows, ffn a multiple of 64): zb [M][F]
+// bf16 = silu(a sg) (b su), ssp [M][F/64] the rows' sums of z^2 per 64 indices.
+bool gemm_swiglu_ok(int wtype, int M, int F, int K, int lda);
+hipError_t launch_gemm_swiglu(const uint16_t *Ab, int lda, const void *wgate, const void *wup, int F, int K,
+                              const float *sg, const float *su, uint16_t *zb, float *ssp, int M, hipStream_t s);
 // Whether launch_gemm reads the fp32 A for this shape (else only the bf16 Ab).
 bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda);
 // Split-K count that fills the chip with 128 x 128 tiles (1 where it does not apply).

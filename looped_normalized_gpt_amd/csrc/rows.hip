@@ -39,9 +39,12 @@ __global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const C
     // (the projection is linear): o times justnorm's factor of |z|^2
     float oc = 1.f;
     if (slerp && rs.o_ss) {
+        // (up to one partial per kv head, or per 64 ffn indices: the lanes of
+        // each wave take them in turn, a wave sum adds them)
+        const float *ps = rs.o_ss + (size_t)r * rs.o_ss_n;
         float t = 0.f;
-        for (int k = 0; k < rs.o_ss_n; ++k) t += rs.o_ss[(size_t)r * rs.o_ss_n + k];
-        oc = norm_factor(t);
+        for (int k = tid & 63; k < rs.o_ss_n; k += 64) t += ps[k];
+        oc = norm_factor(wave_sum(t));
     }
     float h[EPT], o[EPT], al[EPT], in[EPT];
 #pragma unroll
