@@ -249,6 +249,7 @@ struct Enq {
     // the early exit: the loop exit also stores e before its norm (gate_save);
     // a second pass starts at pass k0 from e0 (one row) instead of the embedding
     bool gate_save = false;
+    bool embed_pass = false;     // this pass's GEMV gathers the embedding row itself (one-row calls)
     int k0 = 0;
     const float *e0 = nullptr;
     int o_parts = 1;             // split-K slabs of o the last output projection wrote
@@ -315,7 +316,9 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         a.w[0] = w.wq; a.w[1] = w.wk; a.w[2] = w.wv; a.w[3] = w.wg;
         a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
         a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
-        LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiStore, a, q.s));
+        a.embed = h->w.embed; a.vocab = h->V;
+        const int pro = q.embed_pass ? kProEmbed : rs.loop_op == kLoopNext ? kProResolveInp : kProResolve;
+        LAUNCH(launch_gemv(h->wt, pro, kEpiStore, a, q.s));
     } else {
         LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s));
     }
@@ -418,7 +421,9 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
         GemvArgs a{};
         a.w[0] = w.wgate; a.w[1] = w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H; a.row = 0;
         a.rs = rs; a.y = h->ga; a.sg = w.sg; a.su = w.su; a.rec = h->rec; a.hidden = h->H;
-        LAUNCH(launch_gemv(h->wt, rs.loop_op == kLoopNext ? kProResolveInp : kProResolve, kEpiPair, a, q.s));
+        a.embed = h->w.embed; a.vocab = h->V;
+        const int pro = q.embed_pass ? kProEmbed : rs.loop_op == kLoopNext ? kProResolveInp : kProResolve;
+        LAUNCH(launch_gemv(h->wt, pro, kEpiPair, a, q.s));
         GemvArgs d{};
         d.w[0] = w.wdown; d.seg_end[0] = h->H; d.nseg = 1; d.N = h->H; d.K = h->F; d.row = 0;
         d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
@@ -454,8 +459,9 @@ int enqueue(Enq &q) {
     dory_t *h = q.h;
     const dory_config &c = h->cfg;
     const int T = q.T;
-    if (q.k0 == 0)
-        LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], T > 1 ? h->xb : nullptr, q.s));
+    // one-row calls: the first pass's GEMV gathers the embedding row itself
+    if (q.k0 == 0 && T > 1)
+        LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], h->xb, q.s));
     const int P = passes(h, q.loops);
     auto rows_of = [&](int k) {
         if (k < c.n_in || k >= c.n_in + c.n_rec * q.loops) return T;
@@ -488,8 +494,10 @@ int enqueue(Enq &q) {
         rs.n_next = M;
         if (k == 0) {
             // the first pass takes the embedding as it is; o and alpha only need
-            // to be valid addresses (the GEMV prologue loads them unconditionally)
-            rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0; rs.h_out = nullptr;
+            // to be valid addresses (the GEMV prologue loads them unconditionally).
+            // One row: the GEMV gathers it and stores it as the residual.
+            rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0;
+            rs.h_out = T == 1 ? h->hb[0] : nullptr;
             rs.tap_pass = -1;
             rs.n_prev = T;
         } else if (k == q.k0) {
@@ -506,7 +514,9 @@ int enqueue(Enq &q) {
         if (op == kLoopExit && q.gate_save) rs.e_out = h->gst;
         const LayerInfo &l = h->L[li];
         const float *x = h->hb[k % 2];
+        q.embed_pass = k == 0 && T == 1;
         int rc = l.attn ? enq_attn(q, l, loop_i, rs, x, M) : enq_mlp(q, l, rs, x, M);
+        q.embed_pass = false;
         if (rc) return rc;
         prev_li = li;
     }

@@ -15,6 +15,9 @@
 // Prologues build x in LDS:
 //   kProResolve: the previous sub-layer's slerp and the loop mix (Resolve);
 //                workgroup 0 also stores the new residual, loop input and tap.
+//   kProEmbed:   kProResolve for the very first pass of a one-row call, its
+//                h the embedding row of the record's token (zero for an id
+//                outside the table); workgroup 0 stores it as the residual.
 //   kProNorm:    x = justnorm(src row) (the renorm over Q before O and over F
 //                before down, dory.rs `attn_layer` / `mlp_layer`).
 // Epilogues:
@@ -84,7 +87,7 @@ struct W8<kF32> {
 
 template <int WT, int PRO, int EPI, int MAXC, int ROWS>
 __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-    constexpr bool RES = PRO == kProResolve || PRO == kProResolveInp;
+    constexpr bool RES = PRO == kProResolve || PRO == kProResolveInp || PRO == kProEmbed;
     extern __shared__ float smem[];
     constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
     constexpr int EPT = 8 * MAXC;  // prologue elements per thread: K <= 2048 * MAXC
@@ -110,11 +113,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     float ph[EPT], po[EPT], pa[EPT], pi[EPT];
     {
         const float *src = (RES ? rs.h : a.src) + (size_t)a.row * K;
+        uint32_t tok = 0;
+        bool tok_ok = false;
+        if (PRO == kProEmbed) {
+            tok = (uint32_t)rec->rows[a.row].token;
+            tok_ok = tok < (uint32_t)a.vocab;
+            tok = tok_ok ? tok : 0u;
+        }
 #pragma unroll
         for (int jj = 0; jj < EPT / 4; ++jj) {
             const int i = 4 * tid + 1024 * jj;
             const int ic = i < K ? i : 0;
-            const float4 v = *reinterpret_cast<const float4 *>(src + ic);
+            float4 v;
+            if (PRO == kProEmbed) {
+                if (WT == kBF16) {
+                    const uint2 u = *reinterpret_cast<const uint2 *>(
+                        reinterpret_cast<const uint16_t *>(a.embed) + (size_t)tok * K + ic);
+                    v = make_float4(bf16lo(u.x), bf16hi(u.x), bf16lo(u.y), bf16hi(u.y));
+                } else {
+                    v = *reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(a.embed) + (size_t)tok * K + ic);
+                }
+                if (!tok_ok) v = make_float4(0.f, 0.f, 0.f, 0.f);
+            } else {
+                v = *reinterpret_cast<const float4 *>(src + ic);
+            }
             ph[4 * jj] = v.x; ph[4 * jj + 1] = v.y; ph[4 * jj + 2] = v.z; ph[4 * jj + 3] = v.w;
             if (RES) {
                 const float4 vo = *reinterpret_cast<const float4 *>(rs.o + (size_t)a.row * K + ic);
@@ -263,6 +285,8 @@ hipError_t launch_c(const GemvArgs &a, hipStream_t s) {
 template <int WT>
 hipError_t launch_w(int pro, int epi, const GemvArgs &a, hipStream_t s) {
     if (pro == kProResolve && epi == kEpiStore) return launch_c<WT, kProResolve, kEpiStore>(a, s);
+    if (pro == kProEmbed && epi == kEpiStore) return launch_c<WT, kProEmbed, kEpiStore>(a, s);
+    if (pro == kProEmbed && epi == kEpiPair) return launch_c<WT, kProEmbed, kEpiPair>(a, s);
     if (pro == kProResolveInp && epi == kEpiStore) return launch_c<WT, kProResolveInp, kEpiStore>(a, s);
     if (pro == kProNorm && epi == kEpiStore) return launch_c<WT, kProNorm, kEpiStore>(a, s);
     if (pro == kProResolve && epi == kEpiPair) return launch_c<WT, kProResolve, kEpiPair>(a, s);
@@ -276,6 +300,7 @@ hipError_t launch_w(int pro, int epi, const GemvArgs &a, hipStream_t s) {
 
 hipError_t launch_gemv(int wtype, int pro, int epi, const GemvArgs &a, hipStream_t s) {
     if (a.K <= 0 || a.K > 8192 || a.K % 8 || a.N <= 0) return hipErrorInvalidValue;
+    if (pro == kProEmbed && (!a.embed || a.vocab <= 0)) return hipErrorInvalidValue;
     return wtype == kBF16 ? launch_w<kBF16>(pro, epi, a, s) : launch_w<kF32>(pro, epi, a, s);
 }
 

@@ -92,7 +92,9 @@ enum WType { kF32 = 0, kBF16 = 1 };
 
 // ---------------------------------------------------------------- launchers
 // GEMV for one row (decode).  Prologue builds x in LDS, epilogue stores.
-enum GemvPro { kProPlain = 0, kProNorm = 1, kProResolve = 2, kProResolveInp = 3 };  // Inp: the loop's next pass reads the input
+// Embed: the first pass of a one-row call, its x the embedding row of the
+// record's token (dory.rs `forward_host`: an id outside the table is a zero row).
+enum GemvPro { kProPlain = 0, kProNorm = 1, kProResolve = 2, kProResolveInp = 3, kProEmbed = 4 };  // Inp: the loop's next pass reads the input
 enum GemvEpi { kEpiStore = 0, kEpiPair = 1, kEpiHead = 2 };
 
 struct GemvArgs {
@@ -110,6 +112,8 @@ struct GemvArgs {
     const float *logit_scale;    // kEpiHead
     const CallRec *rec;
     int32_t hidden;      // tap row length
+    const void *embed;   // kProEmbed: the embedding table [vocab][K] (the weights' type)
+    int32_t vocab;
 };
 
 hipError_t launch_gemv(int wtype, int pro, int epi, const GemvArgs &a, hipStream_t s);
