@@ -151,3 +151,33 @@ def test_gate_2b_decode_at_context_2000(D):
     g.close()
     assert worst <= 5e-2, worst
     say(f"2b gate: worst |dlogit| {worst:.3e}")
+
+
+def test_gate_q8_across_the_freeze(D):
+    """q8_2f cache at head dim 128: gated tokens at positions 58..71, so the
+    read-out phase of the token at position 64 freezes the fields and its
+    second pass rewrites the rows against them; threshold 2 (no exits)."""
+    import torch
+    cfg = KV128
+    w = synth.make_weights(cfg)
+    t = synth.make_tokens(80, cfg["vocab"], seq=55)
+    g = D.Dory(cfg, w, max_ctx=256, max_chunk=64, kv_encoding="q8_2f")
+    o = O.Oracle(cfg, w, max_ctx=256, kv_q8=True)
+    g.forward(t[:58], 3, "last_loop", logits=False)
+    o.forward(t[:58], 3, "last_loop", logits=False)
+    g.set_gate(2.0)
+    o.set_gate(2.0)
+    worst = 0.0
+    for i in range(58, 72):
+        lg = g.forward(t[i:i + 1], 3, "last_loop")
+        torch.cuda.synchronize()
+        ol, _ = o.forward(t[i:i + 1], 3, "last_loop")
+        worst = max(worst, float(np.abs(lg.cpu().numpy() - ol).max()))
+        assert g.gate_stats()[:2] == o.gate_stats()[:2]
+    for od in range(g.n_ord):
+        assert g.kv_field(od)[0] and o.kv_field(od)[0]
+    g.close()
+    # bf16 chunk attention on the 58-row first call, and q8 codes of a few new
+    # rows a step apart between the two sides' fp32 keys
+    assert worst <= 2e-2, worst
+    say(f"gate q8 across the freeze: worst |dlogit| {worst:.3e}")
