@@ -768,6 +768,40 @@ bool exit_probe(SeqState &st) {
 // dory.rs `ExitRate::note`: running mean of the exits, weight 0.1.
 void exit_note(SeqState &st, bool exited) { st.exit_rate += 0.1f * ((exited ? 1.0f : 0.0f) - st.exit_rate); }
 
+// Replays the captured graph of key (capturing it first) with the work of q
+// (and the read-out's top probability when top): every pointer a replay needs
+// per call comes from the device record, so one graph serves every call.
+int replay(dory_t *h, std::tuple<int, int, int> key, const Enq &q, bool top, hipStream_t s) {
+    auto it = h->graphs.find(key);
+    if (it == h->graphs.end()) {
+        Enq cq = q;
+        cq.s = h->cap_stream;
+        HIPCHECK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
+        int rc = enqueue(cq);
+        hipError_t e0 = hipSuccess;
+        if (!rc && top) e0 = launch_top_prob(h->rec, h->V, h->gtop, h->cap_stream);
+        hipGraph_t g = nullptr;
+        hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
+        if (rc || e0 != hipSuccess) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc ? rc : hip_fail(h, e0, "launch_top_prob");
+        }
+        if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
+        hipGraphExec_t ex = nullptr;
+        e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
+        it = h->graphs.emplace(key, ex).first;
+    }
+    HIPCHECK(h, hipGraphLaunch(it->second, s));
+    return DORY_OK;
+}
+
+// Graph keys of the early exit's two phases: (kKeyGateFirst / kKeyGateSecond,
+// kv mode, sequence), apart from the (loops 1..16, mode, sequence) of plain
+// one-row calls.
+constexpr int kKeyGateFirst = 101, kKeyGateSecond = 102;
+
 // A gated one-row call whose token reads out after its first pass (dory.rs
 // `stack`, `Gate::Conf`): the first pass, the output block and the head
 // (saving the loop exit's e), the top probability back on the host; then,
@@ -784,9 +818,16 @@ int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, 
     if (rc) return rc;
     Enq q = make_enq(h, s, 1, 1, DORY_LAST_LOOP, false, true, rows);
     q.gate_save = true;
-    rc = enqueue(q);
-    if (rc) return rc;
-    HIPCHECK(h, launch_top_prob(lg, h->V, h->gtop, s));
+    // (q8_2f: graphs once the fields froze, when no phase launches a freeze)
+    const bool graphs = !h->q8 || st.q8_frozen;
+    if (graphs) {
+        rc = replay(h, std::make_tuple(kKeyGateFirst, (int)DORY_LAST_LOOP, seq), q, true, s);
+        if (rc) return rc;
+    } else {
+        rc = enqueue(q);
+        if (rc) return rc;
+        HIPCHECK(h, launch_top_prob(h->rec, h->V, h->gtop, s));
+    }
     HIPCHECK(h, hipMemcpyAsync(h->gtop_host, h->gtop, sizeof(float), hipMemcpyDeviceToHost, s));
     HIPCHECK(h, hipStreamSynchronize(s));
     const float tp = *h->gtop_host;
@@ -800,7 +841,7 @@ int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, 
         q2.gate_save = false;
         q2.k0 = c.n_in + c.n_rec;
         q2.e0 = h->gst;
-        rc = enqueue(q2);
+        rc = graphs ? replay(h, std::make_tuple(kKeyGateSecond, (int)DORY_LAST_LOOP, seq), q2, false, s) : enqueue(q2);
         if (rc) return rc;
     }
     st.gate_tokens += 1;

@@ -131,8 +131,9 @@ hipError_t launch_rownorm(const float *src, int ld_src, float *dst, uint16_t *ds
 hipError_t launch_swiglu_norm(const float *a, const float *b, int ld, const float *sg, const float *su,
                               float *dst, uint16_t *dstb, int F, int T, hipStream_t s, float *ss = nullptr);
 
-// dory.rs `top_prob` of one row of logits lg[V] into *out (one workgroup).
-hipError_t launch_top_prob(const float *lg, int V, float *out, hipStream_t s);
+// dory.rs `top_prob` of the call record's logits row (one-row calls: the
+// record's logits pointer, V floats) into *out (one workgroup).
+hipError_t launch_top_prob(const CallRec *rec, int V, float *out, hipStream_t s);
 
 // Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
 hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,

@@ -211,8 +211,9 @@ __global__ __launch_bounds__(256) void k_logits_rows(const float *hlog, const fl
 // dory.rs `top_prob`: the softmax probability of the largest logit, the terms
 // more than 20 below it left out, the sum in f64.  One workgroup of 1024
 // threads: the maximum, then the sum, each reduced through LDS.
-__global__ __launch_bounds__(1024) void k_top_prob(const float *__restrict__ lg, int V, float *__restrict__ out) {
+__global__ __launch_bounds__(1024) void k_top_prob(const CallRec *rec, int V, float *__restrict__ out) {
     __shared__ float mx[16];
+    const float *lg = rec->logits;  // the call's logits row (one-row calls: row 0)
     __shared__ double sm[16];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float m = -INFINITY;
@@ -242,9 +243,9 @@ __global__ __launch_bounds__(1024) void k_top_prob(const float *__restrict__ lg,
 
 }  // namespace
 
-hipError_t launch_top_prob(const float *lg, int V, float *out, hipStream_t s) {
+hipError_t launch_top_prob(const CallRec *rec, int V, float *out, hipStream_t s) {
     if (V <= 0) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_top_prob, dim3(1), dim3(1024), 0, s, lg, V, out);
+    hipLaunchKernelGGL(k_top_prob, dim3(1), dim3(1024), 0, s, rec, V, out);
     return hipGetLastError();
 }
 
