@@ -163,3 +163,17 @@ def test_2b_full_chunk_past_the_window(model2b, D):
     say("2b chunk of 512 at 700 + 1 decode, loops 1")
     check_pair(run_pair(g, o, [toks[:512], toks[512:]], 1, "last_loop"), COS, DLOGIT, "2b full chunk")
     g.close()
+
+
+def test_2b_chunks_at_the_projection_edges(model2b, D):
+    """Calls of 16, 17, 64 and 65 rows: the few-row projection at one, two and
+    four 16-row tiles (64 its largest), then the 128-row tiles with the SwiGLU
+    epilogue from 65 rows on, each checked after every sub-layer pass."""
+    cfg, w = model2b
+    toks = synth.make_tokens(163, cfg["vocab"], seq=17)
+    g = D.Dory(cfg, w, max_ctx=512, max_chunk=512)
+    o = O.Oracle(cfg, w, max_ctx=512)
+    calls = [toks[:16], toks[16:33], toks[33:97], toks[97:162], toks[162:]]
+    say("2b chunks of 16, 17, 64, 65 + 1 decode")
+    check_pair(run_pair(g, o, calls, 2, "last_loop"), COS, DLOGIT, "2b projection edges")
+    g.close()
