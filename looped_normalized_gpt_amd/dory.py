@@ -47,8 +47,7 @@ class DoryWeights(C.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built: run __graft_entry__.build() "
-                          "(python -c 'import __graft_entry__ as g; g.build()')")
+        raise ImportError(f"{LIB_PATH} is not built: run python -m looped_normalized_gpt_amd.build")
     L = C.CDLL(LIB_PATH)
     vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
     L.dory_create.argtypes = [C.POINTER(DoryConfig), C.POINTER(DoryWeights), C.POINTER(vp)]
