@@ -109,6 +109,33 @@ def test_2b_batch_matches_oracle(D):
     g.close()
 
 
+def test_2b_q8_batch_matches_oracle(D):
+    """The q8_2f batch kernel at head dim 128: four sequences with their caches
+    loaded through the append rules, one whose row at position 64 freezes the
+    field during the first step, one frozen long before, two past the 1024-key
+    sliding window; each row with its own loop count."""
+    cfg = synth.config("2b")
+    w = synth.make_weights(cfg)
+    lens = [64, 200, 1100, 1500]
+    g = D.Dory(cfg, w, max_ctx=1600, max_chunk=512, max_seqs=4, kv_encoding="q8_2f")
+    o = O.Oracle(cfg, w, max_ctx=1600, max_seqs=4, kv_q8=True)
+    n_ord = g.n_ord
+    for s, n in enumerate(lens):
+        k, v = synth.make_kv_rows(n_ord * n, cfg["nk"], cfg["hd"], cfg["hidden"], seed=60 + s)
+        shp = (n_ord, 1, n, cfg["nk"], cfg["hd"])
+        g.kv_load(k.reshape(shp), v.reshape(shp), "last_loop", 1, seq=s)
+        o.kv_load(k.reshape(shp), v.reshape(shp), "last_loop", 1, seq=s)
+    say("2b q8 batch of 4 at contexts 64..1500")
+    worst = _steps(g, o, cfg, 4, 2, "last_loop", lambda t, seqs: np.array([3, 1, 5, 2], np.int32), 5e-2)
+    for s in range(4):
+        for od in range(n_ord):
+            fg, kg, _ = g.kv_field(od, 0, seq=s)
+            fo, ko, _ = o.kv_field(od, 0, seq=s)
+            assert fg and fo and np.array_equal(kg.view(np.uint32), ko.view(np.uint32)), (s, od)
+    say(f"2b q8 batch: worst |dlogit| {worst:.3e}")
+    g.close()
+
+
 def test_batch_errors_change_nothing(D):
     cfg = synth.config("tiny")
     w = synth.make_weights(cfg)
