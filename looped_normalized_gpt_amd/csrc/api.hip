@@ -320,7 +320,19 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         const int pro = q.embed_pass ? kProEmbed : rs.loop_op == kLoopNext ? kProResolveInp : kProResolve;
         LAUNCH(launch_gemv(h->wt, pro, kEpiStore, a, q.s));
     } else {
-        LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s));
+        // A batch's few-row q|k|v|g projection would leave most CUs idle: its K
+        // is split into slabs (while the workgroups fit the chip in one round
+        // and the slabs the buffer), added into the first before attention.
+        int parts = 1;
+        if (q.batch && M <= 64) {
+            const int tiles = (ld + 63) / 64;
+            while (parts < 4 && tiles * (parts + 1) <= 256 && h->H / 128 >= 4 * (parts + 1) &&
+                   (parts + 1) * M <= h->cfg.max_chunk && gemm_splits_ok(h->wt, true, M, h->H, parts + 1))
+                ++parts;
+        }
+        const size_t slab = (size_t)M * ld;
+        LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s, parts, slab));
+        LAUNCH(launch_add_slabs(h->qkvg, slab, parts, slab, q.s));
     }
     AttnArgs aa{};
     aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part;

@@ -118,6 +118,11 @@ struct GemvArgs {
 
 hipError_t launch_gemv(int wtype, int pro, int epi, const GemvArgs &a, hipStream_t s);
 
+// x[i] += x[i + z stride] for z = 1 .. parts-1, i < n, in slab order: the
+// slabs of a K-split projection added into the first (n and stride multiples
+// of 4, stride >= n).
+hipError_t launch_add_slabs(float *x, size_t n, int parts, size_t stride, hipStream_t s);
+
 // Prefill row kernels.
 // The row kernels also write a bf16 copy of what they write (hb, dstb: may be
 // null) for the bf16 GEMMs that read it next.

@@ -241,6 +241,18 @@ __global__ __launch_bounds__(1024) void k_top_prob(const CallRec *rec, int V, fl
     }
 }
 
+__global__ __launch_bounds__(256) void k_add_slabs(float *x, size_t n4, int parts, size_t stride4) {
+    float4 *x4 = reinterpret_cast<float4 *>(x);
+    for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+        float4 v = x4[i];
+        for (int z = 1; z < parts; ++z) {
+            const float4 u = x4[i + z * stride4];
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        }
+        x4[i] = v;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_top_prob(const CallRec *rec, int V, float *out, hipStream_t s) {
@@ -286,6 +298,15 @@ hipError_t launch_rownorm(const float *src, int ld, float *dst, uint16_t *dstb, 
         return hipGetLastError();
     }
     hipLaunchKernelGGL(k_rownorm, dim3(T), dim3(256), 0, s, src, ld, dst, dstb, N);
+    return hipGetLastError();
+}
+
+hipError_t launch_add_slabs(float *x, size_t n, int parts, size_t stride, hipStream_t s) {
+    if (!x || parts < 1 || n % 4 || stride % 4 || (parts > 1 && stride < n)) return hipErrorInvalidValue;
+    if (parts == 1 || n == 0) return hipSuccess;
+    const size_t n4 = n / 4;
+    const unsigned blocks = (unsigned)((n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024);
+    hipLaunchKernelGGL(k_add_slabs, dim3(blocks), dim3(256), 0, s, x, n4, parts, stride / 4);
     return hipGetLastError();
 }
 
