@@ -302,8 +302,9 @@ hipError_t launch_rownorm(const float *src, int ld, float *dst, uint16_t *dstb, 
 }
 
 hipError_t launch_add_slabs(float *x, size_t n, int parts, size_t stride, hipStream_t s) {
-    if (!x || parts < 1 || n % 4 || stride % 4 || (parts > 1 && stride < n)) return hipErrorInvalidValue;
+    if (!x || parts < 1) return hipErrorInvalidValue;
     if (parts == 1 || n == 0) return hipSuccess;
+    if (n % 4 || stride % 4 || stride < n) return hipErrorInvalidValue;
     const size_t n4 = n / 4;
     const unsigned blocks = (unsigned)((n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024);
     hipLaunchKernelGGL(k_add_slabs, dim3(blocks), dim3(256), 0, s, x, n4, parts, stride / 4);
