@@ -202,3 +202,47 @@ def test_2b_batch_of_64_in_the_benchmark_shape(D):
         assert g.position(s) == lens[s] + 1
     say(f"2b batch of 64: worst |dlogit| over rows {sample}: {worst:.3e}")
     g.close()
+
+
+def test_2b_batch_past_64_rows(D):
+    """96 sequences in one call: the first passes run on more than 64 rows (the
+    128-row tile GEMMs, gate|up with SwiGLU in its epilogue and the sums of
+    squares per 64 indices), later passes on the prefix of rows still looping
+    (the few-row GEMMs, q|k|v|g split over K).  Sampled rows against the oracle
+    run on their sequences alone."""
+    import torch
+    cfg = synth.config("2b")
+    w = synth.make_weights(cfg)
+    nseq = 96
+    rng = np.random.default_rng(23)
+    lens = rng.integers(20, 600, nseq)
+    g = D.Dory(cfg, w, max_ctx=640, max_chunk=512, max_seqs=nseq)
+    n_ord = g.n_ord
+    rows = {}
+    for s in range(nseq):
+        k, v = synth.make_kv_rows(n_ord * int(lens[s]), cfg["nk"], cfg["hd"], cfg["hidden"], seed=400 + s)
+        shp = (n_ord, 1, int(lens[s]), cfg["nk"], cfg["hd"])
+        rows[s] = (k.reshape(shp), v.reshape(shp))
+        g.kv_load(rows[s][0], rows[s][1], "last_loop", 1, seq=s)
+    seqs = np.arange(nseq, dtype=np.int32)
+    toks = rng.integers(0, cfg["vocab"], nseq).astype(np.int32)
+    loops = synth.make_loops(nseq, seed=24)
+    say(f"2b batch of 96, loops {loops.min()}..{loops.max()}, rows looping at pass 2: {(loops >= 2).sum()}")
+    lg = g.forward_batch(seqs, toks, loops, "last_loop")
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy()
+    assert np.isfinite(lg).all()
+    sample = sorted({int(np.argmax(loops)), int(np.argmin(loops)), int(np.argmax(lens)), 0, 47, 95})
+    worst = 0.0
+    for s in sample:
+        o = O.Oracle(cfg, w, max_ctx=640)
+        o.kv_load(rows[s][0], rows[s][1], "last_loop", 1)
+        ol, _ = o.forward(toks[s:s + 1], int(loops[s]), "last_loop")
+        o.close()
+        d = float(np.abs(lg[s] - ol).max())
+        worst = max(worst, d)
+        assert d <= 5e-2, f"row {s} (context {lens[s]}, loops {loops[s]}): |dlogit| {d:.3e}"
+    for s in range(nseq):
+        assert g.position(s) == lens[s] + 1
+    say(f"2b batch of 96: worst |dlogit| over rows {sample}: {worst:.3e}")
+    g.close()
