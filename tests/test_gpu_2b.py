@@ -177,3 +177,17 @@ def test_2b_chunks_at_the_projection_edges(model2b, D):
     say("2b chunks of 16, 17, 64, 65 + 1 decode")
     check_pair(run_pair(g, o, calls, 2, "last_loop"), COS, DLOGIT, "2b projection edges")
     g.close()
+
+
+def test_2b_at_the_loop_maximum(model2b, D):
+    """loops = 16, the most a call takes: a 24-row prompt, then one-row calls
+    (the captured graph of 16 recurrent passes, replayed), every pass's
+    residual checked."""
+    cfg, w = model2b
+    toks = synth.make_tokens(27, cfg["vocab"], seq=18)
+    g = D.Dory(cfg, w, max_ctx=64, max_chunk=32)
+    o = O.Oracle(cfg, w, max_ctx=64)
+    calls = [toks[:24], toks[24:25], toks[25:26], toks[26:27]]
+    say("2b at loops 16: prompt 24 + 3 decode")
+    check_pair(run_pair(g, o, calls, 16, "last_loop"), COS, DLOGIT, "2b loops 16")
+    g.close()
