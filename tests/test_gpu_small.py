@@ -126,6 +126,21 @@ def test_tiny_matches_oracle(torch_mod, D, tiny, mode, split):
     g.close()
 
 
+@pytest.mark.parametrize("mode", ["last_loop", "per_loop"])
+def test_tiny_at_the_loop_maximum(torch_mod, D, tiny, mode):
+    """loops = 16 under both modes (per_loop: 16 cache slots per recurrent
+    layer, the most the slot table holds), a prompt in two calls then one-row
+    calls."""
+    cfg, w = tiny
+    toks = synth.make_tokens(60, cfg["vocab"], seq=3)
+    calls = [toks[:40], toks[40:41], toks[41:57], toks[57:58], toks[58:59], toks[59:]]
+    say(f"tiny {mode} loops 16")
+    g = D.Dory(cfg, w, max_ctx=128, max_chunk=64)
+    o = O.Oracle(cfg, w, max_ctx=128)
+    check_pair(run_pair(g, o, calls, 16, mode), 0.99999, 1e-3, f"tiny {mode} loops 16")
+    g.close()
+
+
 def test_tiny_q8_matches_oracle(torch_mod, D, tiny):
     cfg, w = tiny
     toks = synth.make_tokens(140, cfg["vocab"])
