@@ -145,6 +145,7 @@ def test_batch_errors_change_nothing(D):
         sq = np.asarray(seqs, np.int32); tk = np.zeros(len(seqs), np.int32); lp = np.asarray(loops, np.int32)
         return D.lib.dory_forward_batch(g.h, len(sq), sq.ctypes.data_as(C.c_void_p), tk.ctypes.data_as(C.c_void_p),
                                         lp.ctypes.data_as(C.c_void_p), D.MODES[mode], None, None)
+    assert rc([], []) == D.EINVAL                   # no row
     assert rc([0, 0], [1, 1]) == D.EINVAL           # a sequence twice
     assert rc([0, 4], [1, 1]) == D.EINVAL           # out of range
     assert rc([0, 1], [1, 17]) == D.EINVAL          # loops

@@ -179,6 +179,7 @@ def test_call_errors_change_nothing(torch_mod, D, tiny):
     ids = synth.make_tokens(8, cfg["vocab"])
     assert g.forward_rc(ids, 0, "per_loop") == D.EINVAL
     assert g.forward_rc(ids, 17, "per_loop") == D.EINVAL
+    assert g.forward_rc(np.zeros(0, np.int32), 2, "per_loop") == D.EINVAL    # no token
     assert g.forward_rc(ids, 2, 5) == D.EINVAL
     assert g.forward_rc(np.zeros(17, np.int32), 2, "per_loop") == D.ERANGE     # n > max_chunk
     assert g.position() == 0
