@@ -136,6 +136,27 @@ def test_2b_q8_batch_matches_oracle(D):
     g.close()
 
 
+def test_tiny_batch_ids_past_the_table(D):
+    """A batch whose rows carry ids at and past the vocabulary and negative
+    ones (read as unsigned): zero embedding rows, as in one-sequence calls."""
+    import torch
+    cfg = synth.config("tiny")
+    w = synth.make_weights(cfg)
+    g = D.Dory(cfg, w, max_ctx=64, max_chunk=16, max_seqs=4)
+    o = O.Oracle(cfg, w, max_ctx=64, max_seqs=4)
+    _prime(g, o, cfg, [5, 9, 12, 3], "last_loop")
+    toks = np.array([cfg["vocab"], cfg["vocab"] + 7, -1, 3], np.int32)
+    loops = np.array([2, 1, 3, 2], np.int32)
+    lg = g.forward_batch(np.arange(4, dtype=np.int32), toks, loops, "last_loop")
+    torch.cuda.synchronize()
+    lg = lg.cpu().numpy()
+    for s in range(4):
+        ol, _ = o.forward(toks[s:s + 1], int(loops[s]), "last_loop", seq=s)
+        d = float(np.abs(lg[s] - ol).max())
+        assert d <= 1e-3, f"row {s} (id {toks[s]}): |dlogit| {d:.3e}"
+    g.close()
+
+
 def test_batch_errors_change_nothing(D):
     cfg = synth.config("tiny")
     w = synth.make_weights(cfg)
