@@ -28,6 +28,14 @@
  *     pointers are ordinary CPU memory.
  *   - Calls on one handle must be serialised by the caller (one stream, or
  *     synchronised streams); the handle is not thread-safe.
+ *   - A failed call latches (kv_cache.rs `append`: a failed transition is
+ *     terminal until the sequence is cleared).  A forward or batch call that
+ *     fails after its first device work was enqueued latches its sequences; a
+ *     device error reported by a synchronisation inside the library latches
+ *     every sequence.  A latched sequence answers DORY_ESTATE to every call
+ *     (forward, batch row, rollback, taps, load) until dory_kv_reset.  Failed
+ *     argument checks and failures before any device work latch nothing.
+ *     A device fault that ends the process is beyond any latch.
  */
 #ifndef DORY_H
 #define DORY_H
@@ -40,7 +48,8 @@ extern "C" {
 
 #define DORY_OK 0
 #define DORY_EINVAL (-1)   /* bad argument or configuration */
-#define DORY_ESTATE (-2)   /* call disagrees with the sequence's state (kv mode, per_loop loop count) */
+#define DORY_ESTATE (-2)   /* call disagrees with the sequence's state (kv mode, per_loop loop count),
+                              or the sequence is latched after a failed call */
 #define DORY_ERANGE (-3)   /* n > max_chunk, position past max_ctx, a row no longer held */
 #define DORY_ENOMEM (-4)   /* device allocation failed */
 #define DORY_EDEVICE (-5)  /* a HIP call failed */
@@ -186,6 +195,16 @@ int dory_rollback(dory_t *h, int32_t seq, int64_t n);
 
 /* Next position of a sequence (rows held), or a negative status. */
 int64_t dory_position(const dory_t *h, int32_t seq);
+
+/* 1 if the sequence is latched after a failed call (see the conventions
+ * above), 0 if not, DORY_EINVAL for a bad handle or seq. */
+int dory_latched(const dory_t *h, int32_t seq);
+
+/* Test hook for the latch: the n-th kernel or graph launch the library makes
+ * from now on fails before it is launched (as if the runtime had refused it),
+ * with DORY_EDEVICE; the launches before it run normally.  n == 0 turns it off.
+ * Nothing faults on the device. */
+int dory_debug_fail_launch(dory_t *h, int64_t n);
 
 /* Test tap: later calls also write the residual state after every sub-layer pass
  * to buf, device fp32 [passes][n][hidden] with passes = n_in + n_rec*loops +

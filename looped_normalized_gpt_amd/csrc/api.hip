@@ -42,6 +42,12 @@ struct SeqState {
     uint32_t exit_tokens = 0;
     int64_t gate_tokens = 0, gate_one = 0;
     float last_top = -1.0f;
+    // kv_cache.rs `append`: a failed transition is terminal until the sequence is
+    // cleared.  Set when a call on the sequence fails after its first device
+    // work was enqueued, or when a synchronisation reports a device error (which
+    // no call can be blamed for alone: every sequence latches).  Every later
+    // call on the sequence returns DORY_ESTATE until dory_kv_reset.
+    bool latched = false;
 };
 
 constexpr int kStages = 32;
@@ -106,6 +112,9 @@ struct dory {
     bool last_chunk = false;
     int64_t last_pos0 = 0;
     int last_seq0 = 0;
+    // test hook (dory_debug_fail_launch): the fail_in-th launch from now fails
+    // before it is launched; 0 = off
+    int64_t fail_in = 0;
 };
 
 namespace {
@@ -120,6 +129,37 @@ int hip_fail(dory_t *h, hipError_t e, const char *what) {
     return fail(h, e == hipErrorOutOfMemory ? DORY_ENOMEM : DORY_EDEVICE,
                 std::string(what) + ": " + hipGetErrorString(e));
 }
+
+// A device error seen at a synchronisation may come from any work enqueued
+// before it: every sequence latches.
+int sync_fail(dory_t *h, hipError_t e, const char *what) {
+    for (SeqState &st : h->seqs) st.latched = true;
+    const int rc = hip_fail(h, e, what);
+    h->err += " (every sequence latched: dory_kv_reset clears it)";
+    return rc;
+}
+
+#define SYNCCHECK(h, call)                                    \
+    do {                                                      \
+        hipError_t e_ = (call);                               \
+        if (e_ != hipSuccess) return sync_fail(h, e_, #call); \
+    } while (0)
+
+// A call that failed after its first device work: its sequences latch.
+int latch(dory_t *h, int rc, const int32_t *seqs, int n) {
+    if (!rc) return rc;
+    for (int i = 0; i < n; ++i) h->seqs[seqs[i]].latched = true;
+    h->err += " (sequence latched until dory_kv_reset)";
+    return rc;
+}
+
+int latched_error(dory_t *h, const char *fn, int seq) {
+    return fail(h, DORY_ESTATE, std::string(fn) + ": sequence " + std::to_string(seq) +
+                                    " is latched after a failed call; dory_kv_reset clears it");
+}
+
+// The test hook: true when this launch is the one to fail.
+bool inject_failure(dory_t *h) { return h->fail_in > 0 && --h->fail_in == 0; }
 
 #define HIPCHECK(h, call)                                   \
     do {                                                    \
@@ -257,10 +297,11 @@ struct Enq {
     int o_ss_n = 0;
 };
 
-#define LAUNCH(call)                                            \
-    do {                                                        \
-        hipError_t e_ = (call);                                 \
-        if (e_ != hipSuccess) return hip_fail(q.h, e_, #call);  \
+#define LAUNCH(call)                                                                          \
+    do {                                                                                      \
+        if (inject_failure(q.h)) return hip_fail(q.h, hipErrorLaunchFailure, "(injected) " #call); \
+        hipError_t e_ = (call);                                                               \
+        if (e_ != hipSuccess) return hip_fail(q.h, e_, #call);                                \
     } while (0)
 
 uint8_t &froze_at(Enq &q, int seq, int ord, int slot) {
@@ -568,7 +609,7 @@ int enqueue(Enq &q) {
 int put_record(dory_t *h, const std::vector<RowRec> &rows, float *logits, hipStream_t s) {
     const int i = h->stage_i;
     h->stage_i = (i + 1) % kStages;
-    if (h->stage_used[i]) HIPCHECK(h, hipEventSynchronize(h->stage_ev[i]));
+    if (h->stage_used[i]) SYNCCHECK(h, hipEventSynchronize(h->stage_ev[i]));
     CallRec *r = reinterpret_cast<CallRec *>(h->stage + (size_t)i * h->rec_sz);
     r->n = (int32_t)rows.size();
     r->logits = logits;
@@ -805,6 +846,7 @@ int replay(dory_t *h, std::tuple<int, int, int> key, const Enq &q, bool top, hip
         if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
         it = h->graphs.emplace(key, ex).first;
     }
+    if (inject_failure(h)) return hip_fail(h, hipErrorLaunchFailure, "(injected) hipGraphLaunch");
     HIPCHECK(h, hipGraphLaunch(it->second, s));
     return DORY_OK;
 }
@@ -841,7 +883,7 @@ int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, 
         HIPCHECK(h, launch_top_prob(h->rec, h->V, h->gtop, s));
     }
     HIPCHECK(h, hipMemcpyAsync(h->gtop_host, h->gtop, sizeof(float), hipMemcpyDeviceToHost, s));
-    HIPCHECK(h, hipStreamSynchronize(s));
+    SYNCCHECK(h, hipStreamSynchronize(s));
     const float tp = *h->gtop_host;
     const bool stay = tp < h->gate_th;
     st.last_top = tp;
@@ -884,6 +926,7 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
     if (kv_mode != DORY_PER_LOOP && kv_mode != DORY_LAST_LOOP)
         return fail(h, DORY_EINVAL, "dory_forward_chunk: kv_mode must be per_loop or last_loop");
     SeqState &st = h->seqs[seq];
+    if (st.latched) return latched_error(h, "dory_forward_chunk", seq);
     if (st.mode >= 0 && st.mode != kv_mode)
         return fail(h, DORY_ESTATE, "dory_forward_chunk: kv mode changed without dory_kv_reset");
     if (kv_mode == DORY_PER_LOOP && st.loops > 0 && st.loops != loops)
@@ -905,7 +948,8 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
     if (gated) {
         int rc0 = ensure_slots(h, seq, kv_mode, 2);
         if (rc0) return rc0;
-        if (exit_probe(st)) return gated_readout(h, seq, tokens, reinterpret_cast<hipStream_t>(stream), logits);
+        if (exit_probe(st))
+            return latch(h, gated_readout(h, seq, tokens, reinterpret_cast<hipStream_t>(stream), logits), &seq, 1);
         loops = 2;  // no read-out: both passes, then the output block once
     }
     all = all && n > 1;  // one row: its logits are the last row's
@@ -915,37 +959,13 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens, st.q8_frozen, all);
     rc = put_record(h, rows, logits, s);
-    if (rc) return rc;
+    if (rc) return latch(h, rc, &seq, 1);
     Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
     q.want_all = all;
     // (q8_2f: once the fields froze, a one-row call launches no freeze)
     const bool graphable = n == 1 && (!h->q8 || st.q8_frozen);
-    if (graphable) {
-        auto key = std::make_tuple(loops, kv_mode, seq);
-        auto it = h->graphs.find(key);
-        if (it == h->graphs.end()) {
-            Enq cq = q;
-            cq.s = h->cap_stream;
-            HIPCHECK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
-            rc = enqueue(cq);
-            hipGraph_t g = nullptr;
-            hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
-            if (rc) {
-                if (g) (void)hipGraphDestroy(g);
-                return rc;
-            }
-            if (e != hipSuccess) return hip_fail(h, e, "hipStreamEndCapture");
-            hipGraphExec_t ex = nullptr;
-            e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-            (void)hipGraphDestroy(g);
-            if (e != hipSuccess) return hip_fail(h, e, "hipGraphInstantiate");
-            it = h->graphs.emplace(key, ex).first;
-        }
-        HIPCHECK(h, hipGraphLaunch(it->second, s));
-    } else {
-        rc = enqueue(q);
-        if (rc) return rc;
-    }
+    rc = graphable ? replay(h, std::make_tuple(loops, kv_mode, seq), q, false, s) : enqueue(q);
+    if (rc) return latch(h, rc, &seq, 1);
     h->last_T = n;
     h->last_chunk = n > 1;
     h->last_loops = loops;
@@ -1021,6 +1041,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
         seen[sq] = 1;
         if (loops[i] < 1 || loops[i] > DORY_MAX_LOOPS) return fail(h, DORY_EINVAL, "dory_forward_batch: loops must be in 1..16");
         const SeqState &st = h->seqs[sq];
+        if (st.latched) return latched_error(h, "dory_forward_batch", sq);
         if (st.mode >= 0 && st.mode != kv_mode)
             return fail(h, DORY_ESTATE, "dory_forward_batch: kv mode changed without dory_kv_reset");
         if (kv_mode == DORY_PER_LOOP && st.loops > 0 && st.loops != loops[i])
@@ -1056,7 +1077,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     int rc = put_record(h, rows, logits, s);
-    if (rc) return rc;
+    if (rc) return latch(h, rc, seqs, nseq);
     const int lmax = loops[order[0]];
     Enq q = make_enq(h, s, nseq, lmax, kv_mode, true, logits != nullptr, rows);
     for (int i = 0; i < lmax; ++i) {
@@ -1065,7 +1086,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
         q.act[i] = a;
     }
     rc = enqueue(q);
-    if (rc) return rc;
+    if (rc) return latch(h, rc, seqs, nseq);
     h->last_T = nseq;
     h->last_seq0 = seqs[0];
     h->last_chunk = false;
@@ -1094,6 +1115,7 @@ int dory_rollback(dory_t *h, int32_t seq, int64_t n) {
     if (seq < 0 || seq >= h->cfg.max_seqs) return fail(h, DORY_EINVAL, "dory_rollback: seq out of range");
     if (n < 0) return fail(h, DORY_EINVAL, "dory_rollback: n must be >= 0");
     SeqState &st = h->seqs[seq];
+    if (st.latched) return latched_error(h, "dory_rollback", seq);
     if (n >= st.pos) return DORY_OK;
     // The next row, at position n, reads keys max(0, n - W + 1) .. n - 1; a
     // ring of cap rows still holds positions pos - cap .. pos - 1.
@@ -1112,6 +1134,18 @@ int64_t dory_position(const dory_t *h, int32_t seq) {
     return h->seqs[seq].pos;
 }
 
+int dory_debug_fail_launch(dory_t *h, int64_t n) {
+    if (!h) return DORY_EINVAL;
+    if (n < 0) return fail(h, DORY_EINVAL, "dory_debug_fail_launch: n must be >= 0");
+    h->fail_in = n;
+    return DORY_OK;
+}
+
+int dory_latched(const dory_t *h, int32_t seq) {
+    if (!h || seq < 0 || seq >= h->cfg.max_seqs) return DORY_EINVAL;
+    return h->seqs[seq].latched ? 1 : 0;
+}
+
 int dory_debug_tap(dory_t *h, float *buf, int64_t cap) {
     if (!h) return DORY_EINVAL;
     if (buf && cap <= 0) return fail(h, DORY_EINVAL, "dory_debug_tap: cap must be positive");
@@ -1124,6 +1158,7 @@ static int slot_check(dory_t *h, int32_t seq, int32_t ord, int32_t slot, const S
     if (!h) return DORY_EINVAL;
     if (seq < 0 || seq >= h->cfg.max_seqs || ord < 0 || ord >= h->n_ord || slot < 0 || slot >= kMaxLoops)
         return fail(h, DORY_EINVAL, "kv tap: seq, ordinal or slot out of range");
+    if (h->seqs[seq].latched) return latched_error(h, "kv tap", seq);
     const SlotDesc &d = h->tab_host[(seq * h->n_ord + ord) * kMaxLoops + slot];
     if (!d.k && !d.kc) return fail(h, DORY_EINVAL, "kv tap: slot not in use");
     *out = &d;
@@ -1138,7 +1173,7 @@ int dory_kv_read(dory_t *h, int32_t seq, int32_t ord, int32_t slot, int64_t pos,
     const int64_t held = h->seqs[seq].pos;
     if (pos < 0 || pos >= held || pos < held - d->cap) return fail(h, DORY_ERANGE, "dory_kv_read: row not held");
     HIPCHECK(h, hipSetDevice(h->device));
-    HIPCHECK(h, hipDeviceSynchronize());
+    SYNCCHECK(h, hipDeviceSynchronize());
     const size_t row = (size_t)(pos % d->cap);
     char *b = reinterpret_cast<char *>(host_out);
     const int hd = h->hd, nk = h->nk, ngk = h->ngk;
@@ -1167,7 +1202,7 @@ int dory_kv_field(dory_t *h, int32_t seq, int32_t ord, int32_t slot, float *kcol
     if (!h->q8) return fail(h, DORY_EINVAL, "dory_kv_field: the cache is not q8_2f");
     if (!h->seqs[seq].q8_frozen) return 0;
     HIPCHECK(h, hipSetDevice(h->device));
-    HIPCHECK(h, hipDeviceSynchronize());
+    SYNCCHECK(h, hipDeviceSynchronize());
     if (kcol) HIPCHECK(h, hipMemcpy(kcol, d->kcol, sizeof(float) * h->KV, hipMemcpyDeviceToHost));
     if (vcol) HIPCHECK(h, hipMemcpy(vcol, d->vcol, sizeof(float) * h->KV, hipMemcpyDeviceToHost));
     return 1;
@@ -1183,11 +1218,12 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
         return fail(h, DORY_EINVAL, "dory_kv_load: bad rows");
     if (n_slot < (kv_mode == DORY_PER_LOOP ? loops : 1))
         return fail(h, DORY_EINVAL, "dory_kv_load: n_slot below the slots the mode uses");
+    if (h->seqs[seq].latched) return latched_error(h, "dory_kv_load", seq);
     if (h->seqs[seq].pos != 0) return fail(h, DORY_ESTATE, "dory_kv_load: the sequence is not fresh");
     HIPCHECK(h, hipSetDevice(h->device));
     int rc = ensure_slots(h, seq, kv_mode, loops);
     if (rc) return rc;
-    HIPCHECK(h, hipDeviceSynchronize());
+    SYNCCHECK(h, hipDeviceSynchronize());
     const int chunk = std::min(h->cfg.max_chunk, std::min(h->cap_s, h->cap_f));
     const size_t row = h->KV;
     for (const LayerInfo &l : h->L) {
@@ -1225,7 +1261,7 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
                         froze = true;
                     }
                 }
-                HIPCHECK(h, hipDeviceSynchronize());
+                SYNCCHECK(h, hipDeviceSynchronize());
             }
         }
     }

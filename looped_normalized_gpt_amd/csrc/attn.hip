@@ -1245,13 +1245,6 @@ hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {
     return launch_hd(b, T, s);
 }
 
-int attn_chunk_block(int hd, int rep) { return hd == 128 && 128 % rep == 0 ? 128 / rep : 0; }
-
-int attn_dec_max_split(int hd, int steps) {
-    const int kb = 256 / (hd / 4);
-    return steps * kb < 256 ? steps * kb : 256;
-}
-
 hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s) {
     if (a.split <= 0 || a.split > attn_dec_max_split(a.hd, 16) || T <= 0) return hipErrorInvalidValue;
     AttnArgs b = a;

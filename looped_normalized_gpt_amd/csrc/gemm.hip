@@ -595,11 +595,6 @@ __global__ __launch_bounds__(256) void k_gemm_skinny(const uint16_t *__restrict_
 
 }  // namespace
 
-bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda) {
-    if (wtype != kBF16 || !have_bf16 || lda % 8) return true;
-    return !((M <= 64 && K % 128 == 0) || (M > 64 && K % 64 == 0) || (M >= 32 && K % 8 == 0));
-}
-
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &Wb, int N, int K,
                        float *C, int ldc, int M, hipStream_t s, int kparts, size_t pstride) {
     if (kparts < 1 || (kparts > 1 && !gemm_splits_ok(wtype, Ab != nullptr, M, K, kparts))) return hipErrorInvalidValue;
@@ -642,10 +637,6 @@ hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, c
     return hipGetLastError();
 }
 
-bool gemm_swiglu_ok(int wtype, int M, int F, int K, int lda) {
-    return wtype == kBF16 && M > 64 && F % 64 == 0 && K % 64 == 0 && lda % 8 == 0;
-}
-
 hipError_t launch_gemm_swiglu(const uint16_t *Ab, int lda, const void *wgate, const void *wup, int F, int K,
                               const float *sg, const float *su, uint16_t *zb, float *ssp, int M, hipStream_t s) {
     if (!gemm_swiglu_ok(kBF16, M, F, K, lda) || !Ab || !zb || !ssp) return hipErrorInvalidValue;
@@ -654,26 +645,6 @@ hipError_t launch_gemm_swiglu(const uint16_t *Ab, int lda, const void *wgate, co
     hipLaunchKernelGGL(k_gemm_mfma2<true>, grid, dim3(256), 0, s, Ab, lda, W, 2 * F, K, nullptr, 0, M, 1, (size_t)0,
                        sg, su, zb, ssp);
     return hipGetLastError();
-}
-
-bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts) {
-    if (wtype != kBF16 || !have_bf16 || kparts > kMaxKParts) return false;
-    if (M <= 64) return K % 128 == 0 && K / 128 >= kparts;     // k_gemm_skinny: K blocks dealt out
-    return K % (64 * kparts) == 0;
-}
-
-int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K) {
-    if (!gemm_splits_ok(wtype, have_bf16, M, K, 1)) return 1;
-    if (M <= 64) {  // about 256 workgroups of 64 weight rows, at least 4 K blocks each
-        const int tiles = (N + 63) / 64;
-        int S = 1;
-        while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K / 128 >= 4 * S * 2) S *= 2;
-        return S;
-    }
-    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
-    int S = 1;
-    while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K % (64 * S * 2) == 0 && K / (S * 2) >= 512) S *= 2;
-    return S;
 }
 
 }  // namespace dk

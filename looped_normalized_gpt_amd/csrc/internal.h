@@ -160,17 +160,38 @@ inline GemmW gemm_w(const void *w, int N) { return GemmW{{w, w, w, w}, {N, N, N,
 // to C + z * pstride, and the reader adds the kparts slabs.
 hipError_t launch_gemm(int wtype, const float *A, const uint16_t *Ab, int lda, const GemmW &W, int N, int K,
                        float *C, int ldc, int T, hipStream_t s, int kparts = 1, size_t pstride = 0);
-bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts);
+inline bool gemm_splits_ok(int wtype, bool have_bf16, int M, int K, int kparts) {
+    if (wtype != kBF16 || !have_bf16 || kparts > kMaxKParts) return false;
+    if (M <= 64) return K % 128 == 0 && K / 128 >= kparts;     // k_gemm_skinny: K blocks dealt out
+    return K % (64 * kparts) == 0;
+}
 // The MLP's gate | up projection of a multi-row call with SwiGLU in its
 // epilogue (bf16 weights, more than 64 rows, ffn a multiple of 64): zb [M][F]
 // bf16 = silu(a sg) (b su), ssp [M][F/64] the rows' sums of z^2 per 64 indices.
-bool gemm_swiglu_ok(int wtype, int M, int F, int K, int lda);
+inline bool gemm_swiglu_ok(int wtype, int M, int F, int K, int lda) {
+    return wtype == kBF16 && M > 64 && F % 64 == 0 && K % 64 == 0 && lda % 8 == 0;
+}
 hipError_t launch_gemm_swiglu(const uint16_t *Ab, int lda, const void *wgate, const void *wup, int F, int K,
                               const float *sg, const float *su, uint16_t *zb, float *ssp, int M, hipStream_t s);
 // Whether launch_gemm reads the fp32 A for this shape (else only the bf16 Ab).
-bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda);
+inline bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda) {
+    if (wtype != kBF16 || !have_bf16 || lda % 8) return true;
+    return !((M <= 64 && K % 128 == 0) || (M > 64 && K % 64 == 0) || (M >= 32 && K % 8 == 0));
+}
 // Split-K count that fills the chip with 128 x 128 tiles (1 where it does not apply).
-int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K);
+inline int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K) {
+    if (!gemm_splits_ok(wtype, have_bf16, M, K, 1)) return 1;
+    if (M <= 64) {  // about 256 workgroups of 64 weight rows, at least 4 K blocks each
+        const int tiles = (N + 63) / 64;
+        int S = 1;
+        while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K / 128 >= 4 * S * 2) S *= 2;
+        return S;
+    }
+    const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
+    int S = 1;
+    while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K % (64 * S * 2) == 0 && K / (S * 2) >= 512) S *= 2;
+    return S;
+}
 
 // Attention.
 struct PrepArgs {
@@ -230,10 +251,13 @@ hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
 hipError_t launch_attn_dec(const AttnArgs &a, int T, hipStream_t s);
 // Rows per block of the MFMA chunk attention for this geometry, or 0 when it
 // does not serve it (head dim other than 128).
-int attn_chunk_block(int hd, int rep);
+inline int attn_chunk_block(int hd, int rep) { return hd == 128 && 128 % rep == 0 ? 128 / rep : 0; }
 // Keys a decode workgroup takes at most for head dim hd with `steps` load
 // steps (8 or 16).
-int attn_dec_max_split(int hd, int steps);
+inline int attn_dec_max_split(int hd, int steps) {
+    const int kb = 256 / (hd / 4);
+    return steps * kb < 256 ? steps * kb : 256;
+}
 
 // q8_2f cache writes (kv_cache.rs `append` / `freeze_cols`).
 struct Q8WriteArgs {

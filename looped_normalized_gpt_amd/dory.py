@@ -65,6 +65,8 @@ def _load():
     L.dory_gate_stats.argtypes = [vp, i32, vp, vp, vp, vp]
     L.dory_position.argtypes = [vp, i32]
     L.dory_position.restype = i64
+    L.dory_latched.argtypes = [vp, i32]
+    L.dory_debug_fail_launch.argtypes = [vp, i64]
     L.dory_debug_tap.argtypes = [vp, vp, i64]
     L.dory_kv_read.argtypes = [vp, i32, i32, i32, i64, vp]
     L.dory_kv_field.argtypes = [vp, i32, i32, i32, vp, vp]
@@ -85,6 +87,21 @@ class DoryError(RuntimeError):
 
 def _ptr(t):
     return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _device_buffer(t, rows: int, cols: int, device, what: str):
+    """A caller's output tensor, checked before the library writes rows x cols
+    fp32 values through its pointer: contiguous float32 on the model's device
+    with at least that many elements (else DoryError EINVAL, nothing called)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise DoryError(EINVAL, f"{what}: expected a torch tensor, got {type(t).__name__}")
+    if t.dtype != torch.float32 or not t.is_contiguous() or t.device != device:
+        raise DoryError(EINVAL, f"{what}: needs a contiguous float32 tensor on {device} "
+                                f"(got {t.dtype}, contiguous={t.is_contiguous()}, {t.device})")
+    if t.numel() < rows * cols:
+        raise DoryError(EINVAL, f"{what}: {t.numel()} elements, the call writes {rows} x {cols}")
+    return t
 
 
 def _stream(stream):
@@ -176,7 +193,7 @@ class Dory:
         if logits is True:
             out = torch.empty(self.cfg["vocab"], dtype=torch.float32, device=self.device)
         elif logits is not None and logits is not False:
-            out = logits
+            out = _device_buffer(logits, 1, self.cfg["vocab"], self.device, "forward: logits")
         mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
         rc = lib.dory_forward_chunk(self.h, seq, tok.ctypes.data_as(C.c_void_p), int(tok.shape[0]), loops,
                                     mode, _stream(stream), _ptr(out))
@@ -221,7 +238,7 @@ class Dory:
         if logits is True:
             out = torch.empty((len(sq), self.cfg["vocab"]), dtype=torch.float32, device=self.device)
         elif logits is not None and logits is not False:
-            out = logits
+            out = _device_buffer(logits, len(sq), self.cfg["vocab"], self.device, "forward_batch: logits")
         mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
         rc = lib.dory_forward_batch(self.h, len(sq), sq.ctypes.data_as(C.c_void_p), tk.ctypes.data_as(C.c_void_p),
                                     lp.ctypes.data_as(C.c_void_p), mode, _stream(stream), _ptr(out))
@@ -232,8 +249,33 @@ class Dory:
         """Raw status of a call (error-path tests)."""
         tok = np.ascontiguousarray(tokens, dtype=np.int32)
         mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
+        if logits is not None:
+            _device_buffer(logits, 1, self.cfg["vocab"], self.device, "forward_rc: logits")
         return lib.dory_forward_chunk(self.h, seq, tok.ctypes.data_as(C.c_void_p), int(tok.shape[0]), loops,
                                       mode, _stream(None), _ptr(logits))
+
+    def batch_rc(self, seqs, tokens, loops, kv_mode="last_loop", logits=None):
+        """Raw status of a batched call (error-path tests)."""
+        sq = np.ascontiguousarray(seqs, dtype=np.int32)
+        tk = np.ascontiguousarray(tokens, dtype=np.int32)
+        lp = np.ascontiguousarray(loops, dtype=np.int32)
+        mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
+        if logits is not None:
+            _device_buffer(logits, len(sq), self.cfg["vocab"], self.device, "batch_rc: logits")
+        return lib.dory_forward_batch(self.h, len(sq), sq.ctypes.data_as(C.c_void_p), tk.ctypes.data_as(C.c_void_p),
+                                      lp.ctypes.data_as(C.c_void_p), mode, _stream(None), _ptr(logits))
+
+    def latched(self, seq: int = 0) -> bool:
+        """dory_latched: the sequence refuses calls until it is reset."""
+        rc = lib.dory_latched(self.h, seq)
+        if rc < 0:
+            self._check(rc)
+        return bool(rc)
+
+    def fail_launch(self, n: int):
+        """dory_debug_fail_launch: the n-th launch from now fails before it is
+        launched (0: off)."""
+        self._check(lib.dory_debug_fail_launch(self.h, n))
 
     def reset(self, seq: int = -1):
         self._check(lib.dory_kv_reset(self.h, seq))
@@ -247,6 +289,8 @@ class Dory:
 
     def set_tap(self, buf):
         """buf: device fp32 tensor (or None to turn the tap off)."""
+        if buf is not None:
+            _device_buffer(buf, 1, buf.numel(), self.device, "set_tap: buffer")
         self._tap = buf
         self._check(lib.dory_debug_tap(self.h, _ptr(buf), 0 if buf is None else buf.numel()))
 
