@@ -96,7 +96,8 @@ def _device_buffer(t, rows: int, cols: int, device, what: str):
     import torch
     if not isinstance(t, torch.Tensor):
         raise DoryError(EINVAL, f"{what}: expected a torch tensor, got {type(t).__name__}")
-    if t.dtype != torch.float32 or not t.is_contiguous() or t.device != device:
+    same = t.device.type == device.type and (device.index is None or t.device.index == device.index)
+    if t.dtype != torch.float32 or not t.is_contiguous() or not same:
         raise DoryError(EINVAL, f"{what}: needs a contiguous float32 tensor on {device} "
                                 f"(got {t.dtype}, contiguous={t.is_contiguous()}, {t.device})")
     if t.numel() < rows * cols:
@@ -121,6 +122,8 @@ class Dory:
         import torch
         self.cfg = dict(cfg)
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         kv = kv_encoding or cfg.get("kv_encoding", "f32")
         self.q8 = kv == "q8_2f"
         bf16 = cfg["weight_dtype"] == "bf16"

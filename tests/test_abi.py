@@ -92,3 +92,20 @@ def test_null_handles_and_encoder_arguments_are_rejected():
     assert lib.dory_q8_encode_rows(x, None, 1, 300, 32, x, x, None) == EINVAL   # n > 256
     assert lib.dory_q8_encode_rows(x, None, 1, 128, 16, x, x, None) == EINVAL   # group not 32 or >= n
     lib.dory_destroy(None)
+
+
+def test_binding_checks_output_tensors_before_the_call():
+    """The binding refuses a caller's output tensor that the library would
+    write past or misread (dtype, contiguity, device, size), before any call."""
+    import torch
+    from looped_normalized_gpt_amd.dory import DoryError, _device_buffer
+    dev = torch.device("cpu")
+    ok = torch.empty(2 * 10, dtype=torch.float32)
+    assert _device_buffer(ok, 2, 10, dev, "t") is ok
+    assert _device_buffer(torch.empty(30), 2, 10, dev, "t").numel() == 30
+    for bad in (torch.empty(19, dtype=torch.float32), torch.empty(20, dtype=torch.float64),
+                torch.empty(10, 4, dtype=torch.float32)[:, ::2], [0.0] * 20):
+        with pytest.raises(DoryError):
+            _device_buffer(bad, 2, 10, dev, "t")
+    with pytest.raises(DoryError):
+        _device_buffer(ok, 2, 10, torch.device("cuda", 0), "t")
