@@ -140,6 +140,26 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
 int dory_forward_chunk_all(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
                            int32_t loops, int32_t kv_mode, dory_stream_t stream, float *logits);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dory_forward_chunk for calls of up to 8 rows that allocates nothing.  Its
+ * kernels are the same; their scratch (activations, split partials, the call
+ * record) is a carve-out of a static device array of 16 MiB, one per GPU,
+ * held until the process ends, instead of the handle's buffers; no HIP graph
+ * is captured or replayed (the kernels are enqueued on stream each call).
+ * Every such call on a GPU shares that GPU's array and leaves its contents
+ * there: calls that overlap on one GPU -- any handle, any stream -- race, so
+ * the caller serialises them.  Besides dory_forward_chunk's checks:
+ * DORY_ERANGE for n > 8 or a geometry whose scratch for 8 rows exceeds the
+ * array (the message gives both sizes); DORY_EINVAL while the exit gate is on;
+ * DORY_ESTATE when a per_loop slot the call needs does not exist yet (an
+ * ordinary call with that loop count creates it); DORY_EDEVICE when the
+ * array's address could not be had on this device.  It calls no hipMalloc,
+ * hipFree or other allocating routine.  Afterwards dory_stage_bench needs an
+ * ordinary call first. */
+int dory_forward_chunk_noalloc(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
+                               int32_t loops, int32_t kv_mode, dory_stream_t stream, float *logits);
+
 /* dory.rs `prompt_loops` (0..16; 0, the default, turns it off): a last_loop
  * call that wants no logits (logits NULL; a batch with logits NULL, row by row)
  * runs min(loops, n) passes of the recurrent block, since only its cache rows

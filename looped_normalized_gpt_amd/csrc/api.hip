@@ -55,6 +55,29 @@ constexpr int64_t kHuge = (int64_t)1 << 62;
 
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// Per-call device scratch of the forward: activations, split partials and the
+// call record.  The ordinary entry points use the handle's own buffers (sized
+// for max_chunk rows at create); dory_forward_chunk_noalloc carves one out of
+// the library's static array.  A call's kernels take every pointer from here.
+struct Scratch {
+    float *hb[2];          // residual of pass k in hb[k % 2] [T][H]
+    float *inp;            // the loop's input [T][H]
+    float *o;              // output projections: kMaxKParts split-K slabs [T][H], o_stride apart
+    int64_t o_stride;
+    float *qkvg;           // q | k | v | g [T][2Q + 2KV]
+    float *qp;             // rotated, normed, scaled queries [T][Q]
+    float *z, *zn;         // gated attention output [T][Q]; its renormed copy (benchmark stage only)
+    float *ga;             // gate | up [T][2F]
+    float *un;             // SwiGLU output [T][F]
+    float *kstage;         // rotated, normed keys before the q8 encoder [T][KV]
+    float *st;             // batches: loop state of each row [T][H]
+    float *hlog;           // batches: head output before the scale [min(T, seqs)][V]
+    float *part;           // split-attention partials
+    float *zss, *uss, *ussp;  // sums of squares: z per (row, kv head); SwiGLU rows; per 64 ffn indices
+    uint16_t *xb, *znb, *unb; // bf16 copies of x, z, SwiGLU output (GEMM operands)
+    CallRec *rec;          // the call record
+};
+
 }  // namespace
 
 struct dory {
@@ -70,17 +93,12 @@ struct dory {
     int split_bs = 64, split_bf = 64, ms_bs = 1, ms_bf = 1;  // decode splits of batches
     int split_ds = 64, split_df = 64, ms_ds = 1, ms_df = 1;  // one-row calls: sliding, full layers
     int64_t win_s = 0, win_f = 0;
-    // device scratch
-    float *hb[2] = {nullptr, nullptr}, *inp = nullptr, *o = nullptr, *qkvg = nullptr, *qp = nullptr;
-    float *z = nullptr, *zn = nullptr, *ga = nullptr, *un = nullptr, *kstage = nullptr;
-    int64_t o_stride = 0;   // elements between the split-K slabs of o
-    uint16_t *xb = nullptr, *znb = nullptr, *unb = nullptr;  // bf16 copies of x, zn, un (GEMM operands)
-    float *part = nullptr, *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
-    float *zss = nullptr;  // multi-row attention: sums of squares of z per (row, kv head)
-    float *uss = nullptr;  // multi-row MLP: sums of squares of the SwiGLU rows
-    float *ussp = nullptr; // ... per 64 ffn indices, from the fused gate|up GEMM [max_chunk][ffn/64]
-    float *st = nullptr, *hlog = nullptr;  // batches: loop state of each row, head output before the scale
+    Scratch sc{};           // the per-call scratch of the ordinary entry points (sized for max_chunk rows)
+    float *rope_s = nullptr, *rope_f = nullptr, *ld_k = nullptr, *ld_v = nullptr;
     float *hlog_all = nullptr;  // every row's head output of a chunk [max_chunk][vocab] (allocated on first use)
+    void *noalloc = nullptr;    // the static scratch array of this handle's device (dory_forward_chunk_noalloc)
+    size_t noalloc_need = 0;    // bytes a call of kNoAllocRows rows needs of it
+    std::string noalloc_err;    // why the array's address could not be had, if so
     int prompt_loops = 0;       // dory.rs `prompt_loops`: 0 = off
     // dory.rs `Gate::Conf(th)`: one-row last_loop calls leave after one pass
     // when the read-out's top probability reaches gate_th
@@ -90,7 +108,6 @@ struct dory {
     float *glog = nullptr;      // read-out logits of a call that wants none [V]
     float *gtop = nullptr;      // the read-out's top probability (device)
     float *gtop_host = nullptr; // ... copied to pinned host memory
-    CallRec *rec = nullptr;
     SlotDesc *tab = nullptr;
     std::vector<SlotDesc> tab_host;
     std::vector<void *> allocs;
@@ -270,11 +287,62 @@ int ensure_slots(dory_t *h, int seq, int mode, int loops) {
     return DORY_OK;
 }
 
+// The slots a (mode, loops) call touches on seq are all allocated already.
+bool slots_ready(const dory_t *h, int seq, int mode, int loops) {
+    for (const LayerInfo &l : h->L) {
+        if (!l.attn) continue;
+        const int ns = (mode == DORY_PER_LOOP && l.rec) ? loops : 1;
+        for (int s = 0; s < ns; ++s) {
+            const SlotDesc &d = h->tab_host[(seq * h->n_ord + l.ord) * kMaxLoops + s];
+            if (!d.k && !d.kc) return false;
+        }
+    }
+    return true;
+}
+
+// Lays out the scratch of a one-sequence call of up to `rows` rows from base
+// (256-byte aligned pieces; base == nullptr only sizes it) and returns the
+// bytes it takes.  The batch-only buffers (loop state, head rows) are left
+// null: a one-sequence call reads neither.
+size_t carve_scratch(const dory_t *h, int rows, char *base, Scratch *out) {
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char *p = base ? base + off : nullptr;
+        off += (bytes + 255) / 256 * 256;
+        return p;
+    };
+    const size_t T = rows, H = h->H, Q = h->Q, KV = h->KV, F = h->F, rep = h->nh / h->nk;
+    Scratch sc{};
+    sc.hb[0] = (float *)take(4 * T * H);
+    sc.hb[1] = (float *)take(4 * T * H);
+    sc.inp = (float *)take(4 * T * H);
+    sc.o_stride = (int64_t)(T * H);
+    sc.o = (float *)take(4 * T * H * kMaxKParts);
+    sc.qkvg = (float *)take(4 * T * (2 * Q + 2 * KV));
+    sc.qp = (float *)take(4 * T * Q);
+    sc.z = (float *)take(4 * T * Q);
+    sc.zn = (float *)take(4 * T * Q);
+    sc.ga = (float *)take(4 * T * 2 * F);
+    sc.un = (float *)take(4 * T * F);
+    sc.kstage = (float *)take(4 * T * KV);
+    sc.part = (float *)take(4 * std::max((size_t)h->ms_dec, T * h->ms_pf) * h->nk * rep * (h->hd + 2));
+    sc.zss = (float *)take(4 * T * h->nk);
+    sc.uss = (float *)take(4 * T);
+    sc.ussp = h->F % 64 == 0 ? (float *)take(4 * T * (F / 64)) : nullptr;
+    sc.xb = (uint16_t *)take(2 * T * H);
+    sc.znb = (uint16_t *)take(2 * T * Q);
+    sc.unb = (uint16_t *)take(2 * T * F);
+    sc.rec = (CallRec *)take(rec_bytes(rows));
+    if (out) *out = sc;
+    return off;
+}
+
 // ------------------------------------------------------------------ enqueue
 
 struct Enq {
     dory_t *h;
     hipStream_t s;
+    const Scratch *sc;           // the call's scratch
     int T;                       // rows of the call
     int loops;                   // loops of its longest row
     int mode;
@@ -349,6 +417,7 @@ GemmW gateup_w(const dory_t *h, const dory_layer_weights &w) {
 // One attention sub-layer over the first M rows of the call.
 int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const float *x, int M) {
     dory_t *h = q.h;
+    const Scratch &sc = *q.sc;
     const int ld = 2 * h->Q + 2 * h->KV;
     const int slot = slot_of(h, l, q.mode, loop_i);
     const dory_layer_weights &w = l.w;
@@ -356,7 +425,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         GemvArgs a{};
         a.w[0] = w.wq; a.w[1] = w.wk; a.w[2] = w.wv; a.w[3] = w.wg;
         a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
-        a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = h->qkvg; a.rec = h->rec; a.hidden = h->H;
+        a.nseg = 4; a.N = ld; a.K = h->H; a.row = 0; a.rs = rs; a.y = sc.qkvg; a.rec = sc.rec; a.hidden = h->H;
         a.embed = h->w.embed; a.vocab = h->V;
         const int pro = q.embed_pass ? kProEmbed : rs.loop_op == kLoopNext ? kProResolveInp : kProResolve;
         LAUNCH(launch_gemv(h->wt, pro, kEpiStore, a, q.s));
@@ -372,19 +441,19 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
                 ++parts;
         }
         const size_t slab = (size_t)M * ld;
-        LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, qkvg_w(h, w), ld, h->H, h->qkvg, ld, M, q.s, parts, slab));
-        LAUNCH(launch_add_slabs(h->qkvg, slab, parts, slab, q.s));
+        LAUNCH(launch_gemm(h->wt, x, sc.xb, h->H, qkvg_w(h, w), ld, h->H, sc.qkvg, ld, M, q.s, parts, slab));
+        LAUNCH(launch_add_slabs(sc.qkvg, slab, parts, slab, q.s));
     }
     AttnArgs aa{};
-    aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = w.sg; aa.z = h->z; aa.part = h->part;
+    aa.qp = sc.qp; aa.qkvg = sc.qkvg; aa.sg = w.sg; aa.z = sc.z; aa.part = sc.part;
     aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l.ord; aa.slot = slot;
     aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
     aa.window = l.sliding ? h->win_s : h->win_f;
-    aa.q8 = h->q8; aa.rec = h->rec;
+    aa.q8 = h->q8; aa.rec = sc.rec;
     aa.rope = l.sliding ? h->rope_s : h->rope_f; aa.sq = w.sq;
     if (q.T > 1) {
-        aa.zb = h->znb;
-        aa.zss = h->zss;
+        aa.zb = sc.znb;
+        aa.zss = sc.zss;
     }
     if (q.T == 1 || q.batch) {
         // One new row per sequence: prep and the cache write are fused into the
@@ -394,7 +463,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
             for (int r = 0; r < M; ++r) {
                 uint8_t &fz = froze_at(q, q.seq[r], l.ord, slot);
                 if (q.pos[r] >= kWarmup && !q.q8f[r] && !fz) {
-                    LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, r, q.s));
+                    LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, sc.rec, r, q.s));
                     fz = 1;
                 }
             }
@@ -412,9 +481,9 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         // A chunk of one sequence: rows pos0 .. pos0+M-1.
         const int64_t pos0 = q.pos[0];
         PrepArgs pa{};
-        pa.qkvg = h->qkvg; pa.qp = h->qp; pa.kstage = h->q8 ? h->kstage : nullptr;
+        pa.qkvg = sc.qkvg; pa.qp = sc.qp; pa.kstage = h->q8 ? sc.kstage : nullptr;
         pa.rope = l.sliding ? h->rope_s : h->rope_f; pa.sq = w.sq; pa.tab = h->tab;
-        pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = h->rec;
+        pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = sc.rec;
         LAUNCH(launch_prep(pa, M, q.s));
         bool field = false;
         if (h->q8) {
@@ -424,9 +493,9 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
             uint8_t &fz = froze_at(q, q.seq[0], l.ord, slot);
             const bool frozen = q.q8f[0] || fz;
             Q8WriteArgs wa{};
-            wa.ksrc = h->kstage; wa.kld = h->KV; wa.vsrc = h->qkvg + h->Q + h->KV; wa.vld = ld;
+            wa.ksrc = sc.kstage; wa.kld = h->KV; wa.vsrc = sc.qkvg + h->Q + h->KV; wa.vld = ld;
             wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = slot; wa.nk = h->nk; wa.hd = h->hd;
-            wa.rec = h->rec;
+            wa.rec = sc.rec;
             if (frozen) {
                 wa.r0 = 0; wa.r1 = M; wa.field = 1;
                 LAUNCH(launch_q8_write(wa, q.s));
@@ -437,7 +506,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
                 const int split = (int)(kWarmup - pos0);
                 wa.r0 = 0; wa.r1 = split; wa.field = 0;
                 LAUNCH(launch_q8_write(wa, q.s));
-                LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, h->rec, 0, q.s));
+                LAUNCH(launch_q8_freeze(h->tab, h->n_ord, l.ord, slot, h->nk, h->hd, sc.rec, 0, q.s));
                 wa.r0 = split; wa.r1 = M; wa.field = 1;
                 LAUNCH(launch_q8_write(wa, q.s));
                 fz = 1;
@@ -451,16 +520,16 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
     if (q.T == 1) {
         GemvArgs a{};
         a.w[0] = w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.row = 0;
-        a.src = h->z; a.y = h->o; a.rec = h->rec; a.hidden = h->H;
+        a.src = sc.z; a.y = sc.o; a.rec = sc.rec; a.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, a, q.s));
     } else {
         // the projection runs on z as the merge left it (fp32 and bf16); the
         // renorm before it is a per-row factor the next residual step applies
         const int S = gemm_pick_splits(h->wt, true, M, h->H, h->Q);
-        LAUNCH(launch_gemm(h->wt, h->z, h->znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, h->o, h->H, M, q.s, S,
-                           h->o_stride));
+        LAUNCH(launch_gemm(h->wt, sc.z, sc.znb, h->Q, gemm_w(w.wo, h->H), h->H, h->Q, sc.o, h->H, M, q.s, S,
+                           sc.o_stride));
         q.o_parts = S;
-        q.o_ss = h->zss;
+        q.o_ss = sc.zss;
         q.o_ss_n = h->nk;
     }
     return DORY_OK;
@@ -469,35 +538,36 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
 // One MLP sub-layer over the first M rows of the call.
 int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M) {
     dory_t *h = q.h;
+    const Scratch &sc = *q.sc;
     const dory_layer_weights &w = l.w;
     if (q.T == 1) {
         GemvArgs a{};
         a.w[0] = w.wgate; a.w[1] = w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H; a.row = 0;
-        a.rs = rs; a.y = h->ga; a.sg = w.sg; a.su = w.su; a.rec = h->rec; a.hidden = h->H;
+        a.rs = rs; a.y = sc.ga; a.sg = w.sg; a.su = w.su; a.rec = sc.rec; a.hidden = h->H;
         a.embed = h->w.embed; a.vocab = h->V;
         const int pro = q.embed_pass ? kProEmbed : rs.loop_op == kLoopNext ? kProResolveInp : kProResolve;
         LAUNCH(launch_gemv(h->wt, pro, kEpiPair, a, q.s));
         GemvArgs d{};
         d.w[0] = w.wdown; d.seg_end[0] = h->H; d.nseg = 1; d.N = h->H; d.K = h->F; d.row = 0;
-        d.src = h->ga; d.y = h->o; d.rec = h->rec; d.hidden = h->H;
+        d.src = sc.ga; d.y = sc.o; d.rec = sc.rec; d.hidden = h->H;
         LAUNCH(launch_gemv(h->wt, kProNorm, kEpiStore, d, q.s));
     } else {
         // the renorm before the down projection becomes a per-row factor the
         // next residual step applies (the projection is linear)
-        const bool fused = h->ussp && gemm_swiglu_ok(h->wt, M, h->F, h->H, h->H) &&
+        const bool fused = sc.ussp && gemm_swiglu_ok(h->wt, M, h->F, h->H, h->H) &&
                            !gemm_reads_fp32_a(h->wt, true, M, h->F, h->F);
         if (fused) {  // SwiGLU in the GEMM's epilogue: z in bf16, sums of squares per 64 indices
-            LAUNCH(launch_gemm_swiglu(h->xb, h->H, w.wgate, w.wup, h->F, h->H, w.sg, w.su, h->unb, h->ussp, M, q.s));
+            LAUNCH(launch_gemm_swiglu(sc.xb, h->H, w.wgate, w.wup, h->F, h->H, w.sg, w.su, sc.unb, sc.ussp, M, q.s));
         } else {
-            LAUNCH(launch_gemm(h->wt, x, h->xb, h->H, gateup_w(h, w), 2 * h->F, h->H, h->ga, 2 * h->F, M, q.s));
-            float *un = gemm_reads_fp32_a(h->wt, true, M, h->F, h->F) ? h->un : nullptr;
-            LAUNCH(launch_swiglu_norm(h->ga, h->ga + h->F, 2 * h->F, w.sg, w.su, un, h->unb, h->F, M, q.s, h->uss));
+            LAUNCH(launch_gemm(h->wt, x, sc.xb, h->H, gateup_w(h, w), 2 * h->F, h->H, sc.ga, 2 * h->F, M, q.s));
+            float *un = gemm_reads_fp32_a(h->wt, true, M, h->F, h->F) ? sc.un : nullptr;
+            LAUNCH(launch_swiglu_norm(sc.ga, sc.ga + h->F, 2 * h->F, w.sg, w.su, un, sc.unb, h->F, M, q.s, sc.uss));
         }
         const int S = gemm_pick_splits(h->wt, true, M, h->H, h->F);
-        LAUNCH(launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, h->o, h->H, M, q.s, S,
-                           h->o_stride));
+        LAUNCH(launch_gemm(h->wt, sc.un, sc.unb, h->F, gemm_w(w.wdown, h->H), h->H, h->F, sc.o, h->H, M, q.s, S,
+                           sc.o_stride));
         q.o_parts = S;
-        q.o_ss = fused ? h->ussp : h->uss;
+        q.o_ss = fused ? sc.ussp : sc.uss;
         q.o_ss_n = fused ? h->F / 64 : 1;
     }
     return DORY_OK;
@@ -510,11 +580,12 @@ int enq_mlp(Enq &q, const LayerInfo &l, const Resolve &rs, const float *x, int M
 // otherwise.  In a batch, loop i runs the first act[i] rows.
 int enqueue(Enq &q) {
     dory_t *h = q.h;
+    const Scratch &sc = *q.sc;
     const dory_config &c = h->cfg;
     const int T = q.T;
     // one-row calls: the first pass's GEMV gathers the embedding row itself
     if (q.k0 == 0 && T > 1)
-        LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, h->rec, T, h->hb[0], h->xb, q.s));
+        LAUNCH(launch_embed(h->wt, h->w.embed, h->V, h->H, sc.rec, T, sc.hb[0], sc.xb, q.s));
     const int P = passes(h, q.loops);
     auto rows_of = [&](int k) {
         if (k < c.n_in || k >= c.n_in + c.n_rec * q.loops) return T;
@@ -537,36 +608,36 @@ int enqueue(Enq &q) {
         }
         const int M = rows_of(k);
         Resolve rs{};
-        rs.inp = h->inp;
+        rs.inp = sc.inp;
         rs.loop_op = op;
         rs.o_parts = q.o_parts;
-        rs.o_stride = h->o_stride;
+        rs.o_stride = sc.o_stride;
         rs.o_ss = q.o_ss;
         rs.o_ss_n = q.o_ss_n;
-        rs.st = q.batch ? h->st : nullptr;
+        rs.st = q.batch ? sc.st : nullptr;
         rs.n_next = M;
         if (k == 0) {
             // the first pass takes the embedding as it is; o and alpha only need
             // to be valid addresses (the GEMV prologue loads them unconditionally).
             // One row: the GEMV gathers it and stores it as the residual.
-            rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0;
-            rs.h_out = T == 1 ? h->hb[0] : nullptr;
+            rs.h = sc.hb[0]; rs.o = sc.o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0;
+            rs.h_out = T == 1 ? sc.hb[0] : nullptr;
             rs.tap_pass = -1;
             rs.n_prev = T;
         } else if (k == q.k0) {
             // the early exit's second pass: e is the first pass's, as saved
-            rs.h = q.e0; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0;
-            rs.h_out = h->hb[k % 2]; rs.hb_out = h->xb; rs.tap_pass = -1;
+            rs.h = q.e0; rs.o = sc.o; rs.alpha = h->L[0].w.alpha; rs.slerp = 0;
+            rs.h_out = sc.hb[k % 2]; rs.hb_out = sc.xb; rs.tap_pass = -1;
             rs.n_prev = T;
         } else {
-            rs.h = h->hb[(k - 1) % 2]; rs.o = h->o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
-            rs.h_out = h->hb[k % 2]; rs.hb_out = h->xb; rs.tap_pass = k - 1;
+            rs.h = sc.hb[(k - 1) % 2]; rs.o = sc.o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
+            rs.h_out = sc.hb[k % 2]; rs.hb_out = sc.xb; rs.tap_pass = k - 1;
             rs.n_prev = rows_of(k - 1);
-            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, h->rec, q.s));
+            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, sc.rec, q.s));
         }
         if (op == kLoopExit && q.gate_save) rs.e_out = h->gst;
         const LayerInfo &l = h->L[li];
-        const float *x = h->hb[k % 2];
+        const float *x = sc.hb[k % 2];
         q.embed_pass = k == 0 && T == 1;
         int rc = l.attn ? enq_attn(q, l, loop_i, rs, x, M) : enq_mlp(q, l, rs, x, M);
         q.embed_pass = false;
@@ -575,38 +646,38 @@ int enqueue(Enq &q) {
     }
     Resolve rf{};
     rf.o_parts = q.o_parts;
-    rf.o_stride = h->o_stride;
+    rf.o_stride = sc.o_stride;
     rf.o_ss = q.o_ss;
     rf.o_ss_n = q.o_ss_n;
-    rf.h = h->hb[(P - 1) % 2]; rf.o = h->o; rf.alpha = h->L[prev_li].w.alpha; rf.slerp = 1;
-    rf.loop_op = kLoopNone; rf.inp = h->inp; rf.tap_pass = P - 1; rf.n_prev = rf.n_next = T;
+    rf.h = sc.hb[(P - 1) % 2]; rf.o = sc.o; rf.alpha = h->L[prev_li].w.alpha; rf.slerp = 1;
+    rf.loop_op = kLoopNone; rf.inp = sc.inp; rf.tap_pass = P - 1; rf.n_prev = rf.n_next = T;
     GemvArgs a{};
     a.w[0] = h->w.head; a.seg_end[0] = h->V; a.nseg = 1; a.N = h->V; a.K = h->H;
-    a.logit_scale = h->w.logit_scale; a.rec = h->rec; a.hidden = h->H;
+    a.logit_scale = h->w.logit_scale; a.rec = sc.rec; a.hidden = h->H;
     if (T == 1) {
         rf.h_out = nullptr;
         a.row = 0; a.rs = rf;
         LAUNCH(launch_gemv(h->wt, kProResolve, kEpiHead, a, q.s));
     } else {
-        rf.h_out = h->hb[P % 2];
-        rf.hb_out = h->xb;
-        LAUNCH(launch_resolve_rows(rf, h->H, T, h->rec, q.s));
+        rf.h_out = sc.hb[P % 2];
+        rf.hb_out = sc.xb;
+        LAUNCH(launch_resolve_rows(rf, h->H, T, sc.rec, q.s));
         if (q.want_logits && !q.batch && !q.want_all) {
-            a.row = T - 1; a.src = h->hb[P % 2];
+            a.row = T - 1; a.src = sc.hb[P % 2];
             LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));
         } else if (q.want_logits) {
             // every row: the head as a GEMM, then the logit scale into each
             // row's logits row (the record's `out`)
-            float *hl = q.want_all ? h->hlog_all : h->hlog;
-            LAUNCH(launch_gemm(h->wt, h->hb[P % 2], h->xb, h->H, gemm_w(h->w.head, h->V), h->V, h->H, hl, h->V, T, q.s));
-            LAUNCH(launch_logits_rows(hl, h->w.logit_scale, h->V, T, h->rec, q.s));
+            float *hl = q.want_all ? h->hlog_all : sc.hlog;
+            LAUNCH(launch_gemm(h->wt, sc.hb[P % 2], sc.xb, h->H, gemm_w(h->w.head, h->V), h->V, h->H, hl, h->V, T, q.s));
+            LAUNCH(launch_logits_rows(hl, h->w.logit_scale, h->V, T, sc.rec, q.s));
         }
     }
     return DORY_OK;
 }
 
-// Copies a call record to the device on stream s (pinned staging ring).
-int put_record(dory_t *h, const std::vector<RowRec> &rows, float *logits, hipStream_t s) {
+// Copies a call record to dst on the device on stream s (pinned staging ring).
+int put_record(dory_t *h, CallRec *dst, const std::vector<RowRec> &rows, float *logits, hipStream_t s) {
     const int i = h->stage_i;
     h->stage_i = (i + 1) % kStages;
     if (h->stage_used[i]) SYNCCHECK(h, hipEventSynchronize(h->stage_ev[i]));
@@ -615,7 +686,7 @@ int put_record(dory_t *h, const std::vector<RowRec> &rows, float *logits, hipStr
     r->logits = logits;
     r->tap = h->tap;
     memcpy(r->rows, rows.data(), sizeof(RowRec) * rows.size());
-    HIPCHECK(h, hipMemcpyAsync(h->rec, r, rec_used((int)rows.size()), hipMemcpyHostToDevice, s));
+    HIPCHECK(h, hipMemcpyAsync(dst, r, rec_used((int)rows.size()), hipMemcpyHostToDevice, s));
     HIPCHECK(h, hipEventRecord(h->stage_ev[i], s));
     h->stage_used[i] = true;
     return DORY_OK;
@@ -631,7 +702,7 @@ std::vector<RowRec> chunk_rows(int seq, int64_t pos0, int n, const int32_t *toke
 
 Enq make_enq(dory_t *h, hipStream_t s, int T, int loops, int mode, bool batch, bool want_logits,
              const std::vector<RowRec> &rows) {
-    Enq q{h, s, T, loops, mode, batch, want_logits, {}, {}, {}, {}};
+    Enq q{h, s, &h->sc, T, loops, mode, batch, want_logits, {}, {}, {}, {}};
     q.act.assign(loops, T);
     for (const RowRec &r : rows) {
         q.pos.push_back(r.pos);
@@ -734,38 +805,38 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     } while (0)
     CREATE_CHECK(hipGetDevice(&h->device));
     const size_t TH = (size_t)chunk * h->H;
-    CREATE_CHECK(dmalloc(h, &h->hb[0], TH));
-    CREATE_CHECK(dmalloc(h, &h->hb[1], TH));
-    CREATE_CHECK(dmalloc(h, &h->inp, TH));
-    h->o_stride = TH;
-    CREATE_CHECK(dmalloc(h, &h->o, TH * kMaxKParts));   // split-K slabs of the output projections
-    CREATE_CHECK(dmalloc(h, &h->qkvg, (size_t)chunk * (2 * h->Q + 2 * h->KV)));
-    CREATE_CHECK(dmalloc(h, &h->qp, (size_t)chunk * h->Q));
-    CREATE_CHECK(dmalloc(h, &h->z, (size_t)chunk * h->Q));
-    CREATE_CHECK(dmalloc(h, &h->zn, (size_t)chunk * h->Q));
-    CREATE_CHECK(dmalloc(h, &h->ga, (size_t)chunk * 2 * h->F));   // gate | up per row
-    CREATE_CHECK(dmalloc(h, &h->un, (size_t)chunk * h->F));
-    CREATE_CHECK(dmalloc(h, &h->xb, (size_t)chunk * h->H));
-    CREATE_CHECK(dmalloc(h, &h->znb, (size_t)chunk * h->Q));
-    CREATE_CHECK(dmalloc(h, &h->zss, (size_t)chunk * h->nk));
-    CREATE_CHECK(dmalloc(h, &h->uss, (size_t)chunk));
-    if (h->F % 64 == 0) CREATE_CHECK(dmalloc(h, &h->ussp, (size_t)chunk * (h->F / 64)));
-    CREATE_CHECK(dmalloc(h, &h->unb, (size_t)chunk * h->F));
-    CREATE_CHECK(dmalloc(h, &h->kstage, (size_t)chunk * h->KV));
+    CREATE_CHECK(dmalloc(h, &h->sc.hb[0], TH));
+    CREATE_CHECK(dmalloc(h, &h->sc.hb[1], TH));
+    CREATE_CHECK(dmalloc(h, &h->sc.inp, TH));
+    h->sc.o_stride = TH;
+    CREATE_CHECK(dmalloc(h, &h->sc.o, TH * kMaxKParts));   // split-K slabs of the output projections
+    CREATE_CHECK(dmalloc(h, &h->sc.qkvg, (size_t)chunk * (2 * h->Q + 2 * h->KV)));
+    CREATE_CHECK(dmalloc(h, &h->sc.qp, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->sc.z, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->sc.zn, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->sc.ga, (size_t)chunk * 2 * h->F));   // gate | up per row
+    CREATE_CHECK(dmalloc(h, &h->sc.un, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->sc.xb, (size_t)chunk * h->H));
+    CREATE_CHECK(dmalloc(h, &h->sc.znb, (size_t)chunk * h->Q));
+    CREATE_CHECK(dmalloc(h, &h->sc.zss, (size_t)chunk * h->nk));
+    CREATE_CHECK(dmalloc(h, &h->sc.uss, (size_t)chunk));
+    if (h->F % 64 == 0) CREATE_CHECK(dmalloc(h, &h->sc.ussp, (size_t)chunk * (h->F / 64)));
+    CREATE_CHECK(dmalloc(h, &h->sc.unb, (size_t)chunk * h->F));
+    CREATE_CHECK(dmalloc(h, &h->sc.kstage, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_k, (size_t)chunk * h->KV));
     CREATE_CHECK(dmalloc(h, &h->ld_v, (size_t)chunk * h->KV));
-    CREATE_CHECK(dmalloc(h, &h->st, TH));
-    CREATE_CHECK(dmalloc(h, &h->hlog, (size_t)std::min(chunk, cfg->max_seqs) * h->V));
+    CREATE_CHECK(dmalloc(h, &h->sc.st, TH));
+    CREATE_CHECK(dmalloc(h, &h->sc.hlog, (size_t)std::min(chunk, cfg->max_seqs) * h->V));
     const size_t rep = h->nh / h->nk;
     // decode rows (one per sequence of a batch) or the rows of a chunk
     const size_t dec_rows = std::min(chunk, cfg->max_seqs);
     const size_t part = std::max(dec_rows * h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2);
-    CREATE_CHECK(dmalloc(h, &h->part, part));
+    CREATE_CHECK(dmalloc(h, &h->sc.part, part));
     CREATE_CHECK(dmalloc(h, &h->tab, h->tab_host.size()));
     CREATE_CHECK(hipMemset(h->tab, 0, sizeof(SlotDesc) * h->tab_host.size()));
     char *recp = nullptr;
     CREATE_CHECK(dmalloc(h, &recp, h->rec_sz));
-    h->rec = reinterpret_cast<CallRec *>(recp);
+    h->sc.rec = reinterpret_cast<CallRec *>(recp);
     // RoPE tables for every position (dory.rs `stack`): inverse frequencies
     // theta^(-2j/hd) rounded to fp32, angle p * inv in f64, cos and sin rounded
     // to fp32; row p is [cos half | sin half].
@@ -789,6 +860,16 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     CREATE_CHECK(hipHostMalloc((void **)&h->stage, h->rec_sz * kStages, hipHostMallocDefault));
     for (int i = 0; i < kStages; ++i) CREATE_CHECK(hipEventCreateWithFlags(&h->stage_ev[i], hipEventDisableTiming));
     CREATE_CHECK(hipStreamCreateWithFlags(&h->cap_stream, hipStreamNonBlocking));
+    // the static scratch of dory_forward_chunk_noalloc: its address on this
+    // device (looked up once per device and kept); a failure only disables
+    // that entry point
+    {
+        void *p = nullptr;
+        const hipError_t e = noalloc_scratch(&p);
+        if (e == hipSuccess) h->noalloc = p;
+        else h->noalloc_err = std::string("the static scratch's address: ") + hipGetErrorString(e);
+        h->noalloc_need = carve_scratch(h, kNoAllocRows, nullptr, nullptr);
+    }
     // Every sequence's slot 0 of every attention layer; per_loop's further
     // slots come on the first per_loop call that needs them.
     for (int s = 0; s < cfg->max_seqs; ++s)
@@ -832,7 +913,7 @@ int replay(dory_t *h, std::tuple<int, int, int> key, const Enq &q, bool top, hip
         HIPCHECK(h, hipStreamBeginCapture(h->cap_stream, hipStreamCaptureModeThreadLocal));
         int rc = enqueue(cq);
         hipError_t e0 = hipSuccess;
-        if (!rc && top) e0 = launch_top_prob(h->rec, h->V, h->gtop, h->cap_stream);
+        if (!rc && top) e0 = launch_top_prob(q.sc->rec, h->V, h->gtop, h->cap_stream);
         hipGraph_t g = nullptr;
         hipError_t e = hipStreamEndCapture(h->cap_stream, &g);
         if (rc || e0 != hipSuccess) {
@@ -868,7 +949,7 @@ int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, 
     SeqState &st = h->seqs[seq];
     const std::vector<RowRec> rows = chunk_rows(seq, st.pos, 1, tokens, st.q8_frozen);
     float *lg = logits ? logits : h->glog;
-    int rc = put_record(h, rows, lg, s);
+    int rc = put_record(h, h->sc.rec, rows, lg, s);
     if (rc) return rc;
     Enq q = make_enq(h, s, 1, 1, DORY_LAST_LOOP, false, true, rows);
     q.gate_save = true;
@@ -880,7 +961,7 @@ int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, 
     } else {
         rc = enqueue(q);
         if (rc) return rc;
-        HIPCHECK(h, launch_top_prob(h->rec, h->V, h->gtop, s));
+        HIPCHECK(h, launch_top_prob(h->sc.rec, h->V, h->gtop, s));
     }
     HIPCHECK(h, hipMemcpyAsync(h->gtop_host, h->gtop, sizeof(float), hipMemcpyDeviceToHost, s));
     SYNCCHECK(h, hipStreamSynchronize(s));
@@ -915,7 +996,7 @@ int gated_readout(dory_t *h, int32_t seq, const int32_t *tokens, hipStream_t s, 
 // dory_forward_chunk (all = false: logits of the last row, or none) and
 // dory_forward_chunk_all (every row's logits).
 int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
-                  dory_stream_t stream, float *logits, bool all) {
+                  dory_stream_t stream, float *logits, bool all, bool noalloc = false) {
     if (!h) return DORY_EINVAL;
     const dory_config &c = h->cfg;
     if (seq < 0 || seq >= c.max_seqs) return fail(h, DORY_EINVAL, "dory_forward_chunk: seq out of range");
@@ -933,6 +1014,16 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
         return fail(h, DORY_ESTATE, "dory_forward_chunk: per_loop needs the same loop count on every call");
     if (st.pos + n > c.max_ctx) return fail(h, DORY_ERANGE, "dory_forward_chunk: position past max_ctx");
     if (all && !logits) return fail(h, DORY_EINVAL, "dory_forward_chunk_all: logits must not be null");
+    if (noalloc) {
+        if (n > kNoAllocRows)
+            return fail(h, DORY_ERANGE, "dory_forward_chunk_noalloc: n > " + std::to_string(kNoAllocRows));
+        if (h->gate_on) return fail(h, DORY_EINVAL, "dory_forward_chunk_noalloc: takes no exit gate");
+        if (!h->noalloc) return fail(h, DORY_EDEVICE, "dory_forward_chunk_noalloc: " + h->noalloc_err);
+        if (h->noalloc_need > kNoAllocBytes)
+            return fail(h, DORY_ERANGE, "dory_forward_chunk_noalloc: this geometry needs " +
+                                            std::to_string(h->noalloc_need) + " bytes of scratch, the static array holds " +
+                                            std::to_string(kNoAllocBytes));
+    }
     // dory.rs `stack`: under the gate a one-row call runs one pass, a read-out
     // when the exit rate asks for one, and a second pass unless it exits
     const bool gated = n == 1 && h->gate_on;
@@ -954,11 +1045,33 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
     }
     all = all && n > 1;  // one row: its logits are the last row's
     if (all && !h->hlog_all) HIPCHECK(h, dmalloc(h, &h->hlog_all, (size_t)c.max_chunk * h->V));
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (noalloc) {
+        // no allocation, no graph: the slots must exist, the kernels run over a
+        // carve-out of the static array, the record goes there too
+        if (!slots_ready(h, seq, kv_mode, loops))
+            return fail(h, DORY_ESTATE, "dory_forward_chunk_noalloc: a per_loop slot this call needs is not "
+                                        "allocated yet (an ordinary call with this loop count allocates it)");
+        Scratch sc{};
+        carve_scratch(h, kNoAllocRows, reinterpret_cast<char *>(h->noalloc), &sc);
+        const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens, st.q8_frozen);
+        int rc = put_record(h, sc.rec, rows, logits, s);
+        if (rc) return latch(h, rc, &seq, 1);
+        Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
+        q.sc = &sc;
+        rc = enqueue(q);
+        if (rc) return latch(h, rc, &seq, 1);
+        h->last_T = 0;  // the stage benchmark reads the handle's scratch: not this call's
+        if (h->q8 && st.pos + n > kWarmup) st.q8_frozen = true;
+        st.pos += n;
+        st.mode = kv_mode;
+        if (kv_mode == DORY_PER_LOOP) st.loops = loops;
+        return DORY_OK;
+    }
     int rc = ensure_slots(h, seq, kv_mode, loops);
     if (rc) return rc;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const std::vector<RowRec> rows = chunk_rows(seq, st.pos, n, tokens, st.q8_frozen, all);
-    rc = put_record(h, rows, logits, s);
+    rc = put_record(h, h->sc.rec, rows, logits, s);
     if (rc) return latch(h, rc, &seq, 1);
     Enq q = make_enq(h, s, n, loops, kv_mode, false, logits != nullptr, rows);
     q.want_all = all;
@@ -990,6 +1103,11 @@ int dory_forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n,
 int dory_forward_chunk_all(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops, int32_t kv_mode,
                            dory_stream_t stream, float *logits) {
     return forward_chunk(h, seq, tokens, n, loops, kv_mode, stream, logits, true);
+}
+
+int dory_forward_chunk_noalloc(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int32_t loops,
+                               int32_t kv_mode, dory_stream_t stream, float *logits) {
+    return forward_chunk(h, seq, tokens, n, loops, kv_mode, stream, logits, false, true);
 }
 
 int dory_set_gate(dory_t *h, int32_t on, float threshold) {
@@ -1076,7 +1194,7 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
         rows[r] = RowRec{h->seqs[seqs[i]].pos, seqs[i], tokens[i], i, h->seqs[seqs[i]].q8_frozen ? 1 : 0};
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    int rc = put_record(h, rows, logits, s);
+    int rc = put_record(h, h->sc.rec, rows, logits, s);
     if (rc) return latch(h, rc, seqs, nseq);
     const int lmax = loops[order[0]];
     Enq q = make_enq(h, s, nseq, lmax, kv_mode, true, logits != nullptr, rows);
@@ -1235,18 +1353,18 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
             bool froze = false;
             for (int64_t p0 = 0; p0 < npos; p0 += chunk) {
                 const int T = (int)std::min<int64_t>(chunk, npos - p0);
-                rc = put_record(h, chunk_rows(seq, p0, T, nullptr), nullptr, nullptr);
+                rc = put_record(h, h->sc.rec, chunk_rows(seq, p0, T, nullptr), nullptr, nullptr);
                 if (rc) return rc;
                 HIPCHECK(h, hipMemcpy(h->ld_k, kb + p0 * row, sizeof(float) * T * row, hipMemcpyHostToDevice));
                 HIPCHECK(h, hipMemcpy(h->ld_v, vb + p0 * row, sizeof(float) * T * row, hipMemcpyHostToDevice));
                 if (!h->q8) {
                     HIPCHECK(h, launch_kv_store(h->ld_k, h->ld_v, h->tab, h->n_ord, l.ord, s, h->nk, h->hd, T,
-                                                h->rec, nullptr));
+                                                h->sc.rec, nullptr));
                 } else {
                     Q8WriteArgs wa{};
                     wa.ksrc = h->ld_k; wa.kld = h->KV; wa.vsrc = h->ld_v; wa.vld = h->KV;
                     wa.tab = h->tab; wa.n_ord = h->n_ord; wa.ord = l.ord; wa.slot = s; wa.nk = h->nk; wa.hd = h->hd;
-                    wa.rec = h->rec;
+                    wa.rec = h->sc.rec;
                     const bool frozen = froze || p0 >= kWarmup + 1;
                     if (frozen || p0 + T <= kWarmup) {
                         wa.r0 = 0; wa.r1 = T; wa.field = frozen;
@@ -1255,7 +1373,7 @@ int dory_kv_load(dory_t *h, int32_t seq, int32_t kv_mode, int32_t loops, int64_t
                         const int split = (int)(kWarmup - p0);
                         wa.r0 = 0; wa.r1 = split; wa.field = 0;
                         HIPCHECK(h, launch_q8_write(wa, nullptr));
-                        HIPCHECK(h, launch_q8_freeze(h->tab, h->n_ord, l.ord, s, h->nk, h->hd, h->rec, 0, nullptr));
+                        HIPCHECK(h, launch_q8_freeze(h->tab, h->n_ord, l.ord, s, h->nk, h->hd, h->sc.rec, 0, nullptr));
                         wa.r0 = split; wa.r1 = T; wa.field = 1;
                         HIPCHECK(h, launch_q8_write(wa, nullptr));
                         froze = true;
@@ -1294,26 +1412,26 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
     for (int i = 0; i < reps; ++i) {
         const LayerInfo *l = ls[i % ls.size()];
         Resolve rs{};
-        rs.h = h->hb[0]; rs.o = h->o; rs.alpha = h->L[0].w.alpha; rs.slerp = 1; rs.loop_op = kLoopNone;
-        rs.inp = h->inp; rs.h_out = nullptr; rs.tap_pass = -1;
+        rs.h = h->sc.hb[0]; rs.o = h->sc.o; rs.alpha = h->L[0].w.alpha; rs.slerp = 1; rs.loop_op = kLoopNone;
+        rs.inp = h->sc.inp; rs.h_out = nullptr; rs.tap_pass = -1;
         GemvArgs a{};
-        a.rec = h->rec; a.hidden = h->H; a.row = 0; a.rs = rs;
+        a.rec = h->sc.rec; a.hidden = h->H; a.row = 0; a.rs = rs;
         AttnArgs aa{};
         if (stage == 1 || stage == 10) {
-            aa.qp = h->qp; aa.qkvg = h->qkvg; aa.sg = l->w.sg; aa.z = h->z; aa.part = h->part;
+            aa.qp = h->sc.qp; aa.qkvg = h->sc.qkvg; aa.sg = l->w.sg; aa.z = h->sc.z; aa.part = h->sc.part;
             aa.tab = h->tab; aa.n_ord = h->n_ord; aa.ord = l->ord;
             aa.slot = slot_of(h, *l, h->last_mode, 0);
             aa.nh = h->nh; aa.nk = h->nk; aa.hd = h->hd;
             aa.window = l->sliding ? h->win_s : h->win_f;
             aa.rope = l->sliding ? h->rope_s : h->rope_f; aa.sq = l->w.sq; aa.no_write = 1;
-            aa.q8 = h->q8; aa.rec = h->rec;
+            aa.q8 = h->q8; aa.rec = h->sc.rec;
         }
         hipError_t e = hipSuccess;
         switch (stage) {
         case 0:
             a.w[0] = l->w.wq; a.w[1] = l->w.wk; a.w[2] = l->w.wv; a.w[3] = l->w.wg;
             a.seg_end[0] = h->Q; a.seg_end[1] = h->Q + h->KV; a.seg_end[2] = h->Q + 2 * h->KV; a.seg_end[3] = ld;
-            a.nseg = 4; a.N = ld; a.K = h->H; a.y = h->qkvg;
+            a.nseg = 4; a.N = ld; a.K = h->H; a.y = h->sc.qkvg;
             e = launch_gemv(h->wt, kProResolve, kEpiStore, a, s);
             break;
         case 1:
@@ -1324,16 +1442,16 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_attn_dec(aa, h->last_T, s);
             break;
         case 2:
-            a.w[0] = l->w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.src = h->z; a.y = h->o;
+            a.w[0] = l->w.wo; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->Q; a.src = h->sc.z; a.y = h->sc.o;
             e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);
             break;
         case 3:
             a.w[0] = l->w.wgate; a.w[1] = l->w.wup; a.seg_end[0] = h->F; a.nseg = 1; a.N = h->F; a.K = h->H;
-            a.y = h->ga; a.sg = l->w.sg; a.su = l->w.su;
+            a.y = h->sc.ga; a.sg = l->w.sg; a.su = l->w.su;
             e = launch_gemv(h->wt, kProResolve, kEpiPair, a, s);
             break;
         case 4:
-            a.w[0] = l->w.wdown; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->F; a.src = h->ga; a.y = h->o;
+            a.w[0] = l->w.wdown; a.seg_end[0] = h->H; a.nseg = 1; a.N = h->H; a.K = h->F; a.src = h->sc.ga; a.y = h->sc.o;
             e = launch_gemv(h->wt, kProNorm, kEpiStore, a, s);
             break;
         case 5:
@@ -1342,22 +1460,22 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             e = launch_gemv(h->wt, kProResolve, kEpiHead, a, s);
             break;
         case 6:
-            e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, qkvg_w(h, l->w), ld, h->H, h->qkvg, ld, MC, s);
+            e = launch_gemm(h->wt, h->sc.hb[0], h->sc.xb, h->H, qkvg_w(h, l->w), ld, h->H, h->sc.qkvg, ld, MC, s);
             break;
         case 7:
-            e = launch_gemm(h->wt, h->zn, h->znb, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->o, h->H, MC, s,
-                            gemm_pick_splits(h->wt, true, MC, h->H, h->Q), h->o_stride);
+            e = launch_gemm(h->wt, h->sc.zn, h->sc.znb, h->Q, gemm_w(l->w.wo, h->H), h->H, h->Q, h->sc.o, h->H, MC, s,
+                            gemm_pick_splits(h->wt, true, MC, h->H, h->Q), h->sc.o_stride);
             break;
         case 8:
-            if (h->ussp && gemm_swiglu_ok(h->wt, MC, h->F, h->H, h->H))
-                e = launch_gemm_swiglu(h->xb, h->H, l->w.wgate, l->w.wup, h->F, h->H, l->w.sg, l->w.su, h->unb,
-                                       h->ussp, MC, s);
+            if (h->sc.ussp && gemm_swiglu_ok(h->wt, MC, h->F, h->H, h->H))
+                e = launch_gemm_swiglu(h->sc.xb, h->H, l->w.wgate, l->w.wup, h->F, h->H, l->w.sg, l->w.su, h->sc.unb,
+                                       h->sc.ussp, MC, s);
             else
-                e = launch_gemm(h->wt, h->hb[0], h->xb, h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->ga, 2 * h->F, MC, s);
+                e = launch_gemm(h->wt, h->sc.hb[0], h->sc.xb, h->H, gateup_w(h, l->w), 2 * h->F, h->H, h->sc.ga, 2 * h->F, MC, s);
             break;
         case 9:
-            e = launch_gemm(h->wt, h->un, h->unb, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->o, h->H, MC, s,
-                            gemm_pick_splits(h->wt, true, MC, h->H, h->F), h->o_stride);
+            e = launch_gemm(h->wt, h->sc.un, h->sc.unb, h->F, gemm_w(l->w.wdown, h->H), h->H, h->F, h->sc.o, h->H, MC, s,
+                            gemm_pick_splits(h->wt, true, MC, h->H, h->F), h->sc.o_stride);
             break;
         default:
             chunk_split(h, h->last_pos0, h->last_T, aa);

@@ -11,6 +11,9 @@ constexpr int kWarmup = 64;     // kv_cache.rs `KV_COL_WARMUP`: rows before the 
 constexpr int kMaxKParts = 8;  // split-K slabs of the multi-row output projections
 constexpr int kKGroup = 32;     // kv_cache.rs `KV_K_GROUP`: K channels per q8 scale
 constexpr float kEps = 1e-6f;   // dory.rs `EPS`: justnorm's epsilon
+// dory_forward_chunk_noalloc: rows a call may carry, bytes of the static scratch
+constexpr int kNoAllocRows = 8;
+constexpr size_t kNoAllocBytes = (size_t)16 << 20;
 
 // One row of a call: its position, its sequence (which selects the cache
 // slots), its token, and where its logits go.
@@ -143,6 +146,10 @@ hipError_t launch_top_prob(const CallRec *rec, int V, float *out, hipStream_t s)
 // Batches: logits[rows[r].out][v] = hlog[r][v] * logit_scale[v].
 hipError_t launch_logits_rows(const float *hlog, const float *logit_scale, int V, int T, const CallRec *rec,
                               hipStream_t s);
+
+// The device address of the static scratch array on the current GPU (looked up
+// once per device, then cached): kNoAllocBytes bytes, 256-byte aligned.
+hipError_t noalloc_scratch(void **ptr);
 
 // Weights of a GEMM as up to 4 row segments stacked along N: output column n
 // reads row n - seg_end[i-1] of w[i] for seg_end[i-1] <= n < seg_end[i].

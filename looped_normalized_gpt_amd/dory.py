@@ -60,6 +60,7 @@ def _load():
     L.dory_kv_reset.argtypes = [vp, i32]
     L.dory_rollback.argtypes = [vp, i32, i64]
     L.dory_forward_chunk_all.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
+    L.dory_forward_chunk_noalloc.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
     L.dory_set_prompt_loops.argtypes = [vp, i32]
     L.dory_set_gate.argtypes = [vp, i32, C.c_float]
     L.dory_gate_stats.argtypes = [vp, i32, vp, vp, vp, vp]
@@ -202,6 +203,17 @@ class Dory:
                                     mode, _stream(stream), _ptr(out))
         self._check(rc)
         return out
+
+    def forward_noalloc(self, tokens, loops: int, kv_mode="last_loop", seq: int = 0, logits=None, stream=None):
+        """dory_forward_chunk_noalloc (up to 8 rows, nothing allocated by the
+        library): ``logits`` is a caller's device fp32 tensor [vocab] or None."""
+        tok = np.ascontiguousarray(tokens, dtype=np.int32)
+        if logits is not None:
+            _device_buffer(logits, 1, self.cfg["vocab"], self.device, "forward_noalloc: logits")
+        mode = MODES[kv_mode] if isinstance(kv_mode, str) else kv_mode
+        self._check(lib.dory_forward_chunk_noalloc(self.h, seq, tok.ctypes.data_as(C.c_void_p), int(tok.shape[0]),
+                                                   loops, mode, _stream(stream), _ptr(logits)))
+        return logits
 
     def forward_all(self, tokens, loops: int, kv_mode="last_loop", seq: int = 0, stream=None):
         """One call with the logits of every row (dory_forward_chunk_all):
@@ -358,3 +370,4 @@ def q8_encode_rows(x, col, group: int, stream=None):
     if rc != OK:
         raise DoryError(rc, lib.dory_last_error(None).decode())
     return codes, scales
+

@@ -346,6 +346,12 @@ void fake_print_violations(FILE *f) {
 
 namespace dk {
 
+hipError_t noalloc_scratch(void **ptr) {
+    static void *p = fake::alloc(kNoAllocBytes, "static scratch");
+    *ptr = p;
+    return p ? hipSuccess : hipErrorOutOfMemory;
+}
+
 hipError_t launch_gemv(int wt, int pro, int epi, const GemvArgs &a, hipStream_t s) {
     if (a.K <= 0 || a.K > 8192 || a.K % 8 || a.N <= 0) return hipErrorInvalidValue;
     if (pro == kProEmbed && (!a.embed || a.vocab <= 0)) return hipErrorInvalidValue;

@@ -327,6 +327,35 @@ void selftest() {
     printf("selftest: %ld violations reported, as planted\n", fake_violations());
 }
 
+// The no-allocation variant: short calls of both modes over the static array,
+// interleaved with ordinary calls on another sequence, every extent inside it.
+void noalloc_case(const Geo &g, int max_ctx) {
+    Model m(g, max_ctx, 64, 2);
+    std::vector<int32_t> t(8, 5);
+    for (int mode : {DORY_LAST_LOOP, DORY_PER_LOOP}) {
+        expect(dory_kv_reset(m.h, -1) == 0, "reset");
+        expect(m.chunk(0, 8, 3, mode, true) == 0, "an ordinary call creates the slots", m.h);
+        for (int n : {8, 3, 1, 1, 7}) {
+            expect(dory_forward_chunk_noalloc(m.h, 0, t.data(), n, 3, mode, nullptr, m.logits) == 0, "noalloc", m.h);
+            expect(m.chunk(1, n, 3, mode, true) == 0, "ordinary call between", m.h);
+        }
+        expect(dory_forward_chunk_noalloc(m.h, 0, t.data(), 9, 3, mode, nullptr, m.logits) == DORY_ERANGE, "9 rows");
+        expect(dory_forward_chunk_noalloc(m.h, 0, t.data(), 2, 3, mode, nullptr, m.logits) == 0, "noalloc", m.h);
+        expect(dory_stage_bench(m.h, 0, 2, nullptr) == DORY_ESTATE, "the stage benchmark needs an ordinary call");
+    }
+    expect(dory_kv_reset(m.h, -1) == 0, "reset");
+    expect(m.chunk(0, 4, 2, DORY_PER_LOOP, true) == 0, "per_loop at loops 2", m.h);
+    expect(dory_kv_reset(m.h, 0) == 0, "reset");
+    expect(dory_forward_chunk_noalloc(m.h, 0, t.data(), 2, 5, DORY_PER_LOOP, nullptr, m.logits) == DORY_ESTATE,
+           "per_loop slots that do not exist yet", m.h);
+}
+void noalloc() {
+    noalloc_case(gtiny(), 512);
+    noalloc_case(gtiny(true), 512);
+    noalloc_case(g2b(), 4400);
+    noalloc_case(g2b(true, 8192), 40000);
+}
+
 struct Entry {
     const char *name;
     void (*fn)();
@@ -334,7 +363,7 @@ struct Entry {
 const Entry kScenarios[] = {
     {"decode2b", decode2b}, {"q8_2b", q8_2b}, {"prefill2b", prefill2b}, {"batch2b", batch2b},
     {"gate2b", gate2b},     {"tiny", tiny},   {"tiny_q8", tiny_q8},     {"pages", pages},
-    {"shapes2b", shapes2b}, {"shapes2b_q8", shapes2b_q8}, {"latch", latch},
+    {"shapes2b", shapes2b}, {"shapes2b_q8", shapes2b_q8}, {"latch", latch}, {"noalloc", noalloc},
 };
 
 }  // namespace
