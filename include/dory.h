@@ -232,6 +232,16 @@ int dory_debug_fail_launch(dory_t *h, int64_t n);
  * DORY_EINVAL.  buf == NULL turns the tap off. */
 int dory_debug_tap(dory_t *h, float *buf, int64_t cap);
 
+/* Test tap: later calls also write, for every attention sub-layer pass and
+ * every row, the cache row the pass appends before it is stored or encoded:
+ * the rotated, unit-normed key, then the value -- device fp32
+ * [attention passes][n][2][nk*hd], where the attention passes of a call are
+ * those of its walk in order (n_in's, then each loop's, then n_out's).  cap is
+ * buf's size in floats; a call that needs more fails with DORY_EINVAL; gated
+ * calls take no tap.  buf == NULL turns it off.  (A q8_2f cache's codes and
+ * scales are checked bit for bit against these rows.) */
+int dory_debug_kv_tap(dory_t *h, float *buf, int64_t cap);
+
 /* Test tap: copies one stored cache row of (sequence, attention ordinal, slot)
  * at position pos to host memory, after synchronising the device.
  * Layout -- fp32 cache: K [nk][hd] then V [nk][hd] floats (8*nk*hd bytes);

@@ -121,6 +121,8 @@ struct dory {
     std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;  // one-row calls by (loops, kv mode, sequence)
     float *tap = nullptr;
     int64_t tap_cap = 0;
+    float *kvtap = nullptr;  // test tap of the pre-encode cache rows (dory_debug_kv_tap)
+    int64_t kvtap_cap = 0;
     std::vector<SeqState> seqs;
     std::string err;
     int device = 0;
@@ -196,6 +198,14 @@ hipError_t dmalloc(dory_t *h, T **p, size_t count) {
 }
 
 int passes(const dory_t *h, int loops) { return h->cfg.n_in + h->cfg.n_rec * loops + h->cfg.n_out; }
+
+// Attention sub-layer passes of a call of `loops` loops.
+int attn_passes(const dory_t *h, int loops) {
+    int n = 0;
+    for (const LayerInfo &l : h->L)
+        if (l.attn) n += l.rec ? loops : 1;
+    return n;
+}
 
 int check_config(const dory_config *c, const dory_weights *w) {
     auto bad = [](const std::string &m) { return fail(nullptr, DORY_EINVAL, "dory_create: " + m); };
@@ -360,6 +370,7 @@ struct Enq {
     bool embed_pass = false;     // this pass's GEMV gathers the embedding row itself (one-row calls)
     int k0 = 0;
     const float *e0 = nullptr;
+    int attn_pass = 0;           // attention passes enqueued so far (the kv tap's index)
     int o_parts = 1;             // split-K slabs of o the last output projection wrote
     const float *o_ss = nullptr; // multi-row attention: per-row partial sums of |z|^2 scaling o
     int o_ss_n = 0;
@@ -451,6 +462,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
     aa.window = l.sliding ? h->win_s : h->win_f;
     aa.q8 = h->q8; aa.rec = sc.rec;
     aa.rope = l.sliding ? h->rope_s : h->rope_f; aa.sq = w.sq;
+    aa.tap_pass = q.attn_pass++;
     if (q.T > 1) {
         aa.zb = sc.znb;
         aa.zss = sc.zss;
@@ -484,6 +496,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         pa.qkvg = sc.qkvg; pa.qp = sc.qp; pa.kstage = h->q8 ? sc.kstage : nullptr;
         pa.rope = l.sliding ? h->rope_s : h->rope_f; pa.sq = w.sq; pa.tab = h->tab;
         pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = sc.rec;
+        pa.tap_pass = aa.tap_pass;
         LAUNCH(launch_prep(pa, M, q.s));
         bool field = false;
         if (h->q8) {
@@ -685,6 +698,7 @@ int put_record(dory_t *h, CallRec *dst, const std::vector<RowRec> &rows, float *
     r->n = (int32_t)rows.size();
     r->logits = logits;
     r->tap = h->tap;
+    r->kvtap = h->kvtap;
     memcpy(r->rows, rows.data(), sizeof(RowRec) * rows.size());
     HIPCHECK(h, hipMemcpyAsync(dst, r, rec_used((int)rows.size()), hipMemcpyHostToDevice, s));
     HIPCHECK(h, hipEventRecord(h->stage_ev[i], s));
@@ -1029,12 +1043,14 @@ int forward_chunk(dory_t *h, int32_t seq, const int32_t *tokens, int32_t n, int3
     const bool gated = n == 1 && h->gate_on;
     if (gated && kv_mode != DORY_LAST_LOOP)
         return fail(h, DORY_EINVAL, "dory_forward_chunk: the exit gate works on the last_loop cache");
-    if (gated && h->tap) return fail(h, DORY_EINVAL, "dory_forward_chunk: gated calls take no tap");
+    if (gated && (h->tap || h->kvtap)) return fail(h, DORY_EINVAL, "dory_forward_chunk: gated calls take no tap");
     // dory.rs `chunk_loops`: a last_loop call whose logits nobody reads keeps
     // only its cache rows and runs at most prompt_loops passes
     if (!logits && kv_mode == DORY_LAST_LOOP && h->prompt_loops > 0) loops = std::min(loops, h->prompt_loops);
     if (h->tap && (int64_t)passes(h, loops) * n * h->H > h->tap_cap)
         return fail(h, DORY_EINVAL, "dory_forward_chunk: the tap buffer is too small for this call");
+    if (h->kvtap && (int64_t)attn_passes(h, loops) * n * 2 * h->KV > h->kvtap_cap)
+        return fail(h, DORY_EINVAL, "dory_forward_chunk: the kv tap buffer is too small for this call");
     HIPCHECK(h, hipSetDevice(h->device));
     if (gated) {
         int rc0 = ensure_slots(h, seq, kv_mode, 2);
@@ -1178,6 +1194,12 @@ int dory_forward_batch(dory_t *h, int32_t nseq, const int32_t *seqs, const int32
         if ((int64_t)passes(h, lmax) * nseq * h->H > h->tap_cap)
             return fail(h, DORY_EINVAL, "dory_forward_batch: the tap buffer is too small for this call");
     }
+    if (h->kvtap) {
+        int lmax = 0;
+        for (int i = 0; i < nseq; ++i) lmax = std::max(lmax, (int)loops[i]);
+        if ((int64_t)attn_passes(h, lmax) * nseq * 2 * h->KV > h->kvtap_cap)
+            return fail(h, DORY_EINVAL, "dory_forward_batch: the kv tap buffer is too small for this call");
+    }
     if (nseq == 1) return dory_forward_chunk(h, seqs[0], tokens, 1, loops[0], kv_mode, stream, logits);
     HIPCHECK(h, hipSetDevice(h->device));
     for (int i = 0; i < nseq; ++i) {
@@ -1262,6 +1284,14 @@ int dory_debug_fail_launch(dory_t *h, int64_t n) {
 int dory_latched(const dory_t *h, int32_t seq) {
     if (!h || seq < 0 || seq >= h->cfg.max_seqs) return DORY_EINVAL;
     return h->seqs[seq].latched ? 1 : 0;
+}
+
+int dory_debug_kv_tap(dory_t *h, float *buf, int64_t cap) {
+    if (!h) return DORY_EINVAL;
+    if (buf && cap <= 0) return fail(h, DORY_EINVAL, "dory_debug_kv_tap: cap must be positive");
+    h->kvtap = buf;
+    h->kvtap_cap = buf ? cap : 0;
+    return DORY_OK;
 }
 
 int dory_debug_tap(dory_t *h, float *buf, int64_t cap) {

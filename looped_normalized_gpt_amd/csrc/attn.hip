@@ -40,6 +40,19 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
         }
     }
     const float f = norm_factor(wave_sum(s));
+    if (!isq && a.rec->kvtap) {  // test tap: the row's key and value before the cache write
+        float *t = a.rec->kvtap + ((size_t)a.tap_pass * a.rec->n + r) * 2 * KV + kh * hd;
+        const float *vs = a.qkvg + (size_t)r * ld + Q + KV + kh * hd;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int j = lane + 64 * i;
+            if (j < half) {
+                t[j] = nx[i] * f;
+                t[j + half] = ny[i] * f;
+            }
+        }
+        for (int j = lane; j < hd; j += 64) t[KV + j] = vs[j];
+    }
     if (isq) {
         float *dst = a.qp + (size_t)r * Q + hh * hd;
         const float *sq = a.sq + hh * hd;
@@ -569,6 +582,13 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
                 sd.v[row * HD + d] = vn[d];
             }
         }
+        if (rec->kvtap) {  // test tap: the new row's key and value before the cache write
+            float *t = rec->kvtap + ((size_t)a.tap_pass * rec->n + r) * 2 * KV + (size_t)kh * HD;
+            for (int d = tid; d < HD; d += 256) {
+                t[d] = qs[REP][d];
+                t[KV + d] = vn[d];
+            }
+        }
         const int el = len - 1;
         if (g == el % KB) {
 #pragma unroll
@@ -802,6 +822,11 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         } else if (!a.no_write && tid < HD) {
             sd.k[row * HD + tid] = qs[REP][tid];
             sd.v[row * HD + tid] = vn[tid];
+        }
+        if (rec->kvtap && tid < HD) {  // test tap: the new row's key and value before the cache write
+            float *t = rec->kvtap + ((size_t)a.tap_pass * rec->n + r) * 2 * KV + (size_t)kh * HD;
+            t[tid] = qs[REP][tid];
+            t[KV + tid] = vn[tid];
         }
         const int el = len - 1;
         if (g == el % 8) {

@@ -34,6 +34,10 @@ struct CallRec {
     int32_t pad;
     float *logits;     // device [.][vocab] or null
     float *tap;        // device [passes][n][hidden] or null
+    // test tap: the pre-encode cache rows of every attention pass, device
+    // [attention passes][n][2][nk * hd] (the rotated, normed key, then the
+    // value) or null
+    float *kvtap;
     RowRec rows[1];    // [max(max_chunk, max_seqs)]
 };
 inline size_t rec_bytes(int rows) { return sizeof(CallRec) + sizeof(RowRec) * (rows - 1); }
@@ -211,6 +215,7 @@ struct PrepArgs {
     int32_t n_ord, ord, slot;
     int32_t nh, nk, hd;
     const CallRec *rec;
+    int32_t tap_pass;    // the call's attention pass (for the record's kvtap)
 };
 hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s);
 
@@ -249,6 +254,7 @@ struct AttnArgs {
     const SlotDesc *sd1;
     int32_t dec;         // 1: the decode kernel (launch_attn_dec), whose merge reads all
                          // max_split slabs of a row; 0: the multi-row kernels
+    int32_t tap_pass;    // decode kernels: the call's attention pass (for the record's kvtap)
 };
 // Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);

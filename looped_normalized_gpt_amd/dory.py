@@ -69,6 +69,7 @@ def _load():
     L.dory_latched.argtypes = [vp, i32]
     L.dory_debug_fail_launch.argtypes = [vp, i64]
     L.dory_debug_tap.argtypes = [vp, vp, i64]
+    L.dory_debug_kv_tap.argtypes = [vp, vp, i64]
     L.dory_kv_read.argtypes = [vp, i32, i32, i32, i64, vp]
     L.dory_kv_field.argtypes = [vp, i32, i32, i32, vp, vp]
     L.dory_kv_load.argtypes = [vp, i32, i32, i32, i64, i32, vp, vp]
@@ -308,6 +309,19 @@ class Dory:
             _device_buffer(buf, 1, buf.numel(), self.device, "set_tap: buffer")
         self._tap = buf
         self._check(lib.dory_debug_tap(self.h, _ptr(buf), 0 if buf is None else buf.numel()))
+
+    def set_kv_tap(self, buf):
+        """dory_debug_kv_tap: buf a device fp32 tensor [attention passes][n][2][KV],
+        or None to turn the tap off."""
+        if buf is not None:
+            _device_buffer(buf, 1, buf.numel(), self.device, "set_kv_tap: buffer")
+        self._kvtap = buf
+        self._check(lib.dory_debug_kv_tap(self.h, _ptr(buf), 0 if buf is None else buf.numel()))
+
+    def attn_passes(self, loops: int) -> int:
+        c = self.cfg
+        return sum((loops if c["n_in"] <= i < c["n_in"] + c["n_rec"] else 1)
+                   for i, ch in enumerate(c["pattern"]) if ch != "-")
 
     def row_bytes(self) -> int:
         nk, hd = self.cfg["nk"], self.cfg["hd"]

@@ -543,6 +543,8 @@ hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
             const RowRec &row = a.rec->rows[r];
             need("RoPE row", a.rope + (size_t)row.pos * a.hd, (size_t)a.hd * 4);
             if (!a.kstage) fake::slot(a.tab, row.seq, a.n_ord, a.ord, a.slot, a.nk, a.hd, false);
+            if (a.rec->kvtap)
+                need("kv tap", a.rec->kvtap + ((size_t)a.tap_pass * a.rec->n + r) * 2 * KV, (size_t)2 * KV * 4);
         }
     };
     return fake::launch("launch_prep", stat, dyn);
@@ -580,6 +582,8 @@ static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool d
                     fake::violation("the graph's slot belongs to another sequence than the record's row");
             }
             if (dec) need("RoPE row", a.rope + (size_t)p * a.hd, (size_t)a.hd * 4);
+            if (dec && rec->kvtap)
+                need("kv tap", rec->kvtap + ((size_t)a.tap_pass * rec->n + r) * 2 * KV, (size_t)2 * KV * 4);
             const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
             const int64_t nkeys = p - lo + 1;
             if (dec || a.blk == 0) {

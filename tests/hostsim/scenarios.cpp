@@ -349,6 +349,41 @@ void noalloc_case(const Geo &g, int max_ctx) {
     expect(dory_forward_chunk_noalloc(m.h, 0, t.data(), 2, 5, DORY_PER_LOOP, nullptr, m.logits) == DORY_ESTATE,
            "per_loop slots that do not exist yet", m.h);
 }
+// The kv tap, sized exactly for each call: every writer stays inside it.
+void kvtap_case(const Geo &g) {
+    Model m(g, 600, 128, 3);
+    const int KV = g.nk * g.hd;
+    auto attn_passes = [&](int loops) {
+        int n = 0;
+        for (int i = 0; i < (int)g.pattern.size(); ++i)
+            if (g.pattern[i] != '-') n += (i >= g.n_in && i < g.n_in + g.n_rec) ? loops : 1;
+        return n;
+    };
+    for (int mode : {DORY_LAST_LOOP, DORY_PER_LOOP}) {
+        expect(dory_kv_reset(m.h, -1) == 0, "reset");
+        for (int n : {100, 1, 1, 33}) {
+            const size_t cap = (size_t)attn_passes(3) * n * 2 * KV;
+            float *buf = (float *)fake_alloc(cap * 4, "kv tap");
+            expect(dory_debug_kv_tap(m.h, buf, (int64_t)cap) == 0, "kv tap", m.h);
+            expect(m.chunk(0, n, 3, mode, true) == 0, "tapped call", m.h);
+            expect(dory_debug_kv_tap(m.h, buf, (int64_t)cap - 1) == 0, "kv tap", m.h);
+            expect(m.chunk(0, n, 3, mode, true) == DORY_EINVAL, "a tap one float short", m.h);
+        }
+        for (int s = 1; s < 3; ++s) expect(m.chunk(s, 5, 3, mode, false) == 0, "set-up", m.h);
+        const size_t cap = (size_t)attn_passes(3) * 3 * 2 * KV;
+        float *buf = (float *)fake_alloc(cap * 4, "kv tap");
+        expect(dory_debug_kv_tap(m.h, buf, (int64_t)cap) == 0, "kv tap", m.h);
+        expect(m.batch({0, 1, 2}, {3, 3, 3}, mode, true) == 0, "tapped batch", m.h);
+        if (mode == DORY_LAST_LOOP) expect(m.batch({2, 0, 1}, {1, 3, 2}, mode, true) == 0, "tapped batch", m.h);
+        expect(dory_debug_kv_tap(m.h, nullptr, 0) == 0, "kv tap off", m.h);
+    }
+}
+void kvtap() {
+    kvtap_case(gtiny());
+    kvtap_case(gtiny(true));
+    kvtap_case(g2b(true, 300));
+}
+
 void noalloc() {
     noalloc_case(gtiny(), 512);
     noalloc_case(gtiny(true), 512);
@@ -363,7 +398,7 @@ struct Entry {
 const Entry kScenarios[] = {
     {"decode2b", decode2b}, {"q8_2b", q8_2b}, {"prefill2b", prefill2b}, {"batch2b", batch2b},
     {"gate2b", gate2b},     {"tiny", tiny},   {"tiny_q8", tiny_q8},     {"pages", pages},
-    {"shapes2b", shapes2b}, {"shapes2b_q8", shapes2b_q8}, {"latch", latch}, {"noalloc", noalloc},
+    {"shapes2b", shapes2b}, {"shapes2b_q8", shapes2b_q8}, {"latch", latch}, {"noalloc", noalloc}, {"kvtap", kvtap},
 };
 
 }  // namespace

@@ -191,3 +191,22 @@ def test_2b_at_the_loop_maximum(model2b, D):
     say("2b at loops 16: prompt 24 + 3 decode")
     check_pair(run_pair(g, o, calls, 16, "last_loop"), COS, DLOGIT, "2b loops 16")
     g.close()
+
+
+def test_2b_prefill_launch_configuration(model2b, D):
+    """The prefill benchmark's exact launch configuration: a 512-row call under
+    per_loop at loops 8 on a loaded context of 1100 rows per slot (past the
+    1024-key sliding window, so the window cuts through the chunk), every one
+    of its 72 sub-layer passes checked, then one decode row."""
+    cfg, w = model2b
+    k, v = _rows(cfg, 1100, 8, seed=19)
+    g = D.Dory(cfg, w, max_ctx=1700, max_chunk=512)
+    o = O.Oracle(cfg, w, max_ctx=1700)
+    g.kv_load(k, v, "per_loop", 8)
+    o.kv_load(k, v, "per_loop", 8)
+    del k, v
+    toks = synth.make_tokens(513, cfg["vocab"], seq=20)
+    say("2b per_loop loops 8: a 512-row call at 1100 + 1 decode")
+    check_pair(run_pair(g, o, [toks[:512], toks[512:]], 8, "per_loop"), COS, DLOGIT, "2b prefill configuration")
+    g.close()
+

@@ -38,7 +38,7 @@ def test_checker_reports_planted_out_of_bounds_launches(hostsim):
     assert "as planted" in out
 
 
-@pytest.mark.parametrize("name", ["latch", "noalloc", "tiny", "tiny_q8", "pages", "shapes2b", "shapes2b_q8", "decode2b",
+@pytest.mark.parametrize("name", ["latch", "noalloc", "kvtap", "tiny", "tiny_q8", "pages", "shapes2b", "shapes2b_q8", "decode2b",
                                   "gate2b", "prefill2b", "q8_2b"])
 def test_host_runtime_scenario(hostsim, name):
     rc, out = _run(hostsim, name)
