@@ -52,6 +52,9 @@ TRAFFIC = {  # committed counter runs: file, kernel source it was taken on (with
     "batch": ("attn_dec_batch64_traffic.json", "attn.hip"),
 }
 TRAFFIC_HEADERS = ("device.h", "internal.h")
+# the profiler's mean duration of each workload's roofline kernel, from the
+# committed rocprofv3 runs of this script (profiles/*_kernels.md)
+ROCPROF = "roofline_rocprof.json"
 
 
 def sources_digest(src):
@@ -157,6 +160,127 @@ def traffic_entry(mode):
     return t.get("bytes_per_launch")
 
 
+def rocprof_entry(mode):
+    """The profiler's mean launch time of the workload's roofline kernel (its
+    stage-benchmark launches in a rocprofv3 --kernel-trace run of this script),
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", ROCPROF)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(mode)
+    if not t or t.get("sources_sha256") != sources_digest(TRAFFIC[mode][1]):
+        return None
+    return {"us_per_launch": t["us_per_launch"], "launches": t["launches"], "summary": t["summary"]}
+
+
+def measured_peaks():
+    """Practical peaks of this GPU (dory_probe): one streaming read of a 2 GiB
+    buffer (8x the 256 MB Infinity Cache) with 16-byte nontemporal loads, the
+    same read of 46 MB slices rotating over the buffer (the size of the largest
+    decode GEMV, ramp and drain included), and a bf16 MFMA loop from registers
+    (v_mfma_f32_32x32x16_bf16, two waves per SIMD)."""
+    import torch
+    from looped_normalized_gpt_amd import dory
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(16, dtype=torch.float32, device="cuda")
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    slice_b = 46137344
+    slices = [buf[i * slice_b:(i + 1) * slice_b] for i in range(8)]
+
+    def rate(launch, reps):
+        for i in range(3):
+            launch(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        work = sum(launch(i) for i in range(reps))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return work / (e0.elapsed_time(e1) * 1e-3)
+
+    big = rate(lambda i: dory.probe("stream", buf=buf, sink=sink, stream=stream), 10)
+    small = rate(lambda i: dory.probe("stream", buf=slices[i % 8], sink=sink, stream=stream), 64)
+    mfma = rate(lambda i: dory.probe("mfma", iters=20000, sink=sink, stream=stream), 5)
+    del buf, slices
+    torch.cuda.empty_cache()
+    return {"hbm_gbs": round(big / 1e9, 1), "hbm_gbs_46MB_reads": round(small / 1e9, 1),
+            "bf16_mfma_tflops": round(mfma / 1e12, 1),
+            "how": "dory_probe: one 2 GiB streaming read (16-byte nontemporal loads), 46 MB reads rotating over "
+                   "8 slices, and a loop of v_mfma_f32_32x32x16_bf16 from registers; HIP events"}
+
+
+def launch_floor(cfg, ctx, loops):
+    """A measured ceiling for a decode token made of one kernel per step: the
+    probe's streaming read (dory_probe) timed back to back at the size of each
+    kernel of the token (each projection's weights, each attention's cache rows,
+    a 64 KB read for each split merge), buffers rotating past the Infinity
+    Cache, summed over the token's 121 kernels.  What a kernel costs beyond its
+    read at that size is its own excess."""
+    import torch
+    from looped_normalized_gpt_amd import dory
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(16, dtype=torch.float32, device="cuda")
+    H, F, Q, KV, V = cfg["hidden"], cfg["ffn"], cfg["nh"] * cfg["hd"], cfg["nk"] * cfg["hd"], cfg["vocab"]
+    rb = kv_row_bytes(cfg)
+    sizes = {"qkvg GEMV": (2 * Q + 2 * KV) * H * 2, "O GEMV": H * Q * 2, "gate|up GEMV": 2 * F * H * 2,
+             "down GEMV": H * F * 2, "head GEMV": V * H * 2,
+             "sliding attention": visible(cfg, "S", ctx) * rb, "full attention": visible(cfg, "*", ctx) * rb,
+             "merge": 65536}
+    pool = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    us = {}
+    for name, b in sizes.items():
+        b = (b + 255) // 256 * 256
+        nbuf = max(2, min(64, (512 << 20) // b))
+        views = [pool[(i * b) % ((1 << 30) - b):][:b] for i in range(nbuf)]
+        for i in range(4):
+            dory.probe("stream", buf=views[i % nbuf], sink=sink, stream=stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 64
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            dory.probe("stream", buf=views[i % nbuf], sink=sink, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    del pool
+    torch.cuda.empty_cache()
+    n_attn = sum(1 for ch in cfg["pattern"] if ch != "-")
+    per = {"qkvg GEMV": 0, "O GEMV": 0, "gate|up GEMV": 0, "down GEMV": 0, "sliding attention": 0,
+           "full attention": 0, "merge": 0, "head GEMV": 1}
+    for li in passes(cfg, loops):
+        kind = cfg["pattern"][li]
+        if kind == "-":
+            per["gate|up GEMV"] += 1
+            per["down GEMV"] += 1
+        else:
+            per["qkvg GEMV"] += 1
+            per["O GEMV"] += 1
+            per["merge"] += 1
+            per["sliding attention" if kind == "S" else "full attention"] += 1
+    floor = sum(us[k] * n for k, n in per.items())
+    return {"us_per_read": us, "launches_per_token": per, "token_floor_us": round(floor, 1),
+            "token_floor_tokens_per_s": round(1e6 / floor, 1),
+            "how": "dory_probe streaming reads of each kernel's byte count, 64 back to back per size, "
+                   "buffers rotating over 512 MB; summed over the kernels of one token"}
+
+
+def roofline_extra(roof, mode, peaks):
+    """Adds the fraction against the measured peak and the profiler's launch
+    time to a roofline entry."""
+    meas = peaks["hbm_gbs"] if roof["bound"] == "hbm" else peaks["bf16_mfma_tflops"]
+    roof["measured_peak"] = meas
+    roof["frac_of_measured_peak"] = round(roof["achieved"] / meas, 4)
+    rp = rocprof_entry(mode)
+    roof["rocprof"] = rp
+    if rp:
+        work = roof.get("bytes_per_launch") or roof.get("flops_per_launch")
+        scale = 1e9 if roof["bound"] == "hbm" else 1e12
+        roof["achieved_at_rocprof_time"] = round(work / (rp["us_per_launch"] * 1e-6) / scale, 1)
+    return roof
+
+
 def vendor_gemm_tflops(M, N, K, reps=100):
     """Reference point, not part of the path: torch.mm (hipBLASLt) on an
     M x N x K bf16 product with a contiguous [K][N] right operand, rotating over
@@ -215,11 +339,14 @@ def _cores():
     return int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
 
 
-def cpu_decode(cfg, w, context, loops_of, budget_s, what):
+def cpu_decode(cfg, w, context, loops_of, budget_s, what, threads=0):
     """The oracle decoding single tokens after its cache is loaded with
-    `context` synthetic rows; loops_of(i) gives token i's loop count."""
+    `context` synthetic rows; loops_of(i) gives token i's loop count.  threads:
+    the oracle's OpenMP threads (0: all the host's).  At least one token, then
+    as many as fit the budget."""
     from looped_normalized_gpt_amd import synth
     from oracle import oracle as O
+    used = O.set_threads(threads)
     o = O.Oracle(cfg, w, max_ctx=context + 40)
     no = n_ord(cfg)
     k, v = synth.make_kv_rows(no * context, cfg["nk"], cfg["hd"], cfg["hidden"], seed=4)
@@ -235,22 +362,26 @@ def cpu_decode(cfg, w, context, loops_of, budget_s, what):
             break
     dt = time.perf_counter() - t0
     o.close()
-    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
+    O.set_threads(0)
+    return {"value": round(n / dt, 4), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"{n} {what} at context {context}, the oracle's cache loaded with {context} synthetic rows, "
-                      f"{dt:.1f} s"}
+                      f"{dt:.1f} s on {used} thread(s) of {os.cpu_count()} host cores"}
 
 
-def cpu_prefill(cfg, w, rows, loops):
+def cpu_prefill(cfg, w, rows, loops, threads=0):
     from looped_normalized_gpt_amd import synth
     from oracle import oracle as O
+    used = O.set_threads(threads)
     o = O.Oracle(cfg, w, max_ctx=rows + 8)
     toks = synth.make_tokens(rows, cfg["vocab"], seq=9)
     t0 = time.perf_counter()
     o.forward(toks, loops, "per_loop")
     dt = time.perf_counter() - t0
     o.close()
-    return {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": _cores(), "kind": "oracle",
-            "sample": f"one {rows}-row prompt call of Dory-2B (per_loop, loops {loops}) from position 0, {dt:.1f} s"}
+    O.set_threads(0)
+    return {"value": round(rows / dt, 4), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"one {rows}-row prompt call of Dory-2B (per_loop, loops {loops}) from position 0, {dt:.1f} s "
+                      f"on {used} thread(s) of {os.cpu_count()} host cores"}
 
 
 # ------------------------------------------------------------------ workloads
@@ -324,14 +455,18 @@ def run_decode(args, q8, gate=None):
     vendor = {"us": round(v_us, 2), "gbps": round(2 * F * H * 2 / (v_us * 1e-6) / 1e9, 1),
               "what": "torch.mv, bf16 [11264][2048] x bf16 vector (no SwiGLU)"}
 
-    cpu = None
+    log("bench: measured peaks and the per-launch floor of a token")
+    peaks = measured_peaks()
+    floor = launch_floor(cfg, ctx, loops)
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        log("bench: CPU baseline (oracle)")
+        log("bench: CPU baseline (oracle), all host cores and one core")
         # q8: the windows (1024 sliding, 8192 full) cap the rows a token reads, so
         # a context just past 8192 costs the oracle what 32768 does
         cctx = 8200 if q8 else ctx
-        cpu = cpu_decode(cfg, w, cctx, lambda i: loops, 20.0,
-                         f"decode tokens of Dory-2B (loops {loops}, last_loop{', q8_2f' if q8 else ''})")
+        what = f"decode tokens of Dory-2B (loops {loops}, last_loop{', q8_2f' if q8 else ''})"
+        cpu = cpu_decode(cfg, w, cctx, lambda i: loops, 20.0, what)
+        cpu1 = cpu_decode(cfg, w, cctx, lambda i: loops, 15.0, what, threads=1)
     if gate is not None:
         metric = f"gated decode tokens/s (confidence gate {gate}), 1×MI355X, Dory-2B ctx {ctx}"
         workload = (f"Dory-2B decode, batch 1, context {ctx}, confidence-gated early exit at top probability "
@@ -353,17 +488,23 @@ def run_decode(args, q8, gate=None):
         "hbm_gbps_algorithmic": round(gbs, 1), "bytes_per_token": int(bytes_tok),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "wall_ms_per_step": round(wall_ms / K, 4),
         "prefill_tokens_per_s": round(ctx / prefill_s, 1), "stage_us": stages, "vendor_gemv_same_shape": vendor,
-        "roofline": {"kernel": "k_gemv gate|up + SwiGLU (bf16 [2x5632][2048])", "bound": "hbm",
-                     "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gu_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_entry("q8" if q8 else "decode"),
-                     "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3)},
+        "roofline": roofline_extra({"kernel": "k_gemv gate|up + SwiGLU (bf16 [2x5632][2048])", "bound": "hbm",
+                                    "achieved": round(gu_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(gu_gbs / PEAK_HBM_GBS, 4),
+                                    "traffic": traffic_entry("q8" if q8 else "decode"),
+                                    "bytes_per_launch": gu_bytes, "us_per_launch": round(gu_us, 3)},
+                                   "q8" if q8 else "decode", peaks),
+        "measured_peaks": peaks,
+        "hbm_frac_of_measured_peak": round(gbs / peaks["hbm_gbs"], 4),
+        "launch_floor": floor,
         "cpu_baseline": cpu,
+        "cpu_baseline_one_core": cpu1,
     }
     if gate is not None:
         # passes per token follow the gate's decisions, not `loops`: the byte
         # count above assumes 4 loops and is not reported for this workload
         tokens, one, _, rate = gstats
-        for k in ("hbm_gbps_algorithmic", "bytes_per_token", "hbm_frac_of_peak"):
+        for k in ("hbm_gbps_algorithmic", "bytes_per_token", "hbm_frac_of_peak", "hbm_frac_of_measured_peak"):
             out.pop(k)
         out["config"]["loops"] = "1 or 2 (gated)"
         out["gate"] = {"threshold": gate, "tokens": tokens, "one_pass": one, "exit_rate": round(rate, 4),
@@ -416,10 +557,13 @@ def run_prefill(args):
     gu_flops = 2 * chunk * 2 * F * H
     gu_tf = tflops["gemm_gateup"]
 
-    cpu = None
+    log("bench: measured peaks")
+    peaks = measured_peaks()
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        log("bench: CPU baseline (oracle)")
-        cpu = cpu_prefill(cfg, w, 16, loops)
+        log("bench: CPU baseline (oracle): one 512-row call on all host cores, 16 rows on one core")
+        cpu = cpu_prefill(cfg, w, chunk, loops)
+        cpu1 = cpu_prefill(cfg, w, 16, loops, threads=1)
     return {
         "metric": "prefill tokens/s, 1×MI355X, Dory-2B per_loop loops 8, 8192-token prompt in 512-row calls",
         "value": round(tok_s, 1), "unit": "tokens/s", "steps": K, "warmup": W, "ms_per_step": round(ms, 3),
@@ -430,12 +574,17 @@ def run_prefill(args):
                    "parallelism": "none (one GPU)"},
         "projection_tflops_overall": round(gemm_tflops, 1), "wall_ms_per_step": round(wall_ms / K, 3),
         "stage_us": stages, "stage_tflops": tflops, "vendor_gemm_tflops_same_shapes": vendor,
-        "roofline": {"kernel": "k_gemm_mfma2<SwiGLU> gate|up with the SwiGLU epilogue (512 x 11264 x 2048, bf16)",
-                     "bound": "mfma",
-                     "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry("prefill"),
-                     "flops_per_launch": gu_flops, "us_per_launch": stages["gemm_gateup"]},
+        "roofline": roofline_extra({"kernel": "k_gemm_mfma2<SwiGLU> gate|up with the SwiGLU epilogue "
+                                              "(512 x 11264 x 2048, bf16)",
+                                    "bound": "mfma",
+                                    "achieved": gu_tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                    "frac": round(gu_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic_entry("prefill"),
+                                    "flops_per_launch": gu_flops, "us_per_launch": stages["gemm_gateup"]},
+                                   "prefill", peaks),
+        "measured_peaks": peaks,
+        "stage_frac_of_measured_mfma": {k: round(v / peaks["bf16_mfma_tflops"], 4) for k, v in tflops.items()},
         "cpu_baseline": cpu,
+        "cpu_baseline_one_core": cpu1,
     }
 
 
@@ -495,12 +644,15 @@ def run_batch(args):
     g.close()
     at_gbs = at_bytes / (at_us * 1e-6) / 1e9
 
-    cpu = None
+    log("bench: measured peaks")
+    peaks = measured_peaks()
+    cpu = cpu1 = None
     if not args.no_cpu_baseline:
-        log("bench: CPU baseline (oracle)")
+        log("bench: CPU baseline (oracle), all host cores and one core")
         lp = loops[W:, 0]
-        cpu = cpu_decode(cfg, w, ctx, lambda i: int(lp[i % len(lp)]), 20.0,
-                         "single-sequence decode tokens of Dory-2B (loops drawn from 1..16, last_loop)")
+        what = "single-sequence decode tokens of Dory-2B (loops drawn from 1..16, last_loop)"
+        cpu = cpu_decode(cfg, w, ctx, lambda i: int(lp[i % len(lp)]), 20.0, what)
+        cpu1 = cpu_decode(cfg, w, ctx, lambda i: int(lp[i % len(lp)]), 15.0, what, threads=1)
     return {
         "metric": "batched decode tokens/s (64 sequences, all loops) + achieved HBM GB/s, 1×MI355X, Dory-2B ctx 8192",
         "value": round(tok_s, 1), "unit": "tokens/s", "steps": K, "warmup": W, "ms_per_step": round(ms, 3),
@@ -512,11 +664,15 @@ def run_batch(args):
         "hbm_gbps_algorithmic": round(gbs, 1), "bytes_per_step": int(step_bytes),
         "hbm_frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "wall_ms_per_step": round(wall_ms / K, 3),
         "prefill_tokens_per_s": round(nseq * ctx / prefill_s, 1), "stage_us": stages,
-        "roofline": {"kernel": "k_attn_dec + k_attn_merge over 64 rows (S and full layers alternating)",
-                     "bound": "hbm", "achieved": round(at_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(at_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_entry("batch"),
-                     "bytes_per_launch": int(at_bytes), "us_per_launch": round(at_us, 3)},
+        "roofline": roofline_extra({"kernel": "k_attn_dec + k_attn_merge over 64 rows (S and full layers alternating)",
+                                    "bound": "hbm", "achieved": round(at_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(at_gbs / PEAK_HBM_GBS, 4), "traffic": traffic_entry("batch"),
+                                    "bytes_per_launch": int(at_bytes), "us_per_launch": round(at_us, 3)},
+                                   "batch", peaks),
+        "measured_peaks": peaks,
+        "hbm_frac_of_measured_peak": round(gbs / peaks["hbm_gbs"], 4),
         "cpu_baseline": cpu,
+        "cpu_baseline_one_core": cpu1,
     }
 
 

@@ -287,6 +287,18 @@ int dory_q8_encode_rows(const float *x, const float *col, int32_t rows, int32_t 
  * and positions are untouched. */
 int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t stream);
 
+/* Benchmark tap: practical peaks of the GPU, for stating kernel fractions
+ * against measured as well as published peaks.  kind 0: one streaming read of
+ * `bytes` (a positive multiple of 16) at device buf, 16-byte nontemporal
+ * loads; kind 1: `iters` (1 .. 2^24) iterations of four
+ * v_mfma_f32_32x32x16_bf16 per wave on 2048 waves from registers (buf and
+ * bytes unused).  sink: device memory of at least 4 bytes (a store that keeps
+ * the work alive; practically never written).  *work: the bytes read or flops
+ * done by the launch.  Asynchronous on stream: time it with events.
+ * DORY_EINVAL for bad arguments. */
+int dory_probe(int32_t kind, const void *buf, int64_t bytes, int64_t iters, void *sink,
+               dory_stream_t stream, double *work);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ COMMON = ["hipcc", f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-parameter"]
 PER_FILE = {"q8.hip": ["-ffp-contract=off"]}
-SOURCES = ["api.hip", "gemv.hip", "rows.hip", "gemm.hip", "attn.hip", "q8.hip", "scratch.hip"]
+SOURCES = ["api.hip", "gemv.hip", "rows.hip", "gemm.hip", "attn.hip", "q8.hip", "scratch.hip", "probe.hip"]
 
 
 def _compile(src):

@@ -75,6 +75,7 @@ def _load():
     L.dory_kv_load.argtypes = [vp, i32, i32, i32, i64, i32, vp, vp]
     L.dory_q8_encode_rows.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     L.dory_stage_bench.argtypes = [vp, i32, i32, vp]
+    L.dory_probe.argtypes = [i32, vp, i64, i64, vp, vp, C.POINTER(C.c_double)]
     return L
 
 
@@ -385,3 +386,15 @@ def q8_encode_rows(x, col, group: int, stream=None):
         raise DoryError(rc, lib.dory_last_error(None).decode())
     return codes, scales
 
+
+def probe(kind: str, buf=None, iters: int = 0, sink=None, stream=None) -> float:
+    """dory_probe: launches one peak probe ("stream": one read of the device
+    tensor buf; "mfma": iters bf16 MFMA iterations) and returns the bytes or
+    flops of the launch.  sink: a device tensor of at least 4 bytes."""
+    work = C.c_double()
+    k = {"stream": 0, "mfma": 1}[kind]
+    nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+    rc = lib.dory_probe(k, _ptr(buf), nbytes, iters, _ptr(sink), _stream(stream), C.byref(work))
+    if rc != OK:
+        raise DoryError(rc, f"dory_probe({kind})")
+    return work.value

@@ -20,6 +20,7 @@
 #include "dory_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -584,6 +585,15 @@ int ora_gate_stats(const ora_model *m, int32_t seq, int64_t *tokens, int64_t *on
     if (rate) *rate = q->exit_rate;
     return ORA_OK;
 }
+
+/* Threads of the OpenMP loops (n <= 0: as many as the host has); the
+ * arithmetic and its order do not depend on it.  Returns the count in use. */
+int ora_set_threads(int32_t n) {
+    omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
+    return omp_get_max_threads();
+}
+
+int ora_threads(void) { return omp_get_max_threads(); }
 
 int ora_set_prompt_loops(ora_model *m, int32_t n) {
     if (!m || n < 0 || n > ORA_MAX_LOOPS) return ORA_EINVAL;

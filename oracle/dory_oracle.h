@@ -72,6 +72,8 @@ int  ora_forward_want(ora_model *m, int32_t seq, const int32_t *tokens, int32_t 
 /* [dory] `prompt_loops` (0..16, 0 = off): a last_loop call that wants no
  * logits runs min(loops, prompt_loops) passes of the recurrent block. */
 int  ora_set_prompt_loops(ora_model *m, int32_t n);
+int  ora_set_threads(int32_t n);   /* OpenMP threads (n <= 0: all); returns the count in use */
+int  ora_threads(void);
 /* [dory] `Gate::Conf(th)` (on = 0: no gate): a one-row last_loop call runs one
  * pass of the recurrent block, a read-out when the exit rate asks for one, and
  * a second pass unless the read-out's top probability reaches th.  Gated calls

@@ -63,6 +63,7 @@ def lib():
         L.ora_forward_want.argtypes = [C.c_void_p, C.c_int32, C.c_void_p, C.c_int32, C.c_int32,
                                        C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
         L.ora_set_prompt_loops.argtypes = [C.c_void_p, C.c_int32]
+        L.ora_set_threads.argtypes = [C.c_int32]
         L.ora_set_gate.argtypes = [C.c_void_p, C.c_int32, C.c_float]
         L.ora_gate_stats.argtypes = [C.c_void_p, C.c_int32] + [C.c_void_p] * 4
         L.ora_top_prob.argtypes = [C.c_void_p, C.c_int32]
@@ -93,6 +94,16 @@ def lib():
         L.ora_sigmoid_gate.argtypes = [C.c_float] * 3
         L.ora_sigmoid_gate.restype = C.c_float
     return _lib
+
+
+def set_threads(n: int) -> int:
+    """OpenMP threads of the oracle's loops (n <= 0: all the host's); returns
+    the count in use.  Timing only: the results do not depend on it."""
+    return lib().ora_set_threads(n)
+
+
+def threads() -> int:
+    return lib().ora_threads()
 
 
 def _p(a):
