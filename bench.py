@@ -229,21 +229,31 @@ def launch_floor(cfg, ctx, loops):
              "merge": 65536}
     pool = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     us = {}
+    reps = 32
     for name, b in sizes.items():
         b = (b + 255) // 256 * 256
         nbuf = max(2, min(64, (512 << 20) // b))
         views = [pool[(i * b) % ((1 << 30) - b):][:b] for i in range(nbuf)]
         for i in range(4):
             dory.probe("stream", buf=views[i % nbuf], sink=sink, stream=stream)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 64
         torch.cuda.synchronize()
+        # the reads captured back to back in one HIP graph, as the decode
+        # token's kernels are (host launches would be the bound for small ones)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream()
+            for i in range(reps):
+                dory.probe("stream", buf=views[i % nbuf], sink=sink, stream=cs)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(reps):
-            dory.probe("stream", buf=views[i % nbuf], sink=sink, stream=stream)
+        for _ in range(4):
+            g.replay()
         e1.record(stream)
         torch.cuda.synchronize()
-        us[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+        us[name] = round(e0.elapsed_time(e1) * 1e3 / (4 * reps), 2)
+        del g
     del pool
     torch.cuda.empty_cache()
     n_attn = sum(1 for ch in cfg["pattern"] if ch != "-")
@@ -262,8 +272,8 @@ def launch_floor(cfg, ctx, loops):
     floor = sum(us[k] * n for k, n in per.items())
     return {"us_per_read": us, "launches_per_token": per, "token_floor_us": round(floor, 1),
             "token_floor_tokens_per_s": round(1e6 / floor, 1),
-            "how": "dory_probe streaming reads of each kernel's byte count, 64 back to back per size, "
-                   "buffers rotating over 512 MB; summed over the kernels of one token"}
+            "how": "dory_probe streaming reads of each kernel's byte count, 32 back to back in a captured HIP "
+                   "graph per size, buffers rotating over 512 MB; summed over the kernels of one token"}
 
 
 def roofline_extra(roof, mode, peaks):
@@ -390,7 +400,7 @@ def prompt(g, cfg, n, loops, mode, seq=0, chunk=512, tok_seed=None, last_logits=
     from looped_normalized_gpt_amd import synth
     toks = synth.make_tokens(n, cfg["vocab"], seq=seq if tok_seed is None else tok_seed)
     for c in range(0, n, chunk):
-        g.forward(toks[c:c + chunk], loops, mode, seq=seq, logits=(last_logits and c + chunk >= n))
+        g.forward(toks[c:min(c + chunk, n)], loops, mode, seq=seq, logits=(last_logits and c + chunk >= n))
 
 
 def run_decode(args, q8, gate=None):
@@ -410,7 +420,7 @@ def run_decode(args, q8, gate=None):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for c in range(0, ctx, 512):
-        g.forward(toks[c:c + 512], loops, "last_loop", logits=(c + 512 >= ctx))
+        g.forward(toks[c:min(c + 512, ctx)], loops, "last_loop", logits=(c + 512 >= ctx))
         if c % 8192 == 0 and c:
             log(f"bench:   {c} tokens")
     torch.cuda.synchronize()
