@@ -109,3 +109,20 @@ def test_binding_checks_output_tensors_before_the_call():
             _device_buffer(bad, 2, 10, dev, "t")
     with pytest.raises(DoryError):
         _device_buffer(ok, 2, 10, torch.device("cuda", 0), "t")
+
+
+def test_probe_rejects_bad_arguments_before_any_launch():
+    """dory_probe (the peak probes) checks its arguments first: no sink or
+    work pointer, a stream read of a null or unaligned buffer, an MFMA loop of
+    no or too many iterations, an unknown kind."""
+    from looped_normalized_gpt_amd.dory import lib, EINVAL
+    w = C.c_double()
+    sink = C.c_void_p(64)   # never dereferenced: the checks fail first
+    assert lib.dory_probe(0, None, 1 << 20, 0, sink, None, C.byref(w)) == EINVAL
+    assert lib.dory_probe(0, sink, 1000, 0, sink, None, C.byref(w)) == EINVAL      # not a multiple of 16
+    assert lib.dory_probe(0, sink, 0, 0, sink, None, C.byref(w)) == EINVAL
+    assert lib.dory_probe(1, None, 0, 0, sink, None, C.byref(w)) == EINVAL          # no iterations
+    assert lib.dory_probe(1, None, 0, (1 << 24) + 1, sink, None, C.byref(w)) == EINVAL
+    assert lib.dory_probe(2, None, 0, 10, sink, None, C.byref(w)) == EINVAL
+    assert lib.dory_probe(1, None, 0, 10, None, None, C.byref(w)) == EINVAL
+    assert lib.dory_probe(1, None, 0, 10, sink, None, None) == EINVAL
