@@ -646,7 +646,7 @@ int enqueue(Enq &q) {
             rs.h = sc.hb[(k - 1) % 2]; rs.o = sc.o; rs.alpha = h->L[prev_li].w.alpha; rs.slerp = 1;
             rs.h_out = sc.hb[k % 2]; rs.hb_out = sc.xb; rs.tap_pass = k - 1;
             rs.n_prev = rows_of(k - 1);
-            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, sc.rec, q.s));
+            if (T > 1) LAUNCH(launch_resolve_rows(rs, h->H, op == kLoopExit ? T : rs.n_prev, sc.rec, h->tap, T, q.s));
         }
         if (op == kLoopExit && q.gate_save) rs.e_out = h->gst;
         const LayerInfo &l = h->L[li];
@@ -674,7 +674,7 @@ int enqueue(Enq &q) {
     } else {
         rf.h_out = sc.hb[P % 2];
         rf.hb_out = sc.xb;
-        LAUNCH(launch_resolve_rows(rf, h->H, T, sc.rec, q.s));
+        LAUNCH(launch_resolve_rows(rf, h->H, T, sc.rec, h->tap, T, q.s));
         if (q.want_logits && !q.batch && !q.want_all) {
             a.row = T - 1; a.src = sc.hb[P % 2];
             LAUNCH(launch_gemv(h->wt, kProPlain, kEpiHead, a, q.s));

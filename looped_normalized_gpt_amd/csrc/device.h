@@ -230,10 +230,20 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
 // caller's earlier loads are still in flight.
 __device__ __forceinline__ int reg_index(int j) { return 4 * (int)threadIdx.x + 1024 * (j >> 2) + (j & 3); }
 
+// The record's tap row of pass `pass`, row r, rows of n floats (null: no tap).
+__device__ __forceinline__ float *tap_row(const CallRec *rec, int pass, int r, int n) {
+    if (pass < 0) return nullptr;
+    float *t = rec->tap;
+    return t ? t + ((size_t)pass * rec->n + r) * n : nullptr;
+}
+
+// tap: where the writer stores e for the record's tap (row r of pass
+// rs.tap_pass), or null; callers read the record's pointer ahead, with their
+// other loads.
 template <int EPT>
 __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float (&h)[EPT], const float (&o)[EPT],
                                     const float (&al)[EPT], const float (&in)[EPT], float *xs, float *red,
-                                    bool writer, const CallRec *rec) {
+                                    bool writer, float *tap) {
     float e[EPT];
     if (!rs.slerp) {
 #pragma unroll
@@ -258,11 +268,10 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
 #pragma unroll
         for (int j = 0; j < EPT; ++j) e[j] *= re;
     }
-    if (writer && rec->tap && rs.tap_pass >= 0) {
-        float *t = rec->tap + ((size_t)rs.tap_pass * rec->n + r) * H;
+    if (writer && tap) {
 #pragma unroll
         for (int j = 0; j < EPT; j += 4)
-            if (reg_index(j) < H) *reinterpret_cast<float4 *>(t + reg_index(j)) = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
+            if (reg_index(j) < H) *reinterpret_cast<float4 *>(tap + reg_index(j)) = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
     }
     if (rs.loop_op == kLoopEnter) {
         float s = 0.f;

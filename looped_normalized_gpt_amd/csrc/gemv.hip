@@ -200,7 +200,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
             if (4 * tid + 1024 * jj >= K)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) ph[4 * jj + c] = po[4 * jj + c] = pa[4 * jj + c] = pi[4 * jj + c] = 0.f;
-        resolve_regs<EPT>(rs, a.row, K, ph, po, pa, pi, xs, red, blockIdx.x == 0, rec);
+        resolve_regs<EPT>(rs, a.row, K, ph, po, pa, pi, xs, red, blockIdx.x == 0,
+                          blockIdx.x == 0 ? tap_row(rec, rs.tap_pass, a.row, K) : nullptr);
     } else {
         float f = 1.f;
         if (PRO == kProNorm) {

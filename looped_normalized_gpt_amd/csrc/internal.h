@@ -135,7 +135,11 @@ hipError_t launch_add_slabs(float *x, size_t n, int parts, size_t stride, hipStr
 // null) for the bf16 GEMMs that read it next.
 hipError_t launch_embed(int wtype, const void *embed, int V, int H, const CallRec *rec, int T,
                         float *h, uint16_t *hb, hipStream_t s);
-hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s);
+// tap, tap_n: the record's tap buffer and row count (rec->tap, rec->n) as the
+// host set them for this call: multi-row calls are never captured in a graph,
+// so the kernel takes them as arguments instead of reading the record.
+hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, float *tap, int tap_n,
+                               hipStream_t s);
 hipError_t launch_rownorm(const float *src, int ld_src, float *dst, uint16_t *dstb, int N, int T, hipStream_t s);
 // a and b rows have stride ld; dst rows stride F.  dst or dstb may be null.
 // With ss: the un-normalised rows are stored and ss[r] = their |z|^2 (the

@@ -26,47 +26,75 @@ __global__ __launch_bounds__(256) void k_embed(const void *E, int V, int H, cons
 }
 
 // One row per workgroup; thread t holds the float4 groups at 4t + 1024 jj of
-// the row in registers (EPT / 4 groups), every input load issued before any
-// arithmetic.
-template <int EPT>
-__global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const CallRec *rec) {
+// the row in registers (EPT / 4 groups).  Every load is issued before any
+// arithmetic, unconditionally where its count varies (P slabs of o, the
+// renorm's partial sums: clamped addresses, masked values), so none waits
+// for another: the renorm partials, h, o, alpha, the loop input.  The tap
+// pointer and row count come as arguments: a read of the record here cost a
+// round trip before or after the loads.  (A loop over the slabs waited for each slab in turn, and the
+// renorm's sum and the record's tap pointer each took a round trip of their
+// own before and after the loads.)
+template <int EPT, int P>
+__global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, float *tap_base, int tap_n) {
     __shared__ float red[16];  // resolve_regs' two reduction slots
-    const int r = blockIdx.x, tid = threadIdx.x;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const bool from_st = rs.loop_op == kLoopExit && r >= rs.n_prev;  // a batch row whose loops ended early
     const bool slerp = rs.slerp && !from_st;
     const float *hs = (from_st ? rs.st : rs.h) + (size_t)r * H;
     // the renorm of the attention output before its projection, applied here
-    // (the projection is linear): o times justnorm's factor of |z|^2
-    float oc = 1.f;
-    if (slerp && rs.o_ss) {
-        // (up to one partial per kv head, or per 64 ffn indices: the lanes of
-        // each wave take them in turn, a wave sum adds them)
-        const float *ps = rs.o_ss + (size_t)r * rs.o_ss_n;
-        float t = 0.f;
-        for (int k = tid & 63; k < rs.o_ss_n; k += 64) t += ps[k];
-        oc = norm_factor(wave_sum(t));
+    // (the projection is linear): o times justnorm's factor of |z|^2, the sum
+    // of up to 128 partials (one per kv head, or per 64 ffn indices), two a lane
+    const bool ren = slerp && rs.o_ss;
+    const int nss = rs.o_ss_n;
+    float s0 = 0.f, s1 = 0.f;
+    if (ren) {
+        const float *ps = rs.o_ss + (size_t)r * nss;
+        s0 = ps[lane < nss ? lane : 0];
+        s1 = ps[lane + 64 < nss ? lane + 64 : 0];
     }
-    float h[EPT], o[EPT], al[EPT], in[EPT];
+    const int parts = rs.o_parts > 1 ? rs.o_parts : 1;
+    float4 vh[EPT / 4], vo[EPT / 4][P], va[EPT / 4], vi[EPT / 4];
 #pragma unroll
     for (int jj = 0; jj < EPT / 4; ++jj) {
         const int i = 4 * tid + 1024 * jj, ic = i < H ? i : 0;
-        const float4 vh = *reinterpret_cast<const float4 *>(hs + ic);
-        float4 vo = make_float4(0.f, 0.f, 0.f, 0.f), va = vo, vi = vo;
+        vh[jj] = *reinterpret_cast<const float4 *>(hs + ic);
+        vo[jj][0] = va[jj] = vi[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (slerp) {
             // o: the sum of the output projection's split-K slabs
-            for (int p = 0; p < (rs.o_parts > 1 ? rs.o_parts : 1); ++p) {
-                const float4 t = *reinterpret_cast<const float4 *>(rs.o + (size_t)p * rs.o_stride + (size_t)r * H + ic);
-                vo.x += t.x; vo.y += t.y; vo.z += t.z; vo.w += t.w;
-            }
-            va = *reinterpret_cast<const float4 *>(rs.alpha + ic);
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                vo[jj][p] = *reinterpret_cast<const float4 *>(rs.o + (size_t)(p < parts ? p : 0) * rs.o_stride +
+                                                              (size_t)r * H + ic);
+            va[jj] = *reinterpret_cast<const float4 *>(rs.alpha + ic);
         }
-        if (rs.loop_op == kLoopNext) vi = *reinterpret_cast<const float4 *>(rs.inp + (size_t)r * H + ic);
-        const bool ok = i < H;
-        h[4 * jj] = ok ? vh.x : 0.f; h[4 * jj + 1] = ok ? vh.y : 0.f; h[4 * jj + 2] = ok ? vh.z : 0.f; h[4 * jj + 3] = ok ? vh.w : 0.f;
-        o[4 * jj] = ok ? vo.x * oc : 0.f; o[4 * jj + 1] = ok ? vo.y * oc : 0.f;
-        o[4 * jj + 2] = ok ? vo.z * oc : 0.f; o[4 * jj + 3] = ok ? vo.w * oc : 0.f;
-        al[4 * jj] = va.x; al[4 * jj + 1] = va.y; al[4 * jj + 2] = va.z; al[4 * jj + 3] = va.w;
-        in[4 * jj] = ok ? vi.x : 0.f; in[4 * jj + 1] = ok ? vi.y : 0.f; in[4 * jj + 2] = ok ? vi.z : 0.f; in[4 * jj + 3] = ok ? vi.w : 0.f;
+        if (rs.loop_op == kLoopNext) vi[jj] = *reinterpret_cast<const float4 *>(rs.inp + (size_t)r * H + ic);
+    }
+    // every load above is in flight before the first use of any of them
+    asm volatile("" ::"v"(s0), "v"(s1));
+#pragma unroll
+    for (int jj = 0; jj < EPT / 4; ++jj) {
+        asm volatile("" ::"v"(vh[jj].x), "v"(vh[jj].w), "v"(va[jj].x), "v"(va[jj].w), "v"(vi[jj].x), "v"(vi[jj].w));
+#pragma unroll
+        for (int p = 0; p < P; ++p) asm volatile("" ::"v"(vo[jj][p].x), "v"(vo[jj][p].w));
+    }
+    float *tap = !from_st && rs.tap_pass >= 0 && tap_base ? tap_base + ((size_t)rs.tap_pass * tap_n + r) * H : nullptr;
+    const float oc = ren ? norm_factor(wave_sum((lane < nss ? s0 : 0.f) + (lane + 64 < nss ? s1 : 0.f))) : 1.f;
+    float h[EPT], o[EPT], al[EPT], in[EPT];
+#pragma unroll
+    for (int jj = 0; jj < EPT / 4; ++jj) {
+        const bool ok = 4 * tid + 1024 * jj < H;
+        float4 so = vo[jj][0];
+#pragma unroll
+        for (int p = 1; p < P; ++p)
+            if (p < parts) {
+                so.x += vo[jj][p].x; so.y += vo[jj][p].y; so.z += vo[jj][p].z; so.w += vo[jj][p].w;
+            }
+        const float4 vhh = vh[jj], vaa = va[jj], vii = vi[jj];
+        h[4 * jj] = ok ? vhh.x : 0.f; h[4 * jj + 1] = ok ? vhh.y : 0.f; h[4 * jj + 2] = ok ? vhh.z : 0.f; h[4 * jj + 3] = ok ? vhh.w : 0.f;
+        o[4 * jj] = ok ? so.x * oc : 0.f; o[4 * jj + 1] = ok ? so.y * oc : 0.f;
+        o[4 * jj + 2] = ok ? so.z * oc : 0.f; o[4 * jj + 3] = ok ? so.w * oc : 0.f;
+        al[4 * jj] = vaa.x; al[4 * jj + 1] = vaa.y; al[4 * jj + 2] = vaa.z; al[4 * jj + 3] = vaa.w;
+        in[4 * jj] = ok ? vii.x : 0.f; in[4 * jj + 1] = ok ? vii.y : 0.f; in[4 * jj + 2] = ok ? vii.z : 0.f; in[4 * jj + 3] = ok ? vii.w : 0.f;
     }
     if (from_st) {
 #pragma unroll
@@ -84,7 +112,7 @@ __global__ __launch_bounds__(256) void k_resolve_rows(Resolve rs, int H, const C
     }
     Resolve rr = rs;
     rr.slerp = slerp;
-    resolve_regs<EPT>(rr, r, H, h, o, al, in, nullptr, red, true, rec);
+    resolve_regs<EPT>(rr, r, H, h, o, al, in, nullptr, red, true, tap);
 }
 
 // dst[r] = justnorm(src[r]) over N values.
@@ -273,12 +301,26 @@ hipError_t launch_embed(int wtype, const void *E, int V, int H, const CallRec *r
     return hipGetLastError();
 }
 
-hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s) {
-    if (H <= 2048) hipLaunchKernelGGL((k_resolve_rows<8>), dim3(T), dim3(256), 0, s, rs, H, rec);
-    else if (H <= 4096) hipLaunchKernelGGL((k_resolve_rows<16>), dim3(T), dim3(256), 0, s, rs, H, rec);
-    else if (H <= 8192) hipLaunchKernelGGL((k_resolve_rows<32>), dim3(T), dim3(256), 0, s, rs, H, rec);
-    else return hipErrorInvalidValue;
+template <int EPT>
+hipError_t launch_resolve_p(const Resolve &rs, int H, int T, float *tap, int tap_n, hipStream_t s) {
+    const int parts = rs.slerp && rs.o_parts > 1 ? rs.o_parts : 1;
+    if (parts == 1) hipLaunchKernelGGL((k_resolve_rows<EPT, 1>), dim3(T), dim3(256), 0, s, rs, H, tap, tap_n);
+    else if (parts == 2) hipLaunchKernelGGL((k_resolve_rows<EPT, 2>), dim3(T), dim3(256), 0, s, rs, H, tap, tap_n);
+    else if (parts <= 4) hipLaunchKernelGGL((k_resolve_rows<EPT, 4>), dim3(T), dim3(256), 0, s, rs, H, tap, tap_n);
+    else hipLaunchKernelGGL((k_resolve_rows<EPT, 8>), dim3(T), dim3(256), 0, s, rs, H, tap, tap_n);
     return hipGetLastError();
+}
+
+hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, float *tap, int tap_n,
+                               hipStream_t s) {
+    (void)rec;  // what the kernel would read from it comes as tap, tap_n
+    if (rs.slerp && rs.o_parts > kMaxKParts) return hipErrorInvalidValue;
+    if (rs.slerp && rs.o_ss && (rs.o_ss_n < 1 || rs.o_ss_n > 128)) return hipErrorInvalidValue;
+    if (tap && tap_n < T) return hipErrorInvalidValue;
+    if (H <= 2048) return launch_resolve_p<8>(rs, H, T, tap, tap_n, s);
+    if (H <= 4096) return launch_resolve_p<16>(rs, H, T, tap, tap_n, s);
+    if (H <= 8192) return launch_resolve_p<32>(rs, H, T, tap, tap_n, s);
+    return hipErrorInvalidValue;
 }
 
 #define DK_G_SWITCH(G, KERNEL, ...)                                                          \

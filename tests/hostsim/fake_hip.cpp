@@ -427,8 +427,13 @@ hipError_t launch_embed(int wt, const void *E, int V, int H, const CallRec *rec,
     return fake::launch("launch_embed", stat, [=]() { fake::need_record(rec, T); });
 }
 
-hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, hipStream_t s) {
+hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *rec, float *tap, int tap_n,
+                               hipStream_t s) {
     if (H > 8192) return hipErrorInvalidValue;
+    if (rs.slerp && rs.o_parts > kMaxKParts) return hipErrorInvalidValue;
+    if (rs.slerp && rs.o_ss && (rs.o_ss_n < 1 || rs.o_ss_n > 128)) return hipErrorInvalidValue;
+    if (tap && tap_n < T) return hipErrorInvalidValue;
+    if (fake::capturing) fake::violation("a multi-row residual step in a graph: its tap arguments would go stale");
     auto stat = [=]() {
         // rows past n_prev leave the loops early: after them (kLoopExit) their
         // state comes from st
@@ -446,6 +451,8 @@ hipError_t launch_resolve_rows(const Resolve &rs, int H, int T, const CallRec *r
     };
     auto dyn = [=]() {
         fake::need_record(rec, T);
+        if (tap != rec->tap || (tap && tap_n != rec->n))
+            fake::violation("the residual step's tap arguments differ from the record's");
         for (int r = 0; r < T; ++r) fake::resolve_writes(rs, r, H, rec, true);
     };
     return fake::launch("launch_resolve_rows", stat, dyn);
