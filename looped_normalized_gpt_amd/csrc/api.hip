@@ -497,6 +497,12 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         pa.rope = l.sliding ? h->rope_s : h->rope_f; pa.sq = w.sq; pa.tab = h->tab;
         pa.n_ord = h->n_ord; pa.ord = l.ord; pa.slot = slot; pa.nh = h->nh; pa.nk = h->nk; pa.hd = h->hd; pa.rec = sc.rec;
         pa.tap_pass = aa.tap_pass;
+        pa.pos0 = pos0;
+        if (!h->q8) {
+            const SlotDesc &d = h->tab_host[((size_t)q.seq[0] * h->n_ord + l.ord) * kMaxLoops + slot];
+            pa.kring = d.k; pa.vring = d.v; pa.cap = d.cap;
+        }
+        pa.kvtap = h->kvtap; pa.kvtap_n = q.T;
         LAUNCH(launch_prep(pa, M, q.s));
         bool field = false;
         if (h->q8) {

@@ -17,14 +17,41 @@ __device__ __forceinline__ bool field_on(const AttnArgs &a, const RowRec &row) {
 // dory.rs `attn_layer` (rotate, justnorm per head, q times sq), with the RoPE
 // table row of the position (dory.rs `stack`: cos half, sin half).  One wave
 // per (row, head); lane j owns the pairs (j, j + hd/2), (j + 64, j + 64 + hd/2).
+// Every load is issued first and unconditionally (clamped, masked at use), and
+// nothing is read from the record or the slot table (the host passes the
+// chunk's first position and the slot's rings): one round trip a wave, where
+// the record, slot and value-row reads had made six.
 __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
     const int r = blockIdx.x, hh = blockIdx.y, lane = threadIdx.x;
     const int hd = a.hd, half = hd / 2, Q = a.nh * hd, KV = a.nk * hd;
     const int ld = Q + 2 * KV + Q;
-    const int64_t p = a.rec->rows[r].pos;
+    const int64_t p = a.pos0 + r;
     const bool isq = hh < a.nh;
     const int kh = hh - a.nh;
     const float *src = a.qkvg + (size_t)r * ld + (isq ? hh * hd : Q + kh * hd);
+    const float *vsrc = a.qkvg + (size_t)r * ld + Q + KV + (isq ? 0 : kh) * hd;  // the value row
+    const float *rp = a.rope + (size_t)p * hd;
+    const float *sqh = a.sq + (size_t)(isq ? hh : 0) * hd;
+    float x[2], y[2], cs[2], sn[2], q0[2], q1[2], vv[4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int j = lane + 64 * i, jc = j < half ? j : 0;
+        x[i] = src[jc];
+        y[i] = src[jc + half];
+        cs[i] = rp[jc];
+        sn[i] = rp[half + jc];
+        q0[i] = sqh[jc];
+        q1[i] = sqh[jc + half];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = lane + 64 * i;
+        vv[i] = vsrc[j < hd ? j : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) asm volatile("" ::"v"(x[i]), "v"(y[i]), "v"(cs[i]), "v"(sn[i]), "v"(q0[i]), "v"(q1[i]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" ::"v"(vv[i]));
     float nx[2], ny[2];
     float s = 0.f;
 #pragma unroll
@@ -32,17 +59,14 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
         const int j = lane + 64 * i;
         nx[i] = ny[i] = 0.f;
         if (j < half) {
-            const float cs = a.rope[(size_t)p * hd + j], sn = a.rope[(size_t)p * hd + half + j];
-            const float x = src[j], y = src[j + half];
-            nx[i] = x * cs - y * sn;
-            ny[i] = y * cs + x * sn;
+            nx[i] = x[i] * cs[i] - y[i] * sn[i];
+            ny[i] = y[i] * cs[i] + x[i] * sn[i];
             s += nx[i] * nx[i] + ny[i] * ny[i];
         }
     }
     const float f = norm_factor(wave_sum(s));
-    if (!isq && a.rec->kvtap) {  // test tap: the row's key and value before the cache write
-        float *t = a.rec->kvtap + ((size_t)a.tap_pass * a.rec->n + r) * 2 * KV + kh * hd;
-        const float *vs = a.qkvg + (size_t)r * ld + Q + KV + kh * hd;
+    if (!isq && a.kvtap) {  // test tap: the row's key and value before the cache write
+        float *t = a.kvtap + ((size_t)a.tap_pass * a.kvtap_n + r) * 2 * KV + kh * hd;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int j = lane + 64 * i;
@@ -51,17 +75,18 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
                 t[j + half] = ny[i] * f;
             }
         }
-        for (int j = lane; j < hd; j += 64) t[KV + j] = vs[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (lane + 64 * i < hd) t[KV + lane + 64 * i] = vv[i];
     }
     if (isq) {
         float *dst = a.qp + (size_t)r * Q + hh * hd;
-        const float *sq = a.sq + hh * hd;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int j = lane + 64 * i;
             if (j < half) {
-                dst[j] = nx[i] * f * sq[j];
-                dst[j + half] = ny[i] * f * sq[j + half];
+                dst[j] = nx[i] * f * q0[i];
+                dst[j + half] = ny[i] * f * q1[i];
             }
         }
         return;
@@ -78,9 +103,8 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
         }
         return;
     }
-    const SlotDesc &sd = slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot);
-    const size_t row = (size_t)kh * sd.cap + (size_t)(p % sd.cap);
-    float *kd = sd.k + row * hd;
+    const size_t row = (size_t)kh * a.cap + (size_t)(p % a.cap);
+    float *kd = a.kring + row * hd;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int j = lane + 64 * i;
@@ -89,9 +113,10 @@ __global__ __launch_bounds__(64) void k_prep(PrepArgs a) {
             kd[j + half] = ny[i] * f;
         }
     }
-    const float *v = a.qkvg + (size_t)r * ld + Q + KV + kh * hd;
-    float *vd = sd.v + row * hd;
-    for (int j = lane; j < hd; j += 64) vd[j] = v[j];
+    float *vd = a.vring + row * hd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < hd) vd[lane + 64 * i] = vv[i];
 }
 
 
@@ -1258,6 +1283,8 @@ hipError_t launch_hd(const AttnArgs &a, int T, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
+    if (a.hd > 256 || a.hd % 2 || (!a.kstage && (!a.kring || !a.vring || a.cap < 1)) || (a.kvtap && a.kvtap_n < T))
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_prep, dim3(T, a.nh + a.nk), dim3(64), 0, s, a);
     return hipGetLastError();
 }

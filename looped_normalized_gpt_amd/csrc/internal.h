@@ -220,6 +220,14 @@ struct PrepArgs {
     int32_t nh, nk, hd;
     const CallRec *rec;
     int32_t tap_pass;    // the call's attention pass (for the record's kvtap)
+    // A chunk of one sequence is never captured in a graph, so what the kernel
+    // would read from the record and the slot table (tab .. slot, rec: kept for
+    // checking) comes from the host as it set them for this call:
+    int64_t pos0;        // position of row 0 (rows at pos0 .. pos0+T-1)
+    float *kring, *vring;  // fp32 cache: the slot's rings [nk][cap][hd] (unused with kstage)
+    int32_t cap;
+    float *kvtap;        // the record's kv tap, or null; rows of kvtap_n
+    int32_t kvtap_n;
 };
 hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s);
 

@@ -538,6 +538,9 @@ hipError_t launch_gemm_swiglu(const uint16_t *Ab, int lda, const void *wgate, co
 
 hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
     const int Q = a.nh * a.hd, KV = a.nk * a.hd, ld = 2 * Q + 2 * KV;
+    if (a.hd > 256 || a.hd % 2 || (!a.kstage && (!a.kring || !a.vring || a.cap < 1)) || (a.kvtap && a.kvtap_n < T))
+        return hipErrorInvalidValue;
+    if (fake::capturing) fake::violation("a chunk's prep in a graph: its position and ring arguments would go stale");
     auto stat = [=]() {
         need("prep projections", a.qkvg, (size_t)T * ld * 4);
         need("prep queries", a.qp, (size_t)T * Q * 4);
@@ -546,12 +549,21 @@ hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
     };
     auto dyn = [=]() {
         fake::need_record(a.rec, T);
+        if (a.kvtap != a.rec->kvtap || (a.kvtap && a.kvtap_n != a.rec->n))
+            fake::violation("the prep's kv tap arguments differ from the record's");
         for (int r = 0; r < T; ++r) {
             const RowRec &row = a.rec->rows[r];
+            if (row.pos != a.pos0 + r) fake::violation("prep row " + std::to_string(r) + " is not at pos0 + r");
             need("RoPE row", a.rope + (size_t)row.pos * a.hd, (size_t)a.hd * 4);
-            if (!a.kstage) fake::slot(a.tab, row.seq, a.n_ord, a.ord, a.slot, a.nk, a.hd, false);
-            if (a.rec->kvtap)
-                need("kv tap", a.rec->kvtap + ((size_t)a.tap_pass * a.rec->n + r) * 2 * KV, (size_t)2 * KV * 4);
+            if (!a.kstage) {
+                const SlotDesc *d = fake::slot(a.tab, row.seq, a.n_ord, a.ord, a.slot, a.nk, a.hd, false);
+                if (d && (d->k != a.kring || d->v != a.vring || d->cap != a.cap))
+                    fake::violation("the prep's ring arguments differ from the row's slot");
+                const size_t ring = (size_t)(a.nk - 1) * a.cap + (size_t)(row.pos % a.cap);
+                need("prep key ring row", a.kring, (ring + 1) * a.hd * 4);
+                need("prep value ring row", a.vring, (ring + 1) * a.hd * 4);
+            }
+            if (a.kvtap) need("kv tap", a.kvtap + ((size_t)a.tap_pass * a.kvtap_n + r) * 2 * KV, (size_t)2 * KV * 4);
         }
     };
     return fake::launch("launch_prep", stat, dyn);
