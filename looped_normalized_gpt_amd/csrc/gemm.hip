@@ -228,12 +228,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
         const int am = m0 + 32 * i + lr < M ? m0 + 32 * i + lr : M - 1;
         arow[i] = A + (size_t)am * lda + kz + lc;
         if (SWIGLU) {  // tile column c: gate row 64x + c, or up row 64x + c - 64
+            // (a select of the two pointers: indexing W.w by the lane's column
+            // made the compiler reload them from the argument block and wait)
             const int c = 32 * i + lr;
-            brow[i] = reinterpret_cast<const uint16_t *>(W.w[c < 64 ? 0 : 1]) +
-                      (size_t)(blockIdx.x * 64 + (c & 63)) * K + kz + lc;
+            const void *wsel = c < 64 ? W.w[0] : W.w[1];
+            brow[i] = reinterpret_cast<const uint16_t *>(wsel) + (size_t)(blockIdx.x * 64 + (c & 63)) * K + kz + lc;
         } else {
             const int bn = n0 + 32 * i + lr < N ? n0 + 32 * i + lr : N - 1;
             brow[i] = seg_row<uint16_t>(W, bn, K) + kz + lc;
+        }
+    }
+    // the SwiGLU epilogue's gate and up scales, loaded with the first tiles
+    // (after the loop they cost a round trip of their own)
+    float sgv[2] = {0.f, 0.f}, suv[2] = {0.f, 0.f};
+    if constexpr (SWIGLU) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            sgv[j] = sg[blockIdx.x * 64 + j * 32 + (lane & 31)];
+            suv[j] = su[blockIdx.x * 64 + j * 32 + (lane & 31)];
         }
     }
     u32x4_t ra0[4], rb0[4];
@@ -316,12 +328,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_mfma2(const uint16_t *__restric
         }
         __syncthreads();
         const int F = N / 2, x = blockIdx.x;
-        float sgv[2], suv[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            sgv[j] = sg[x * 64 + j * 32 + (lane & 31)];
-            suv[j] = su[x * 64 + j * 32 + (lane & 31)];
-        }
         const int i = wn;  // the 32-row tile this wave finishes
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
