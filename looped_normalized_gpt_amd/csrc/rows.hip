@@ -163,10 +163,18 @@ __global__ __launch_bounds__(256) void k_rownorm_v(const float *src, int ld, flo
     const float *x = src + (size_t)blockIdx.x * ld;
     float4 v[G];
     float s = 0.f;
+    // every load before any use (computing each group as it arrived waited
+    // for the groups one at a time)
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const int i = 4 * (threadIdx.x + 256 * j);
         v[j] = *reinterpret_cast<const float4 *>(x + (i < N ? i : 0));
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) asm volatile("" ::"v"(v[j].x), "v"(v[j].w));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int i = 4 * (threadIdx.x + 256 * j);
         if (i >= N) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         s += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
     }
@@ -191,13 +199,25 @@ __global__ __launch_bounds__(256) void k_swiglu_norm_v(const float *a, const flo
     const size_t offi = (size_t)blockIdx.x * ld, off = (size_t)blockIdx.x * F;
     float4 z[G];
     float s = 0.f;
+    // every load before any use (computing each group as it arrived waited
+    // for the groups one at a time)
+    float4 la[G], lb[G], lg[G], lu[G];
 #pragma unroll
     for (int j = 0; j < G; ++j) {
         const int i = 4 * (threadIdx.x + 256 * j), ic = i < F ? i : 0;
-        const float4 va = *reinterpret_cast<const float4 *>(a + offi + ic);
-        const float4 vb = *reinterpret_cast<const float4 *>(b + offi + ic);
-        const float4 vg = *reinterpret_cast<const float4 *>(sg + ic);
-        const float4 vu = *reinterpret_cast<const float4 *>(su + ic);
+        la[j] = *reinterpret_cast<const float4 *>(a + offi + ic);
+        lb[j] = *reinterpret_cast<const float4 *>(b + offi + ic);
+        lg[j] = *reinterpret_cast<const float4 *>(sg + ic);
+        lu[j] = *reinterpret_cast<const float4 *>(su + ic);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        asm volatile("" ::"v"(la[j].x), "v"(la[j].w), "v"(lb[j].x), "v"(lb[j].w), "v"(lg[j].x), "v"(lg[j].w),
+                     "v"(lu[j].x), "v"(lu[j].w));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        const int i = 4 * (threadIdx.x + 256 * j);
+        const float4 va = la[j], vb = lb[j], vg = lg[j], vu = lu[j];
         const float ga[4] = {va.x * vg.x, va.y * vg.y, va.z * vg.z, va.w * vg.w};
         const float ub[4] = {vb.x * vu.x, vb.y * vu.y, vb.z * vu.z, vb.w * vu.w};
         float zz[4];
