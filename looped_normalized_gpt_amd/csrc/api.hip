@@ -534,6 +534,9 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         }
         chunk_split(h, pos0, M, aa);
         aa.field = field;
+        aa.pos0 = pos0;
+        aa.nrows = q.T;
+        aa.sdc = h->tab_host[((size_t)q.seq[0] * h->n_ord + l.ord) * kMaxLoops + slot];
         LAUNCH(launch_attn(aa, M, q.s));
     }
     if (q.T == 1) {
@@ -1516,6 +1519,9 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
         default:
             chunk_split(h, h->last_pos0, h->last_T, aa);
             aa.field = h->q8 && h->last_pos0 >= kWarmup + 1;
+            aa.pos0 = h->last_pos0;
+            aa.nrows = h->last_T;
+            aa.sdc = h->tab_host[((size_t)h->last_seq0 * h->n_ord + l->ord) * kMaxLoops + aa.slot];
             e = launch_attn(aa, h->last_T, s);
             break;
         }

@@ -218,7 +218,10 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a) {
 // arithmetic.  Wave w takes splits w, w+4, ... (4 at a time in flight), lane l
 // the CPL channels l*CPL .. of the group's REP*HD (one head); the 4 waves'
 // running (max, sum, acc) are then combined through LDS.
-template <int Q8, int HD, int REP>
+// MODE: 0 the decode kernel's partials (a.dec), 1 a chunk's (a.blk > 0), 2 the
+// one-row-per-workgroup kernel's: a compile-time choice, so no path loads what
+// only another needs (a hoisted read of the record cost a round trip).
+template <int Q8, int HD, int REP, int MODE>
 __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
     constexpr int CH = REP * HD, CPL = CH >= 64 ? CH / 64 : 1;
     static_assert(CH % 64 == 0 || CH < 64, "channels split evenly over the lanes");
@@ -227,16 +230,25 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
     const int r = blockIdx.x, kh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Q = a.nh * HD, ld = 2 * Q + 2 * a.nk * HD;
-    const int64_t p = a.rec->rows[r].pos;
+    // the gate and its scale of this thread's channels, loaded first (after
+    // the barrier below they took a round trip of their own)
+    float gpre[(CH + 255) / 256], spre[(CH + 255) / 256];
+#pragma unroll
+    for (int k = 0; k < (CH + 255) / 256; ++k) {
+        const int c = tid + 256 * k < CH ? tid + 256 * k : 0, hq = kh * REP + c / HD, d = c % HD;
+        gpre[k] = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * HD + hq * HD + d];
+        spre[k] = a.sg[hq * HD + d];
+    }
     int nsplit;
-    if (a.dec) {  // decode kernel: every slab of the grid, those past the row's keys hold max -inf
+    if constexpr (MODE == 0) {  // decode kernel: every slab of the grid, those past the row's keys hold max -inf
         nsplit = a.max_split;
-    } else if (a.blk > 0) {
-        const int rb0 = r / a.blk * a.blk, rb1 = (rb0 + a.blk < a.rec->n ? rb0 + a.blk : a.rec->n) - 1;
-        const int64_t pos0 = a.rec->rows[0].pos;
+    } else if constexpr (MODE == 1) {  // a chunk: its first position and rows come from the host
+        const int rb0 = r / a.blk * a.blk, rb1 = (rb0 + a.blk < a.nrows ? rb0 + a.blk : a.nrows) - 1;
+        const int64_t pos0 = a.pos0;
         const int64_t klo = pos0 + rb0 + 1 - a.window > 0 ? pos0 + rb0 + 1 - a.window : 0;
         nsplit = (int)((pos0 + rb1 - klo + a.split) / a.split);
     } else {
+        const int64_t p = a.rec->rows[r].pos;
         const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
         nsplit = (int)((p - lo + 1 + a.split - 1) / a.split);
     }
@@ -293,7 +305,10 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
     __syncthreads();
     const bool field = Q8 && field_on(a, a.rec->rows[r]);
     float ss = 0.f;
-    for (int c = tid; c < CH; c += 256) {
+#pragma unroll
+    for (int k = 0; k < (CH + 255) / 256; ++k) {
+        const int c = tid + 256 * k;
+        if (c >= CH) break;
         const int ln = c / CPL, hh = c / HD, d = c % HD, hq = kh * REP + hh;
         float Mt = -INFINITY;
 #pragma unroll
@@ -306,10 +321,11 @@ __global__ __launch_bounds__(256) void k_attn_merge_rows(AttnArgs a) {
             Lt += wl[w][ln] * e;
             y += wacc[w][c] * e;
         }
-        const float vcol = field ? slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot).vcol[kh * HD + d] : 1.f;
-        const float gate = a.qkvg[(size_t)r * ld + Q + 2 * a.nk * HD + hq * HD + d];
+        const float vcol =
+            field ? (MODE == 1 ? a.sdc : slot_at(a.tab, a.rec->rows[r].seq, a.n_ord, a.ord, a.slot)).vcol[kh * HD + d]
+                  : 1.f;
         y = y / Lt * vcol;
-        const float zv = y / (1.0f + expf(-(gate * a.sg[hq * HD + d])));
+        const float zv = y / (1.0f + expf(-(gpre[k] * spre[k])));
         a.z[(size_t)r * Q + hq * HD + d] = zv;
         if (a.zb) a.zb[(size_t)r * Q + hq * HD + d] = f2bf(zv);
         ss += zv * zv;
@@ -974,17 +990,16 @@ __global__ __launch_bounds__(256, Q8 ? 1 : 2) void k_fattn(AttnArgs a) {
     __shared__ __bf16 Vt[2][HD][VP];
     const int s = blockIdx.x, kh = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-    const CallRec *rec = a.rec;
-    const int T = rec->n;
+    const int T = a.nrows;
     const int r0 = b * BQ, r1 = (r0 + BQ < T ? r0 + BQ : T) - 1;
-    const int64_t pos0 = rec->rows[0].pos;
+    const int64_t pos0 = a.pos0;
     const int64_t klo = pos0 + r0 + 1 - a.window > 0 ? pos0 + r0 + 1 - a.window : 0;
     const int64_t khi = pos0 + r1;
     const int64_t eb = klo + (int64_t)s * a.split;
     if (eb > khi) return;
     const int64_t ee = eb + a.split - 1 < khi ? eb + a.split - 1 : khi;  // last key of the split
     const int ntiles = (int)((ee - eb + KT) / KT);
-    const SlotDesc &sd = slot_at(a.tab, rec->rows[0].seq, a.n_ord, a.ord, a.slot);
+    const SlotDesc &sd = a.sdc;
     const int cap = sd.cap;
     const int Q = a.nh * HD;
 
@@ -1251,8 +1266,15 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
         }
     } else {
         dim3 mgrid(rows, a.nk);
-        if (a.q8) hipLaunchKernelGGL((k_attn_merge_rows<1, HD, REP>), mgrid, dim3(256), 0, s, a);
-        else hipLaunchKernelGGL((k_attn_merge_rows<0, HD, REP>), mgrid, dim3(256), 0, s, a);
+#define DK_MERGE_ROWS(MODE)                                                                          \
+    do {                                                                                             \
+        if (a.q8) hipLaunchKernelGGL((k_attn_merge_rows<1, HD, REP, MODE>), mgrid, dim3(256), 0, s, a); \
+        else hipLaunchKernelGGL((k_attn_merge_rows<0, HD, REP, MODE>), mgrid, dim3(256), 0, s, a);      \
+    } while (0)
+        if (a.dec) DK_MERGE_ROWS(0);
+        else if (a.blk > 0) DK_MERGE_ROWS(1);
+        else DK_MERGE_ROWS(2);
+#undef DK_MERGE_ROWS
     }
     return hipGetLastError();
 }

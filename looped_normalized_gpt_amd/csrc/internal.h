@@ -267,6 +267,12 @@ struct AttnArgs {
     int32_t dec;         // 1: the decode kernel (launch_attn_dec), whose merge reads all
                          // max_split slabs of a row; 0: the multi-row kernels
     int32_t tap_pass;    // decode kernels: the call's attention pass (for the record's kvtap)
+    // Multi-row chunks of one sequence (k_fattn and its merge; never captured
+    // in a graph): what these kernels would read from the record and the slot
+    // table, as the host set them for this call.
+    int64_t pos0;        // the chunk's first position (the record's rows[0].pos)
+    int32_t nrows;       // the call's rows (the record's n)
+    SlotDesc sdc;        // the sequence's slot
 };
 // Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);

@@ -573,6 +573,8 @@ hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
 // position; chunk: consecutive positions of one sequence).
 static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool dec) {
     const int Q = a.nh * a.hd, KV = a.nk * a.hd, ld = 2 * Q + 2 * KV, rep = a.nh / a.nk;
+    if (!dec && a.blk > 0 && fake::capturing)
+        fake::violation("a chunk's attention in a graph: its position, row and slot arguments would go stale");
     auto stat = [=]() {
         need("attention sg", a.sg, (size_t)Q * 4);
         need("attention z", a.z, (size_t)T * Q * 4);
@@ -614,6 +616,14 @@ static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool d
             fake::keys_held(d, lo, p, dec ? p : pos0 + T - 1);
         }
         if (!dec && a.blk > 0) {
+            // the chunk kernels take these from the arguments, not the record
+            if (a.pos0 != pos0 || a.nrows != rec->n)
+                fake::violation("the chunk attention's position or row arguments differ from the record's");
+            const SlotDesc &e = slot_at(a.tab, rec->rows[0].seq, a.n_ord, a.ord, a.slot);
+            const SlotDesc &c = a.sdc;
+            if (c.k != e.k || c.v != e.v || c.kc != e.kc || c.vc != e.vc || c.ks != e.ks || c.vs != e.vs ||
+                c.kcol != e.kcol || c.vcol != e.vcol || c.cap != e.cap)
+                fake::violation("the chunk attention's slot argument differs from the table's entry");
             const int nb = (T + a.blk - 1) / a.blk;
             for (int b = 0; b < nb; ++b) {
                 const int rb0 = b * a.blk, rb1 = (rb0 + a.blk < T ? rb0 + a.blk : T) - 1;
