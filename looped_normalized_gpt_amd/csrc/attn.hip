@@ -1046,6 +1046,25 @@ __global__ __launch_bounds__(256, Q8 ? 1 : 2) void k_fattn(AttnArgs a) {
         const int t0 = (int)eb + tile * KT;
         const int rb = (int)((unsigned)t0 % (unsigned)cap);
         const int last = (int)ee - t0;
+        if (!Q8 && rb + KT <= cap && last >= KT - 1) {
+            // the common tile (no ring wrap, every key inside the split): key k
+            // sits at row rb + k, so one 32-bit offset for the tile and a fixed
+            // one per key (the per-key wrap and 64-bit row arithmetic below were
+            // ~20% of the kernel's VALU work)
+            // (byte offsets in 32 bits: the loads then take the ring's base as a
+            // scalar and the offset as a 32-bit register, no 64-bit adds)
+            const uint32_t tb = ((uint32_t)kh * (uint32_t)cap + (uint32_t)rb) * (HD * 4);
+            const char *kb = reinterpret_cast<const char *>(sd.k), *vb = reinterpret_cast<const char *>(sd.v);
+#pragma unroll
+            for (int i = 0; i < KPASS; ++i)
+                kr[i] = gld4(reinterpret_cast<const float *>(kb + (tb + (uint32_t)(((lk + KL * i) * HD + 4 * lc) * 4))));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int kk = 16 * (vci >> 1) + 8 * (j >> 2) + 4 * (vci & 1) + (j & 3);
+                vr[0][j] = gld4(reinterpret_cast<const float *>(vb + (tb + (uint32_t)((kk * HD + 4 * vlc) * 4))));
+            }
+            return;
+        }
         auto key_row = [&](int k) -> size_t {
             int rr = rb + (k < last ? k : last);
             rr = rr >= cap ? rr - cap : rr;
