@@ -91,6 +91,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     extern __shared__ float smem[];
     constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
     constexpr int EPT = 8 * MAXC;  // prologue elements per thread: K <= 2048 * MAXC
+    static_assert(ROWS >= 1 && ROWS <= 64 && (ROWS & (ROWS - 1)) == 0, "ROWS: a power of two");
     float *xs = smem;              // [K]
     float *red = smem + a.K;       // [16]: two reduction slots
     float *part = red + 16;        // [4][WR]
@@ -153,6 +154,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         }
     }
 
+    // The epilogue's per-row scalars, the head's output row and the record's tap
+    // pointer, read now with the prologue's inputs: read where they are used,
+    // each would add a round trip to the workgroup (the tap's after the whole
+    // weight stream).  Every lane reads (the row of lane tid % ROWS, clamped).
+    float e0 = 0.f, e1 = 0.f;
+    int32_t out_row = 0;
+    float *tap = nullptr;
+    {
+        const int en = row0 + (tid & (ROWS - 1));
+        const int enc = en < N ? en : row0;
+        if (EPI == kEpiPair) {
+            e0 = a.sg[enc];
+            e1 = a.su[enc];
+        } else if (EPI == kEpiHead) {
+            e0 = a.logit_scale[enc];
+            out_row = rec->rows[a.row].out;
+        }
+        if (RES) {
+            float *t = rec->tap;
+            const int tn = rec->n;
+            tap = blockIdx.x == 0 && rs.tap_pass >= 0 && t ? t + ((size_t)rs.tap_pass * tn + a.row) * K : nullptr;
+        }
+    }
+
     // 2. Weight rows of this workgroup, every load issued now (the prologue runs
     // while they fly).  Rows past N and chunks past K re-read a valid address
     // and are masked at use.
@@ -183,6 +208,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
 #pragma unroll
         for (int j = 0; j < WR; ++j) wv[j][c].load(base[j], roff[j] + kc);
     }
+    // Nothing below moves above this point: the weight loads stay ahead of the
+    // prologue's waits.
+    __builtin_amdgcn_sched_barrier(0);
     // Pin the prologue's inputs here: otherwise the compiler sinks their loads
     // into the branches of the prologue that use them, behind the weight loads,
     // and the prologue then waits for every weight load.
@@ -192,6 +220,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         if (RES) asm volatile("" ::"v"(po[j]), "v"(pa[j]));
         if (PRO == kProResolveInp) asm volatile("" ::"v"(pi[j]));
     }
+    asm volatile("" ::"v"(e0), "v"(e1), "v"(out_row), "v"(tap));
 
     // 3. x in LDS.
     if (RES) {
@@ -200,8 +229,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
             if (4 * tid + 1024 * jj >= K)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) ph[4 * jj + c] = po[4 * jj + c] = pa[4 * jj + c] = pi[4 * jj + c] = 0.f;
-        resolve_regs<EPT>(rs, a.row, K, ph, po, pa, pi, xs, red, blockIdx.x == 0,
-                          blockIdx.x == 0 ? tap_row(rec, rs.tap_pass, a.row, K) : nullptr);
+        resolve_regs<EPT>(rs, a.row, K, ph, po, pa, pi, xs, red, blockIdx.x == 0, tap);
     } else {
         float f = 1.f;
         if (PRO == kProNorm) {
@@ -250,10 +278,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
             } else if (EPI == kEpiPair) {
                 const int j = ROWS + tid;
                 float b = part[j] + part[WR + j] + part[2 * WR + j] + part[3 * WR + j];
-                float g = v * a.sg[n];
-                a.y[n] = g / (1.0f + expf(-g)) * (b * a.su[n]);
+                float g = v * e0;
+                a.y[n] = g / (1.0f + expf(-g)) * (b * e1);
             } else {
-                rec->logits[(size_t)rec->rows[a.row].out * N + n] = v * a.logit_scale[n];
+                rec->logits[(size_t)out_row * N + n] = v * e0;
             }
         }
     }
