@@ -226,6 +226,15 @@ int dory_latched(const dory_t *h, int32_t seq);
  * Nothing faults on the device. */
 int dory_debug_fail_launch(dory_t *h, int64_t n);
 
+/* Test hook: one-row calls merge the sliding layers' attention splits inside
+ * the attention kernel, per kv head within one XCD, where a check at
+ * dory_create found every workgroup id of one residue mod 8 on one XCD;
+ * elsewhere, and for full layers, a merge kernel of its own does it.  on = 0
+ * selects the merge kernel for every layer, 1 the default, -1 leaves it as it
+ * is; changing it drops the captured graphs.  Returns 1 if the in-kernel merge
+ * is in use after the call, 0 if not, DORY_EINVAL for a bad handle or on. */
+int dory_debug_xcd_merge(dory_t *h, int on);
+
 /* Test tap: later calls also write the residual state after every sub-layer pass
  * to buf, device fp32 [passes][n][hidden] with passes = n_in + n_rec*loops +
  * n_out.  cap is buf's size in floats; a call that needs more fails with

@@ -122,6 +122,12 @@ struct dory {
     float *tap = nullptr;
     int64_t tap_cap = 0;
     float *kvtap = nullptr;  // test tap of the pre-encode cache rows (dory_debug_kv_tap)
+    // One-row calls' sliding layers merge their attention splits inside the
+    // attention kernel (per kv head within one XCD): the kernel's arrival
+    // counters, and whether the create-time XCD check allowed it (xm) and a
+    // test has not turned it off (xm_off)
+    uint32_t *xcnt = nullptr;
+    bool xm = false, xm_off = false;
     int64_t kvtap_cap = 0;
     std::vector<SeqState> seqs;
     std::string err;
@@ -335,7 +341,8 @@ size_t carve_scratch(const dory_t *h, int rows, char *base, Scratch *out) {
     sc.ga = (float *)take(4 * T * 2 * F);
     sc.un = (float *)take(4 * T * F);
     sc.kstage = (float *)take(4 * T * KV);
-    sc.part = (float *)take(4 * std::max((size_t)h->ms_dec, T * h->ms_pf) * h->nk * rep * (h->hd + 2));
+    sc.part = (float *)take(4 * std::max(std::max((size_t)h->ms_dec, T * h->ms_pf) * h->nk * rep * (h->hd + 2),
+                                         attn_xm_part_floats(h->nk, h->ms_ds, (int)rep, h->hd)));
     sc.zss = (float *)take(4 * T * h->nk);
     sc.uss = (float *)take(4 * T);
     sc.ussp = h->F % 64 == 0 ? (float *)take(4 * T * (F / 64)) : nullptr;
@@ -483,6 +490,7 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
             aa.split = l.sliding ? h->split_ds : h->split_df;
             aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
             aa.sd1 = h->tab + ((size_t)q.seq[0] * h->n_ord + l.ord) * kMaxLoops + slot;
+            if (l.sliding && h->xm && !h->xm_off) aa.xcnt = h->xcnt;
         } else {
             aa.split = l.sliding ? h->split_bs : h->split_bf;
             aa.max_split = l.sliding ? h->ms_bs : h->ms_bf;
@@ -853,7 +861,8 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     const size_t rep = h->nh / h->nk;
     // decode rows (one per sequence of a batch) or the rows of a chunk
     const size_t dec_rows = std::min(chunk, cfg->max_seqs);
-    const size_t part = std::max(dec_rows * h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2);
+    const size_t part = std::max(std::max(dec_rows * h->ms_dec, (size_t)chunk * h->ms_pf) * h->nk * rep * (h->hd + 2),
+                                 attn_xm_part_floats(h->nk, h->ms_ds, (int)rep, h->hd));
     CREATE_CHECK(dmalloc(h, &h->sc.part, part));
     CREATE_CHECK(dmalloc(h, &h->tab, h->tab_host.size()));
     CREATE_CHECK(hipMemset(h->tab, 0, sizeof(SlotDesc) * h->tab_host.size()));
@@ -878,6 +887,26 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
             float *&dst = kind == 0 ? h->rope_s : h->rope_f;
             CREATE_CHECK(dmalloc(h, &dst, tab.size()));
             CREATE_CHECK(hipMemcpy(dst, tab.data(), sizeof(float) * tab.size(), hipMemcpyHostToDevice));
+        }
+    }
+    // The in-kernel merge of the sliding layers' one-row attention (head dim
+    // 128, at most 64 splits) needs every workgroup id of one residue mod 8 on
+    // one XCD: checked once on this device over the grid it launches (else the
+    // merge kernel serves, as for the full layers).
+    if (h->hd == 128 && h->ms_ds <= 64 && h->split_ds <= 64) {
+        const int G = 8 * h->ms_ds * ((h->nk + 7) / 8);
+        unsigned *ids = nullptr;
+        CREATE_CHECK(dmalloc(h, &ids, (size_t)G));
+        CREATE_CHECK(launch_xcd_check(ids, G, nullptr));
+        std::vector<unsigned> got(G);
+        CREATE_CHECK(hipMemcpy(got.data(), ids, sizeof(unsigned) * G, hipMemcpyDeviceToHost));
+        bool same = true;
+        for (int i = 8; i < G; ++i) same = same && got[i] == got[i % 8];
+        if (same) {
+            CREATE_CHECK(dmalloc(h, &h->xcnt, (size_t)32 * h->nk));
+            CREATE_CHECK(hipMemset(h->xcnt, 0, sizeof(uint32_t) * 32 * h->nk));
+            CREATE_CHECK(hipDeviceSynchronize());
+            h->xm = true;
         }
     }
     CREATE_CHECK(hipHostMalloc((void **)&h->stage, h->rec_sz * kStages, hipHostMallocDefault));
@@ -1290,6 +1319,22 @@ int dory_debug_fail_launch(dory_t *h, int64_t n) {
     return DORY_OK;
 }
 
+int dory_debug_xcd_merge(dory_t *h, int on) {
+    if (!h) return DORY_EINVAL;
+    if (on == 0 || on == 1) {
+        if (h->xm_off != (on == 0)) {
+            // captured graphs hold the other path's launches
+            (void)hipDeviceSynchronize();
+            for (auto &g : h->graphs) (void)hipGraphExecDestroy(g.second);
+            h->graphs.clear();
+        }
+        h->xm_off = on == 0;
+    } else if (on != -1) {
+        return fail(h, DORY_EINVAL, "dory_debug_xcd_merge: on must be 0, 1 or -1");
+    }
+    return h->xm && !h->xm_off ? 1 : 0;
+}
+
 int dory_latched(const dory_t *h, int32_t seq) {
     if (!h || seq < 0 || seq >= h->cfg.max_seqs) return DORY_EINVAL;
     return h->seqs[seq].latched ? 1 : 0;
@@ -1477,6 +1522,7 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             aa.split = h->last_T == 1 ? (l->sliding ? h->split_ds : h->split_df) : (l->sliding ? h->split_bs : h->split_bf);
             aa.max_split = h->last_T == 1 ? (l->sliding ? h->ms_ds : h->ms_df) : (l->sliding ? h->ms_bs : h->ms_bf);
             if (h->last_T == 1) aa.sd1 = h->tab + ((size_t)h->last_seq0 * h->n_ord + l->ord) * kMaxLoops + aa.slot;
+            if (h->last_T == 1 && l->sliding && h->xm && !h->xm_off) aa.xcnt = h->xcnt;
             aa.field = -1;
             e = launch_attn_dec(aa, h->last_T, s);
             break;

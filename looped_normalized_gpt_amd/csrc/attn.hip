@@ -746,42 +746,41 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
 //      query from LDS, and the softmax of the head's 64 keys stays in the wave.
 //   3. Lane l accumulates channels 2l, 2l+1 over the 64 keys, taking each
 //      key's weight from its lane (readlane), and stores the partial.
-template <int REP, int Q8>
+// XM = 1 (one row, a.xcnt set): the splits are merged in the kernel, inside
+// one XCD.  A 1-D grid whose workgroup L runs on XCD L % 8 (the dispatcher
+// deals workgroups to the XCDs in turn; launch_xcd_check confirms it at
+// create) gives kv head kh the ids L = kh (mod 8), so the group's partials
+// meet in that XCD's L2, which every CU of the XCD shares.  Each workgroup
+// writes its partial, waits until the L2 has acknowledged the stores, and
+// takes a ticket from the group's counter (an L2 atomic); the last one reads
+// the group's partials past its L1 (sc0), merges them as k_attn_merge does,
+// applies the gate, writes z and clears the counter for the next launch.
+template <int REP, int Q8, int XM>
 __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
     constexpr int HD = 128, HALF = 64, NK = 64, KP = HD + 4, IT = NK / 8;
     constexpr int NGK = HD / kKGroup;
     constexpr int VPW = (REP + 1 + 3) / 4;  // vectors a wave prepares
-    __shared__ float Ks[NK][KP], Vs[NK][KP];
+    constexpr int HPW = (REP + 3) / 4;      // heads a wave merges (XM)
     __shared__ float qs[REP + 1][HD];  // queries (times the key field and 1/sqrt(hd)), then the new key
     __shared__ float vn[HD];
     __shared__ int8_t kcn[HD], vcn[HD];
     __shared__ float ksn[NGK], vsn[1];
-    const int s = blockIdx.x, kh = blockIdx.y, r = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const CallRec *rec = a.rec;
-    SlotDesc sd;
-    if (a.sd1) sd = *a.sd1;
-    else sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
-    const int64_t p = rec->rows[r].pos;
-    if (Q8) asm volatile("" ::"s"(sd.cap), "s"(sd.kc), "s"(sd.vc), "s"(sd.ks), "s"(sd.vs));
-    else asm volatile("" ::"s"(sd.cap), "s"(sd.k), "s"(sd.v));
-    const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
-    const int64_t nkeys = p - lo + 1;
-    const int nsplit = (int)((nkeys + a.split - 1) / a.split);
-    if (s >= nsplit) {  // no key here: the merge skips a slab whose max is -inf
-        if (tid < REP)
-            a.part[(((size_t)r * a.nk + kh) * a.max_split + s) * REP * (HD + 2) + (size_t)tid * (HD + 2)] = -INFINITY;
-        return;
+    __shared__ int xm_last;
+    int s, kh;
+    if (XM) {
+        const int L = blockIdx.x, j = L >> 3;
+        kh = (L & 7) + 8 * (j / a.max_split);
+        s = j % a.max_split;
+        if (kh >= a.nk) return;
+    } else {
+        s = blockIdx.x;
+        kh = blockIdx.y;
     }
-    const int64_t e0 = lo + (int64_t)s * a.split;
-    const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
-    const bool tail = s == nsplit - 1;
-    const bool field = Q8 && field_on(a, a.rec->rows[r]);
-    const int cap = sd.cap;
+    const int r = XM ? 0 : blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int Q = a.nh * HD, KV = a.nk * HD;
-    const int g = tid >> 5, dq = tid & 31;
-
-    // ---- 0. the prologue's inputs, then every cache row of the split
+    // ---- 0. the prologue's inputs (which do not depend on the row's position:
+    // issued before the record's read), then every cache row of the split
     const float *qrow = a.qkvg + (size_t)r * (2 * Q + 2 * KV);
     float x0[VPW], x1[VPW], s0[VPW], s1[VPW];
 #pragma unroll
@@ -795,7 +794,41 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         s1[i] = a.sq[(size_t)(kh * REP + vq) * HD + lane + HALF];
     }
     const float vr0 = qrow[Q + KV + (size_t)kh * HD + lane], vr1 = qrow[Q + KV + (size_t)kh * HD + lane + HALF];
+    // XM: what the merge applies to lane l's channels 2l, 2l+1 of head wave + 4i
+    // (the gate and its scale), read now in case this workgroup merges
+    float2 xg[HPW], xs[HPW];
+    if (XM) {
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int hq = kh * REP + (wave + 4 * i < REP ? wave + 4 * i : 0);
+            xg[i] = *reinterpret_cast<const float2 *>(qrow + Q + 2 * KV + (size_t)hq * HD + 2 * lane);
+            xs[i] = *reinterpret_cast<const float2 *>(a.sg + (size_t)hq * HD + 2 * lane);
+        }
+    }
+    const CallRec *rec = a.rec;
+    SlotDesc sd;
+    if (a.sd1) sd = *a.sd1;
+    else sd = slot_at(a.tab, rec->rows[r].seq, a.n_ord, a.ord, a.slot);
+    const int64_t p = rec->rows[r].pos;
+    if (Q8) asm volatile("" ::"s"(sd.cap), "s"(sd.kc), "s"(sd.vc), "s"(sd.ks), "s"(sd.vs));
+    else asm volatile("" ::"s"(sd.cap), "s"(sd.k), "s"(sd.v));
+    const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
+    const int64_t nkeys = p - lo + 1;
+    const int nsplit = (int)((nkeys + a.split - 1) / a.split);
+    if (s >= nsplit) {  // no key here: the merge skips a slab whose max is -inf (XM: not in the group)
+        if (!XM && tid < REP)
+            a.part[(((size_t)r * a.nk + kh) * a.max_split + s) * REP * (HD + 2) + (size_t)tid * (HD + 2)] = -INFINITY;
+        return;
+    }
+    const int64_t e0 = lo + (int64_t)s * a.split;
+    const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
+    const bool tail = s == nsplit - 1;
+    const bool field = Q8 && field_on(a, a.rec->rows[r]);
+    const int cap = sd.cap;
+    const int g = tid >> 5, dq = tid & 31;
     const float cs = a.rope[(size_t)p * HD + lane], sn = a.rope[(size_t)p * HD + HALF + lane];
+    float2 xv = make_float2(1.f, 1.f);  // XM: q8's V field of lane l's channels 2l, 2l+1
+    if (XM && Q8 && field) xv = *reinterpret_cast<const float2 *>(sd.vcol + (size_t)kh * HD + 2 * lane);
     const int rbase = (int)(e0 % cap);
     float4 kr[IT], vr[IT];
     float ksr[IT], vsr[IT];
@@ -889,68 +922,227 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         }
     }
 
-    // ---- 1. the split's rows to LDS
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int e = g + 8 * it;
-        float4 k = kr[it], v = vr[it];
-        if (Q8) {
-            k.x *= ksr[it]; k.y *= ksr[it]; k.z *= ksr[it]; k.w *= ksr[it];
-            v.x *= vsr[it]; v.y *= vsr[it]; v.z *= vsr[it]; v.w *= vsr[it];
-        }
-        *reinterpret_cast<float4 *>(&Ks[e][dq * 4]) = k;
-        *reinterpret_cast<float4 *>(&Vs[e][dq * 4]) = v;
-    }
-    __syncthreads();
-
-    // ---- 2, 3. per head: scores of lane e's key, softmax, values
     const size_t pstride = (size_t)REP * (HD + 2);
-    float *mine = a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride;
-    for (int h = wave; h < REP; h += 4) {
-        // LDS reads in batches, all issued before their first use (else the
-        // compiler keeps two in flight and waits on each pair)
-        float d = 0.f;
+    // XM: a group's slabs start on a 128-byte line of their own (no line is
+    // shared with another XCD's group)
+    const size_t gstride = ((size_t)a.max_split * pstride + 31) & ~(size_t)31;
+    float *mine = XM ? a.part + (size_t)kh * gstride + (size_t)s * pstride
+                     : a.part + (((size_t)r * a.nk + kh) * a.max_split + s) * pstride;
+    if constexpr (REP == 4) {
+        // ---- 1. scores from registers.  Lane (g, dq) holds channels 4dq..4dq+3
+        // of keys g + 8 it; its 32 partial products (value v = 4 it + h) are
+        // summed over the 32 lanes of its half wave by a reduce-scatter: each
+        // step pairs lanes that differ in one bit of dq (a DPP mirror, quad
+        // permute or the swizzle across rows), and each lane keeps the half of
+        // its values whose matching bit of v equals its own, adding its
+        // partner's copy.  After the five steps lane dq holds value v = dq: the
+        // score of key g + 8 (dq >> 2) for head dq & 3.
+        __shared__ float scs[REP][NK + 1];      // scores by head (padded row)
+        __shared__ float4 pw[NK];               // softmax weights by key, the 4 heads
+        __shared__ float red[8][REP][HD];       // per key group g: its sums of p * v
+        float4 q4[REP];
 #pragma unroll
-        for (int c0 = 0; c0 < HD; c0 += 32) {
-            float4 k[8], q[8];
+        for (int h = 0; h < REP; ++h) q4[h] = *reinterpret_cast<const float4 *>(&qs[h][dq * 4]);
+        float cur[32];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                k[i] = *reinterpret_cast<const float4 *>(&Ks[lane][c0 + 4 * i]);
-                q[i] = *reinterpret_cast<const float4 *>(&qs[h][c0 + 4 * i]);
+        for (int it = 0; it < IT; ++it)
+#pragma unroll
+            for (int h = 0; h < REP; ++h) {
+                float d = q4[h].x * kr[it].x + q4[h].y * kr[it].y + q4[h].z * kr[it].z + q4[h].w * kr[it].w;
+                if (Q8) d *= ksr[it];
+                cur[4 * it + h] = d;
             }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(k[i].x), "v"(k[i].w), "v"(q[i].x), "v"(q[i].w));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) d += k[i].x * q[i].x + k[i].y * q[i].y + k[i].z * q[i].z + k[i].w * q[i].w;
+#define DK_RS_STEP(BIT, DONE, STEP)                                           \
+    do {                                                                      \
+        const bool hi_ = (dq >> (BIT)) & 1;                                   \
+        _Pragma("unroll") for (int v = 0; v < 32; ++v) {                      \
+            if ((v & (DONE)) || (v & (1 << (BIT)))) continue;                 \
+            const float lo = cur[v], hv = cur[v | (1 << (BIT))];              \
+            cur[v] = (hi_ ? hv : lo) + STEP(hi_ ? lo : hv);                   \
+        }                                                                     \
+    } while (0)
+        DK_RS_STEP(3, 0, dpp<0x140>);   // row_mirror: lane i <-> 15 - i (flips bits 0-3; every lane holds all values)
+        DK_RS_STEP(2, 8, dpp<0x141>);   // row_half_mirror: i <-> 7 - i (bit 3 equal)
+        DK_RS_STEP(0, 12, dpp<0xB1>);   // quad_perm [1,0,3,2]: i ^ 1
+        DK_RS_STEP(1, 13, dpp<0x4E>);   // quad_perm [2,3,0,1]: i ^ 2
+        DK_RS_STEP(4, 15, swap16);      // swizzle: i ^ 16 within the half wave
+#undef DK_RS_STEP
+        {
+            const int e = g + 8 * (dq >> 2);
+            scs[dq & 3][e] = e < len ? cur[0] : -INFINITY;
         }
-        const float sc = lane < len ? d : -INFINITY;
-        const float m = wave_max(sc);
-        const float pe = fexp(sc - m);  // 0 past len
-        const float l = wave_sum(pe);
-        float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-        for (int e0 = 0; e0 < NK; e0 += 16) {
-            float2 v[16];
-            float w[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const float2 *>(&Vs[e0 + i][2 * lane]);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) w[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), e0 + i));
-#pragma unroll
-            for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y));
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                acc0 += w[i] * v[i].x;
-                acc1 += w[i] * v[i].y;
+        __syncthreads();
+        // ---- 2. softmax of head `wave` over the split's keys (lane = key)
+        {
+            const int h = wave;
+            const float sv = scs[h][lane];
+            const float m = wave_max(sv);
+            const float pe = fexp(sv - m);  // 0 past len
+            const float l = wave_sum(pe);
+            reinterpret_cast<float *>(&pw[lane])[h] = pe;
+            if (lane == 0) {
+                mine[(size_t)h * (HD + 2)] = m;
+                mine[(size_t)h * (HD + 2) + 1] = l;
             }
         }
-        float *dst = mine + (size_t)h * (HD + 2);
-        *reinterpret_cast<float2 *>(dst + 2 + 2 * lane) = make_float2(acc0, acc1);
-        if (lane == 0) {
-            dst[0] = m;
-            dst[1] = l;
+        __syncthreads();
+        // ---- 3. values: lane (g, dq) adds p v over its 8 keys for the 4 heads;
+        // the 8 key groups' sums meet in LDS
+        float4 acc[REP];
+#pragma unroll
+        for (int h = 0; h < REP; ++h) acc[h] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            float4 pv = pw[g + 8 * it];
+            if (Q8) {
+                pv.x *= vsr[it]; pv.y *= vsr[it]; pv.z *= vsr[it]; pv.w *= vsr[it];
+            }
+            const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+            for (int h = 0; h < REP; ++h) {
+                acc[h].x += pa[h] * vr[it].x;
+                acc[h].y += pa[h] * vr[it].y;
+                acc[h].z += pa[h] * vr[it].z;
+                acc[h].w += pa[h] * vr[it].w;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < REP; ++h) *reinterpret_cast<float4 *>(&red[g][h][dq * 4]) = acc[h];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, h = idx >> 7, c = idx & (HD - 1);
+            float v = 0.f;
+#pragma unroll
+            for (int gg = 0; gg < 8; ++gg) v += red[gg][h][c];
+            mine[(size_t)h * (HD + 2) + 2 + c] = v;
+        }
+    } else {
+        __shared__ float Ks[NK][KP], Vs[NK][KP];
+        // ---- 1. the split's rows to LDS
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+            const int e = g + 8 * it;
+            float4 k = kr[it], v = vr[it];
+            if (Q8) {
+                k.x *= ksr[it]; k.y *= ksr[it]; k.z *= ksr[it]; k.w *= ksr[it];
+                v.x *= vsr[it]; v.y *= vsr[it]; v.z *= vsr[it]; v.w *= vsr[it];
+            }
+            *reinterpret_cast<float4 *>(&Ks[e][dq * 4]) = k;
+            *reinterpret_cast<float4 *>(&Vs[e][dq * 4]) = v;
+        }
+        __syncthreads();
+
+        // ---- 2, 3. per head: scores of lane e's key, softmax, values
+        for (int h = wave; h < REP; h += 4) {
+            // LDS reads in batches, all issued before their first use (else the
+            // compiler keeps two in flight and waits on each pair)
+            float d = 0.f;
+#pragma unroll
+            for (int c0 = 0; c0 < HD; c0 += 32) {
+                float4 k[8], q[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    k[i] = *reinterpret_cast<const float4 *>(&Ks[lane][c0 + 4 * i]);
+                    q[i] = *reinterpret_cast<const float4 *>(&qs[h][c0 + 4 * i]);
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(k[i].x), "v"(k[i].w), "v"(q[i].x), "v"(q[i].w));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) d += k[i].x * q[i].x + k[i].y * q[i].y + k[i].z * q[i].z + k[i].w * q[i].w;
+            }
+            const float sc = lane < len ? d : -INFINITY;
+            const float m = wave_max(sc);
+            const float pe = fexp(sc - m);  // 0 past len
+            const float l = wave_sum(pe);
+            float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+            for (int e0 = 0; e0 < NK; e0 += 16) {
+                float2 v[16];
+                float w[16];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = *reinterpret_cast<const float2 *>(&Vs[e0 + i][2 * lane]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) w[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pe), e0 + i));
+#pragma unroll
+                for (int i = 0; i < 16; ++i) asm volatile("" ::"v"(v[i].x), "v"(v[i].y));
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc0 += w[i] * v[i].x;
+                    acc1 += w[i] * v[i].y;
+                }
+            }
+            float *dst = mine + (size_t)h * (HD + 2);
+            *reinterpret_cast<float2 *>(dst + 2 + 2 * lane) = make_float2(acc0, acc1);
+            if (lane == 0) {
+                dst[0] = m;
+                dst[1] = l;
+            }
         }
     }
+    if (!XM) return;
+
+    // ---- XM: the group's ticket; the last workgroup merges
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores acknowledged (by the L2)
+    __syncthreads();
+    if (tid == 0)
+        xm_last = __hip_atomic_fetch_add(a.xcnt + 32 * kh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+                  (unsigned)(nsplit - 1);
+    __syncthreads();
+    if (!xm_last) return;
+    const float *gp = a.part + (size_t)kh * gstride;
+    // the group's slabs, read with sc0 (past this CU's L1); offsets past the
+    // nsplit slabs read 0
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(gp), (short)0, (int)(nsplit * pstride * 4), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < HPW; ++i) {
+        const int h = wave + 4 * i;
+        if (h >= REP) break;
+        const int hoff = h * (HD + 2);
+        // lane j: split j's (max, sum); the channels of splits 16 at a time
+        const float2 ml = __builtin_bit_cast(
+            float2, __builtin_amdgcn_raw_buffer_load_b64(rs, (lane * (int)pstride + hoff) * 4, 0, 1));
+        float2 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            v[j] = __builtin_bit_cast(
+                float2, __builtin_amdgcn_raw_buffer_load_b64(rs, (j * (int)pstride + hoff + 2 + 2 * lane) * 4, 0, 1));
+        // all 17 loads in flight before the first use (else the channel loads
+        // wait for the reductions)
+        asm volatile("" ::"v"(ml.x), "v"(ml.y));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(v[j].x), "v"(v[j].y));
+        const float mj = lane < nsplit ? ml.x : -INFINITY;
+        const float M = wave_max(mj);
+        const float c = lane < nsplit ? fexp(mj - M) : 0.f;
+        const float Lt = wave_sum(ml.y * c);
+        float y0 = 0.f, y1 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), j));
+            y0 += cj * v[j].x;
+            y1 += cj * v[j].y;
+        }
+        for (int j0 = 16; j0 < nsplit; j0 += 16) {  // more than 16 splits
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                v[j] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                      rs, ((j0 + j) * (int)pstride + hoff + 2 + 2 * lane) * 4, 0, 1));
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float cj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c), j0 + j));
+                y0 += cj * v[j].x;
+                y1 += cj * v[j].y;
+            }
+        }
+        const int hq = kh * REP + h;
+        y0 = y0 / Lt * xv.x;
+        y1 = y1 / Lt * xv.y;
+        *reinterpret_cast<float2 *>(a.z + (size_t)hq * HD + 2 * lane) =
+            make_float2(y0 / (1.0f + expf(-(xg[i].x * xs[i].x))), y1 / (1.0f + expf(-(xg[i].y * xs[i].y))));
+    }
+    if (tid == 0) a.xcnt[32 * kh] = 0u;
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -1239,9 +1431,16 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
         dim3 grid(a.max_split, a.nk, -T), block(256);
         // one row, head dim 128, up to 64 keys a workgroup: the short-latency
         // kernel; else 8 load steps per workgroup, or 16 when the split needs them
-        if (HD == 128 && T == -1 && a.split <= 64) {
-            if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_attn_dec1<REP, 0>), grid, block, 0, s, a);
+        if (HD == 128 && T == -1 && a.split <= 64 && a.xcnt) {
+            // the splits merged in the kernel: no merge launch follows
+            if (a.max_split > 64) return hipErrorInvalidValue;
+            const dim3 xgrid(8 * a.max_split * ((a.nk + 7) / 8));
+            if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 1>), xgrid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 1>), xgrid, block, 0, s, a);
+            return hipGetLastError();
+        } else if (HD == 128 && T == -1 && a.split <= 64) {
+            if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 0>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 0>), grid, block, 0, s, a);
         } else if (a.split <= 8 * (256 / (HD / 4))) {
             if (a.q8) hipLaunchKernelGGL((k_attn_dec<HD, REP, 1, 8>), grid, block, 0, s, a);
             else hipLaunchKernelGGL((k_attn_dec<HD, REP, 0, 8>), grid, block, 0, s, a);
@@ -1321,7 +1520,18 @@ hipError_t launch_hd(const AttnArgs &a, int T, hipStream_t s) {
     }
 }
 
+// Each workgroup's XCD (hardware register XCC_ID, bits 3:0) into ids[blockIdx.x].
+__global__ void k_xcd_ids(unsigned *ids) {
+    if (threadIdx.x == 0) ids[blockIdx.x] = __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11));
+}
+
 }  // namespace
+
+hipError_t launch_xcd_check(unsigned *ids, int G, hipStream_t s) {
+    if (!ids || G < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_xcd_ids, dim3(G), dim3(64), 0, s, ids);
+    return hipGetLastError();
+}
 
 hipError_t launch_prep(const PrepArgs &a, int T, hipStream_t s) {
     if (a.hd > 256 || a.hd % 2 || (!a.kstage && (!a.kring || !a.vring || a.cap < 1)) || (a.kvtap && a.kvtap_n < T))

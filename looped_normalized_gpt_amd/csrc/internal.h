@@ -273,7 +273,21 @@ struct AttnArgs {
     int64_t pos0;        // the chunk's first position (the record's rows[0].pos)
     int32_t nrows;       // the call's rows (the record's n)
     SlotDesc sdc;        // the sequence's slot
+    // One-row calls, head dim 128, at most 64 splits: the splits merged inside
+    // the attention kernel, per kv head within one XCD (no merge launch).
+    // Arrival counters, kv head kh's at xcnt[32 kh] (128 bytes apart), zero
+    // between launches (the kernel clears them); partials then laid out per kv
+    // head on 128-byte lines (attn_xm_part_floats).  Null: the merge kernel.
+    uint32_t *xcnt;
 };
+// Floats of partials the in-kernel merge needs: per kv head, max_split slabs
+// of rep x (2 + hd), rounded up to 32 floats.
+inline size_t attn_xm_part_floats(int nk, int max_split, int rep, int hd) {
+    return (size_t)nk * (((size_t)max_split * rep * (hd + 2) + 31) / 32 * 32);
+}
+// Writes each workgroup's XCD number to ids[0 .. G-1] (a one-off check that
+// workgroup L runs on XCD L % 8, which the in-kernel merge relies on).
+hipError_t launch_xcd_check(unsigned *ids, int G, hipStream_t s);
 // Multi-row calls (after launch_prep): grid (max_split, nk, T), then the merge.
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s);
 // Decode rows (one new row per sequence: a one-row call, or one row of each

@@ -70,6 +70,7 @@ def _load():
     L.dory_debug_fail_launch.argtypes = [vp, i64]
     L.dory_debug_tap.argtypes = [vp, vp, i64]
     L.dory_debug_kv_tap.argtypes = [vp, vp, i64]
+    L.dory_debug_xcd_merge.argtypes = [vp, i32]
     L.dory_kv_read.argtypes = [vp, i32, i32, i32, i64, vp]
     L.dory_kv_field.argtypes = [vp, i32, i32, i32, vp, vp]
     L.dory_kv_load.argtypes = [vp, i32, i32, i32, i64, i32, vp, vp]
@@ -293,6 +294,15 @@ class Dory:
         """dory_debug_fail_launch: the n-th launch from now fails before it is
         launched (0: off)."""
         self._check(lib.dory_debug_fail_launch(self.h, n))
+
+    def xcd_merge(self, on=None) -> bool:
+        """dory_debug_xcd_merge: True/False selects the sliding layers'
+        in-kernel split merge or the merge kernel for one-row calls (None:
+        unchanged); returns whether the in-kernel merge is in use."""
+        rc = lib.dory_debug_xcd_merge(self.h, -1 if on is None else int(bool(on)))
+        if rc < 0:
+            self._check(rc)
+        return bool(rc)
 
     def reset(self, seq: int = -1):
         self._check(lib.dory_kv_reset(self.h, seq))

@@ -580,7 +580,16 @@ static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool d
         need("attention z", a.z, (size_t)T * Q * 4);
         if (a.zb) need("attention z (bf16)", a.zb, (size_t)T * Q * 2);
         if (a.zss) need("attention z sums of squares", a.zss, (size_t)T * a.nk * 4);
-        need("attention partials", a.part, (size_t)T * a.nk * a.max_split * rep * (a.hd + 2) * 4);
+        if (a.xcnt) {
+            // one row, the splits merged in the kernel: per-kv-head counters and
+            // the line-aligned partial layout
+            if (!dec || T != 1 || a.hd != 128 || a.split > 64 || a.max_split > 64)
+                fake::violation("in-kernel merge counters passed where that merge does not apply");
+            need("in-kernel merge counters", a.xcnt, (size_t)32 * a.nk * 4);
+            need("attention partials (in-kernel merge)", a.part, attn_xm_part_floats(a.nk, a.max_split, rep, a.hd) * 4);
+        } else {
+            need("attention partials", a.part, (size_t)T * a.nk * a.max_split * rep * (a.hd + 2) * 4);
+        }
         need("attention projections", a.qkvg, (size_t)T * ld * 4);
         if (dec) {
             need("attention sq", a.sq, (size_t)Q * 4);
@@ -636,6 +645,20 @@ static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool d
         }
     };
     return fake::launch(name, stat, dyn);
+}
+
+// The XCD check at create: reports workgroup L on XCD L % 8 (the in-kernel
+// merge's paths then run here too).
+hipError_t launch_xcd_check(unsigned *ids, int G, hipStream_t s) {
+    if (!ids || G < 1) return hipErrorInvalidValue;
+    auto stat = [=]() {
+        need("XCD ids", ids, (size_t)G * 4);
+        uintptr_t base = 0;
+        const fake::Alloc *al = fake::find(ids, &base);
+        if (al && al->mapped && reinterpret_cast<uintptr_t>(ids) + (size_t)G * 4 <= base + al->bytes)
+            for (int i = 0; i < G; ++i) ids[i] = (unsigned)(i % 8);
+    };
+    return fake::launch("launch_xcd_check", stat, [] {});
 }
 
 hipError_t launch_attn(const AttnArgs &a, int T, hipStream_t s) {

@@ -130,9 +130,17 @@ void stage_all(Model &m, std::initializer_list<int> stages) {
 void decode2b() {
     const int ctx = 4096, W = 16, K = 256;
     Model m(g2b(), ctx + W + K + 8, 512, 1);
+    expect(dory_debug_xcd_merge(m.h, -1) == 1, "sliding layers merge their splits in the attention kernel", m.h);
     for (int c = 0; c < ctx; c += 512) expect(m.chunk(0, 512, 4, DORY_LAST_LOOP, c + 512 >= ctx, c) == 0, "prompt", m.h);
     for (int i = 0; i < W + K; ++i) expect(m.chunk(0, 1, 4, DORY_LAST_LOOP, true, i) == 0, "decode", m.h);
     stage_all(m, {0, 1, 2, 3, 4, 5});
+    // the merge kernel for every layer, then back
+    expect(dory_debug_xcd_merge(m.h, 0) == 0, "merge kernel selected", m.h);
+    for (int i = 0; i < 4; ++i) expect(m.chunk(0, 1, 4, DORY_LAST_LOOP, true, i) == 0, "decode, merge kernel", m.h);
+    stage_all(m, {1});
+    expect(dory_debug_xcd_merge(m.h, 1) == 1, "in-kernel merge selected again", m.h);
+    for (int i = 0; i < 4; ++i) expect(m.chunk(0, 1, 4, DORY_LAST_LOOP, true, i) == 0, "decode, in-kernel merge", m.h);
+    expect(dory_debug_xcd_merge(m.h, 2) == DORY_EINVAL, "bad switch value", m.h);
 }
 
 void q8_2b() {
@@ -324,6 +332,28 @@ void selftest() {
     expect(fake_violations() == v0, "a GEMM inside its buffers passes");
     dk::launch_gemm(dk::kF32, a, nullptr, 100, dk::gemm_w(w, 65), 65, 100, c, 65, 4, nullptr);
     expect(fake_violations() > v0, "a GEMM reading a weight row too many is caught");
+    // the in-kernel merge's partials: its layout needs more than the plain one
+    {
+        dk::AttnArgs aa{};
+        // (15 splits: 15 slabs of 520 floats end off a 32-float line)
+        aa.nh = 16; aa.nk = 4; aa.hd = 128; aa.split = 64; aa.max_split = 15; aa.window = 960;
+        const size_t Q = 16 * 128, KV = 4 * 128, plain = (size_t)4 * 15 * 4 * 130;
+        aa.sg = (float *)fake_alloc(Q * 4, "sg"); aa.z = (float *)fake_alloc(Q * 4, "z");
+        aa.sq = (float *)fake_alloc(Q * 4, "sq");
+        aa.qkvg = (float *)fake_alloc((2 * Q + 2 * KV) * 4, "qkvg");
+        aa.xcnt = (uint32_t *)fake_alloc(32 * 4 * 4, "xcnt");
+        aa.rec = (dk::CallRec *)fake_alloc(dk::rec_bytes(1), "rec");
+        // the same launch over a buffer of the in-kernel layout's size, then a
+        // plain-sized one: only the second adds a violation
+        aa.part = (float *)fake_alloc(dk::attn_xm_part_floats(4, 15, 4, 128) * 4, "part");
+        v0 = fake_violations();
+        dk::launch_attn_dec(aa, 1, nullptr);
+        const long d1 = fake_violations() - v0;
+        aa.part = (float *)fake_alloc(plain * 4, "part (plain size)");
+        v0 = fake_violations();
+        dk::launch_attn_dec(aa, 1, nullptr);
+        expect(fake_violations() - v0 > d1, "in-kernel merge partials past a plain-sized buffer are caught");
+    }
     printf("selftest: %ld violations reported, as planted\n", fake_violations());
 }
 

@@ -68,6 +68,44 @@ def test_2b_decode_at_context_4096(model2b, D):
     g.close()
 
 
+def test_2b_decode_split_merge_paths(model2b, D):
+    """One-row calls at context 4096 through both merges of the sliding
+    layers' attention splits: inside the attention kernel (per kv head within
+    one XCD; the default where the create-time XCD check passes) and the merge
+    kernel.  Each matches the oracle; the two agree to fp32 rounding."""
+    import torch
+    cfg, w = model2b
+    k, v = _rows(cfg, 4096, 1, seed=6)
+    g = D.Dory(cfg, w, max_ctx=4096 + 512, max_chunk=512)
+    o = O.Oracle(cfg, w, max_ctx=4096 + 512)
+    g.kv_load(k, v, "last_loop", 1)
+    o.kv_load(k, v, "last_loop", 1)
+    assert g.xcd_merge(), "the create-time XCD check turned the in-kernel merge off on this device"
+    toks = synth.make_tokens(3, cfg["vocab"], seq=9)
+    calls = [toks[i:i + 1] for i in range(3)]
+    fused = run_pair(g, o, calls, 4, "last_loop")
+    check_pair(fused, COS, DLOGIT, "2b decode, in-kernel merge")
+    # the same calls again from position 4096 with the merge kernel
+    g.rollback(4096)
+    assert not g.xcd_merge(False)
+    sep = []
+    for toks1 in calls:
+        buf = torch.full((g.passes(4), 1, cfg["hidden"]), float("nan"), dtype=torch.float32, device=g.device)
+        g.set_tap(buf)
+        lg = g.forward(np.asarray(toks1, np.int32), 4, "last_loop", logits=True)
+        torch.cuda.synchronize()
+        sep.append((lg.cpu().numpy(), buf.cpu().numpy()))
+    g.set_tap(None)
+    for i, ((glg, _, gtap, otap), (slg, stap)) in enumerate(zip(fused, sep)):
+        check_pair([(slg, fused[i][1], stap, otap)], COS, DLOGIT, f"2b decode call {i}, merge kernel")
+        dt = float(np.abs(gtap - stap).max())
+        dl = float(np.abs(glg - slg).max())
+        say(f"call {i}: in-kernel vs merge kernel: max |dtap| {dt:.2e}, max |dlogit| {dl:.2e}")
+        assert dt <= 1e-4 and dl <= 1e-3, f"call {i}: the two merges differ by {dt:.2e} (tap), {dl:.2e} (logits)"
+    assert g.xcd_merge(True)
+    g.close()
+
+
 def test_2b_chunk_past_the_window(model2b, D):
     """A multi-row call whose rows cross the 1024-key sliding window, on a
     loaded context (the prefill path: tiled GEMMs, multi-row attention)."""
