@@ -890,10 +890,10 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
         }
     }
     // The in-kernel merge of the sliding layers' one-row attention (head dim
-    // 128, at most 64 splits) needs every workgroup id of one residue mod 8 on
+    // 128, 4 q heads per kv head, at most 64 splits) needs every workgroup id of one residue mod 8 on
     // one XCD: checked once on this device over the grid it launches (else the
     // merge kernel serves, as for the full layers).
-    if (h->hd == 128 && h->ms_ds <= 64 && h->split_ds <= 64) {
+    if (h->hd == 128 && h->nh == 4 * h->nk && h->ms_ds <= 64 && h->split_ds <= 64) {
         const int G = 8 * h->ms_ds * ((h->nk + 7) / 8);
         unsigned *ids = nullptr;
         CREATE_CHECK(dmalloc(h, &ids, (size_t)G));
@@ -903,8 +903,8 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
         bool same = true;
         for (int i = 8; i < G; ++i) same = same && got[i] == got[i % 8];
         if (same) {
-            CREATE_CHECK(dmalloc(h, &h->xcnt, (size_t)32 * h->nk));
-            CREATE_CHECK(hipMemset(h->xcnt, 0, sizeof(uint32_t) * 32 * h->nk));
+            CREATE_CHECK(dmalloc(h, &h->xcnt, (size_t)32 * h->nh));
+            CREATE_CHECK(hipMemset(h->xcnt, 0, sizeof(uint32_t) * 32 * h->nh));
             CREATE_CHECK(hipDeviceSynchronize());
             h->xm = true;
         }

@@ -751,10 +751,11 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
 // deals workgroups to the XCDs in turn; launch_xcd_check confirms it at
 // create) gives kv head kh the ids L = kh (mod 8), so the group's partials
 // meet in that XCD's L2, which every CU of the XCD shares.  Each workgroup
-// writes its partial, waits until the L2 has acknowledged the stores, and
-// takes a ticket from the group's counter (an L2 atomic); the last one reads
-// the group's partials past its L1 (sc0), merges them as k_attn_merge does,
-// applies the gate, writes z and clears the counter for the next launch.
+// wave (one q head each: REP = 4) writes its head's partial, waits until the
+// L2 has acknowledged the stores, and takes a ticket from the (kv head, head)
+// counter (an L2 atomic); the wave with the last one reads the head's partials
+// past its L1 (sc0), merges them as k_attn_merge does, applies the gate,
+// writes z and clears the counter for the next launch.
 template <int REP, int Q8, int XM>
 __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
     constexpr int HD = 128, HALF = 64, NK = 64, KP = HD + 4, IT = NK / 8;
@@ -765,7 +766,6 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
     __shared__ float vn[HD];
     __shared__ int8_t kcn[HD], vcn[HD];
     __shared__ float ksn[NGK], vsn[1];
-    __shared__ int xm_last;
     int s, kh;
     if (XM) {
         const int L = blockIdx.x, j = L >> 3;
@@ -1009,13 +1009,17 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
 #pragma unroll
         for (int h = 0; h < REP; ++h) *reinterpret_cast<float4 *>(&red[g][h][dq * 4]) = acc[h];
         __syncthreads();
+        {
+            // wave h writes head h's channels (as it wrote its max and sum)
+            const int h = wave;
+            float2 v = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, h = idx >> 7, c = idx & (HD - 1);
-            float v = 0.f;
-#pragma unroll
-            for (int gg = 0; gg < 8; ++gg) v += red[gg][h][c];
-            mine[(size_t)h * (HD + 2) + 2 + c] = v;
+            for (int gg = 0; gg < 8; ++gg) {
+                const float2 t = *reinterpret_cast<const float2 *>(&red[gg][h][2 * lane]);
+                v.x += t.x;
+                v.y += t.y;
+            }
+            *reinterpret_cast<float2 *>(mine + (size_t)h * (HD + 2) + 2 + 2 * lane) = v;
         }
     } else {
         __shared__ float Ks[NK][KP], Vs[NK][KP];
@@ -1080,25 +1084,21 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
             }
         }
     }
-    if (!XM) return;
-
-    // ---- XM: the group's ticket; the last workgroup merges
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial stores acknowledged (by the L2)
-    __syncthreads();
-    if (tid == 0)
-        xm_last = __hip_atomic_fetch_add(a.xcnt + 32 * kh, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
-                  (unsigned)(nsplit - 1);
-    __syncthreads();
-    if (!xm_last) return;
-    const float *gp = a.part + (size_t)kh * gstride;
-    // the group's slabs, read with sc0 (past this CU's L1); offsets past the
-    // nsplit slabs read 0
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(gp), (short)0, (int)(nsplit * pstride * 4), 0x00020000);
-#pragma unroll
-    for (int i = 0; i < HPW; ++i) {
-        const int h = wave + 4 * i;
-        if (h >= REP) break;
+    if constexpr (XM) {
+        static_assert(REP == 4, "the in-kernel merge takes one head a wave");
+        // ---- XM: head h = wave's ticket; the wave that takes the last one
+        // merges head h (each wave wrote all of its head's partial)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores acknowledged (by the L2)
+        const int h = wave;
+        uint32_t *cnt = a.xcnt + 32 * (kh * REP + h);
+        unsigned t = 0;
+        if (lane == 0) t = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readlane(t, 0) != (unsigned)(nsplit - 1)) return;
+        const float *gp = a.part + (size_t)kh * gstride;
+        // the group's slabs, read with sc0 (past this CU's L1); offsets past the
+        // nsplit slabs read 0
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(gp), (short)0, (int)(nsplit * pstride * 4), 0x00020000);
         const int hoff = h * (HD + 2);
         // lane j: split j's (max, sum); the channels of splits 16 at a time
         const float2 ml = __builtin_bit_cast(
@@ -1140,9 +1140,9 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         y0 = y0 / Lt * xv.x;
         y1 = y1 / Lt * xv.y;
         *reinterpret_cast<float2 *>(a.z + (size_t)hq * HD + 2 * lane) =
-            make_float2(y0 / (1.0f + expf(-(xg[i].x * xs[i].x))), y1 / (1.0f + expf(-(xg[i].y * xs[i].y))));
+            make_float2(y0 / (1.0f + expf(-(xg[0].x * xs[0].x))), y1 / (1.0f + expf(-(xg[0].y * xs[0].y))));
+        if (lane == 0) *cnt = 0u;
     }
-    if (tid == 0) a.xcnt[32 * kh] = 0u;
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -1431,14 +1431,17 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
         dim3 grid(a.max_split, a.nk, -T), block(256);
         // one row, head dim 128, up to 64 keys a workgroup: the short-latency
         // kernel; else 8 load steps per workgroup, or 16 when the split needs them
-        if (HD == 128 && T == -1 && a.split <= 64 && a.xcnt) {
-            // the splits merged in the kernel: no merge launch follows
-            if (a.max_split > 64) return hipErrorInvalidValue;
-            const dim3 xgrid(8 * a.max_split * ((a.nk + 7) / 8));
-            if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 1>), xgrid, block, 0, s, a);
-            else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 1>), xgrid, block, 0, s, a);
-            return hipGetLastError();
-        } else if (HD == 128 && T == -1 && a.split <= 64) {
+        if constexpr (HD == 128 && REP == 4) {
+            if (T == -1 && a.split <= 64 && a.xcnt) {
+                // the splits merged in the kernel: no merge launch follows
+                if (a.max_split > 64) return hipErrorInvalidValue;
+                const dim3 xgrid(8 * a.max_split * ((a.nk + 7) / 8));
+                if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 1>), xgrid, block, 0, s, a);
+                else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 1>), xgrid, block, 0, s, a);
+                return hipGetLastError();
+            }
+        }
+        if (HD == 128 && T == -1 && a.split <= 64) {
             if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 0>), grid, block, 0, s, a);
             else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 0>), grid, block, 0, s, a);
         } else if (a.split <= 8 * (256 / (HD / 4))) {

@@ -273,11 +273,12 @@ struct AttnArgs {
     int64_t pos0;        // the chunk's first position (the record's rows[0].pos)
     int32_t nrows;       // the call's rows (the record's n)
     SlotDesc sdc;        // the sequence's slot
-    // One-row calls, head dim 128, at most 64 splits: the splits merged inside
-    // the attention kernel, per kv head within one XCD (no merge launch).
-    // Arrival counters, kv head kh's at xcnt[32 kh] (128 bytes apart), zero
-    // between launches (the kernel clears them); partials then laid out per kv
-    // head on 128-byte lines (attn_xm_part_floats).  Null: the merge kernel.
+    // One-row calls, head dim 128, 4 q heads per kv head, at most 64 splits:
+    // the splits merged inside the attention kernel, per kv head within one XCD
+    // (no merge launch).  Arrival counters, (kv head kh, head h)'s at
+    // xcnt[32 (4 kh + h)] (128 bytes apart), zero between launches (the kernel
+    // clears them); partials then laid out per kv head on 128-byte lines
+    // (attn_xm_part_floats).  Null: the merge kernel.
     uint32_t *xcnt;
 };
 // Floats of partials the in-kernel merge needs: per kv head, max_split slabs

@@ -583,9 +583,9 @@ static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool d
         if (a.xcnt) {
             // one row, the splits merged in the kernel: per-kv-head counters and
             // the line-aligned partial layout
-            if (!dec || T != 1 || a.hd != 128 || a.split > 64 || a.max_split > 64)
+            if (!dec || T != 1 || a.hd != 128 || rep != 4 || a.split > 64 || a.max_split > 64)
                 fake::violation("in-kernel merge counters passed where that merge does not apply");
-            need("in-kernel merge counters", a.xcnt, (size_t)32 * a.nk * 4);
+            need("in-kernel merge counters", a.xcnt, (size_t)32 * a.nh * 4);
             need("attention partials (in-kernel merge)", a.part, attn_xm_part_floats(a.nk, a.max_split, rep, a.hd) * 4);
         } else {
             need("attention partials", a.part, (size_t)T * a.nk * a.max_split * rep * (a.hd + 2) * 4);

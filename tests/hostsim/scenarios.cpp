@@ -341,7 +341,7 @@ void selftest() {
         aa.sg = (float *)fake_alloc(Q * 4, "sg"); aa.z = (float *)fake_alloc(Q * 4, "z");
         aa.sq = (float *)fake_alloc(Q * 4, "sq");
         aa.qkvg = (float *)fake_alloc((2 * Q + 2 * KV) * 4, "qkvg");
-        aa.xcnt = (uint32_t *)fake_alloc(32 * 4 * 4, "xcnt");
+        aa.xcnt = (uint32_t *)fake_alloc(32 * 16 * 4, "xcnt");
         aa.rec = (dk::CallRec *)fake_alloc(dk::rec_bytes(1), "rec");
         // the same launch over a buffer of the in-kernel layout's size, then a
         // plain-sized one: only the second adds a violation
