@@ -128,6 +128,10 @@ struct dory {
     // test has not turned it off (xm_off)
     uint32_t *xcnt = nullptr;
     bool xm = false, xm_off = false;
+    // One-row calls' full layers whose window needs 65..72 splits of 64 keys:
+    // 64 workgroups per kv head whose splits grow to cover the keys (one per
+    // CU over the 4 kv heads, where 65+ would put two on some CUs)
+    bool ext_df = false;
     int64_t kvtap_cap = 0;
     std::vector<SeqState> seqs;
     std::string err;
@@ -489,6 +493,10 @@ int enq_attn(Enq &q, const LayerInfo &l, int loop_i, const Resolve &rs, const fl
         if (q.T == 1) {
             aa.split = l.sliding ? h->split_ds : h->split_df;
             aa.max_split = l.sliding ? h->ms_ds : h->ms_df;
+            if (!l.sliding && h->ext_df) {
+                aa.max_split = 64;
+                aa.ext = 1;
+            }
             aa.sd1 = h->tab + ((size_t)q.seq[0] * h->n_ord + l.ord) * kMaxLoops + slot;
             if (l.sliding && h->xm && !h->xm_off) aa.xcnt = h->xcnt;
         } else {
@@ -811,6 +819,7 @@ int dory_create(const dory_config *cfg, const dory_weights *w, dory_t **out) {
     h->ms_bs = (int)((ws + h->split_bs - 1) / h->split_bs);
     h->ms_bf = (int)((wf + h->split_bf - 1) / h->split_bf);
     h->ms_dec = std::max(std::max(h->ms_ds, h->ms_df), std::max(h->ms_bs, h->ms_bf));
+    h->ext_df = h->hd == 128 && h->nh == 4 * h->nk && h->split_df == 64 && h->ms_df > 64 && h->ms_df <= 72;
     // multi-row calls: at least 256 keys per split over a block's key range,
     // which is at most wmax + 127 keys
     h->split_pf = 256;
@@ -1523,6 +1532,10 @@ int dory_stage_bench(dory_t *h, int32_t stage, int32_t reps, dory_stream_t strea
             aa.max_split = h->last_T == 1 ? (l->sliding ? h->ms_ds : h->ms_df) : (l->sliding ? h->ms_bs : h->ms_bf);
             if (h->last_T == 1) aa.sd1 = h->tab + ((size_t)h->last_seq0 * h->n_ord + l->ord) * kMaxLoops + aa.slot;
             if (h->last_T == 1 && l->sliding && h->xm && !h->xm_off) aa.xcnt = h->xcnt;
+            if (h->last_T == 1 && !l->sliding && h->ext_df) {
+                aa.max_split = 64;
+                aa.ext = 1;
+            }
             aa.field = -1;
             e = launch_attn_dec(aa, h->last_T, s);
             break;

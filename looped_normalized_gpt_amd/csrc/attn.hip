@@ -756,9 +756,12 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
 // counter (an L2 atomic); the wave with the last one reads the head's partials
 // past its L1 (sc0), merges them as k_attn_merge does, applies the gate,
 // writes z and clears the counter for the next launch.
-template <int REP, int Q8, int XM>
+template <int REP, int Q8, int XM, int EXT = 0>
 __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
-    constexpr int HD = 128, HALF = 64, NK = 64, KP = HD + 4, IT = NK / 8;
+    static_assert(!EXT || (REP == 4 && !XM), "the extended split takes the register path, merge kernel");
+    constexpr int HD = 128, HALF = 64, NK = 64, KP = HD + 4;
+    constexpr int IT = EXT ? 9 : NK / 8;  // load steps: keys g + 8 it
+    constexpr int NKX = 8 * IT;           // keys a workgroup can take
     constexpr int NGK = HD / kKGroup;
     constexpr int VPW = (REP + 1 + 3) / 4;  // vectors a wave prepares
     constexpr int HPW = (REP + 3) / 4;      // heads a wave merges (XM)
@@ -814,14 +817,21 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
     else asm volatile("" ::"s"(sd.cap), "s"(sd.k), "s"(sd.v));
     const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
     const int64_t nkeys = p - lo + 1;
-    const int nsplit = (int)((nkeys + a.split - 1) / a.split);
+    // EXT: the max_split workgroups cover the row's keys, each taking more
+    // than `split` (at most 9/8 of it) once the keys outgrow split x max_split
+    int S = a.split;
+    if (EXT) {
+        const int need = (int)((nkeys + a.max_split - 1) / a.max_split);
+        S = need > S ? need : S;
+    }
+    const int nsplit = (int)((nkeys + S - 1) / S);
     if (s >= nsplit) {  // no key here: the merge skips a slab whose max is -inf (XM: not in the group)
         if (!XM && tid < REP)
             a.part[(((size_t)r * a.nk + kh) * a.max_split + s) * REP * (HD + 2) + (size_t)tid * (HD + 2)] = -INFINITY;
         return;
     }
-    const int64_t e0 = lo + (int64_t)s * a.split;
-    const int len = (int)(nkeys - (int64_t)s * a.split < a.split ? nkeys - (int64_t)s * a.split : a.split);
+    const int64_t e0 = lo + (int64_t)s * S;
+    const int len = (int)(nkeys - (int64_t)s * S < S ? nkeys - (int64_t)s * S : S);
     const bool tail = s == nsplit - 1;
     const bool field = Q8 && field_on(a, a.rec->rows[r]);
     const int cap = sd.cap;
@@ -937,15 +947,15 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
         // its values whose matching bit of v equals its own, adding its
         // partner's copy.  After the five steps lane dq holds value v = dq: the
         // score of key g + 8 (dq >> 2) for head dq & 3.
-        __shared__ float scs[REP][NK + 1];      // scores by head (padded row)
-        __shared__ float4 pw[NK];               // softmax weights by key, the 4 heads
+        __shared__ float scs[REP][NKX + 1];     // scores by head (padded row)
+        __shared__ float4 pw[NKX];              // softmax weights by key, the 4 heads
         __shared__ float red[8][REP][HD];       // per key group g: its sums of p * v
         float4 q4[REP];
 #pragma unroll
         for (int h = 0; h < REP; ++h) q4[h] = *reinterpret_cast<const float4 *>(&qs[h][dq * 4]);
         float cur[32];
 #pragma unroll
-        for (int it = 0; it < IT; ++it)
+        for (int it = 0; it < 8; ++it)
 #pragma unroll
             for (int h = 0; h < REP; ++h) {
                 float d = q4[h].x * kr[it].x + q4[h].y * kr[it].y + q4[h].z * kr[it].z + q4[h].w * kr[it].w;
@@ -971,15 +981,31 @@ __global__ __launch_bounds__(256) void k_attn_dec1(AttnArgs a) {
             const int e = g + 8 * (dq >> 2);
             scs[dq & 3][e] = e < len ? cur[0] : -INFINITY;
         }
+        if (EXT) {
+            // the ninth step's key 64 + g: its 4 heads' dot products summed over
+            // the half wave; lane dq < 4 writes head dq's
+            float x[REP];
+#pragma unroll
+            for (int h = 0; h < REP; ++h) {
+                float d = q4[h].x * kr[IT - 1].x + q4[h].y * kr[IT - 1].y + q4[h].z * kr[IT - 1].z +
+                          q4[h].w * kr[IT - 1].w;
+                if (Q8) d *= ksr[IT - 1];
+                x[h] = group_sum<32>(d);
+            }
+            const float xe = dq == 0 ? x[0] : dq == 1 ? x[1] : dq == 2 ? x[2] : x[3];
+            if (dq < REP) scs[dq][NK + g] = NK + g < len ? xe : -INFINITY;
+        }
         __syncthreads();
         // ---- 2. softmax of head `wave` over the split's keys (lane = key)
         {
             const int h = wave;
             const float sv = scs[h][lane];
-            const float m = wave_max(sv);
-            const float pe = fexp(sv - m);  // 0 past len
-            const float l = wave_sum(pe);
+            const float sv2 = EXT && lane < NKX - NK ? scs[h][NK + lane] : -INFINITY;  // keys 64..
+            const float m = wave_max(fmaxf(sv, sv2));
+            const float pe = fexp(sv - m), pe2 = fexp(sv2 - m);  // 0 past len
+            const float l = wave_sum(pe + pe2);
             reinterpret_cast<float *>(&pw[lane])[h] = pe;
+            if (EXT && lane < NKX - NK) reinterpret_cast<float *>(&pw[NK + lane])[h] = pe2;
             if (lane == 0) {
                 mine[(size_t)h * (HD + 2)] = m;
                 mine[(size_t)h * (HD + 2) + 1] = l;
@@ -1441,7 +1467,17 @@ hipError_t launch_hr(const AttnArgs &a, int T, hipStream_t s) {
                 return hipGetLastError();
             }
         }
-        if (HD == 128 && T == -1 && a.split <= 64) {
+        bool ext = false;
+        if constexpr (HD == 128 && REP == 4) {
+            if (T == -1 && a.split == 64 && a.ext) {
+                // 64-key splits grown to cover the row's keys with max_split workgroups
+                if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 0, 1>), grid, block, 0, s, a);
+                else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 0, 1>), grid, block, 0, s, a);
+                ext = true;
+            }
+        }
+        if (ext) {
+        } else if (HD == 128 && T == -1 && a.split <= 64) {
             if (a.q8) hipLaunchKernelGGL((k_attn_dec1<REP, 1, 0>), grid, block, 0, s, a);
             else hipLaunchKernelGGL((k_attn_dec1<REP, 0, 0>), grid, block, 0, s, a);
         } else if (a.split <= 8 * (256 / (HD / 4))) {

@@ -280,6 +280,11 @@ struct AttnArgs {
     // clears them); partials then laid out per kv head on 128-byte lines
     // (attn_xm_part_floats).  Null: the merge kernel.
     uint32_t *xcnt;
+    // One-row calls, head dim 128, 4 q heads per kv head, split 64: 1 lets the
+    // max_split workgroups grow their splits to cover the row's keys (up to 72
+    // keys each, so the keys may reach 72 max_split) instead of adding
+    // workgroups; the grid then stays at max_split per kv head.
+    int32_t ext;
 };
 // Floats of partials the in-kernel merge needs: per kv head, max_split slabs
 // of rep x (2 + hd), rounded up to 32 floats.

@@ -616,7 +616,15 @@ static hipError_t attn_common(const char *name, const AttnArgs &a, int T, bool d
                 need("kv tap", rec->kvtap + ((size_t)a.tap_pass * rec->n + r) * 2 * KV, (size_t)2 * KV * 4);
             const int64_t lo = p + 1 - a.window > 0 ? p + 1 - a.window : 0;
             const int64_t nkeys = p - lo + 1;
-            if (dec || a.blk == 0) {
+            if (a.ext) {
+                // the grown split: max_split workgroups of up to 72 keys
+                if (!dec || T != 1 || a.hd != 128 || rep != 4 || a.split != 64)
+                    fake::violation("a grown split where the one-row kernel does not take it");
+                const int64_t S = std::max<int64_t>(a.split, (nkeys + a.max_split - 1) / a.max_split);
+                if (S > a.split * 9 / 8)
+                    fake::violation("row at " + std::to_string(p) + " needs splits of " + std::to_string(S) +
+                                    " keys, more than the grown split's 72");
+            } else if (dec || a.blk == 0) {
                 const int64_t ns = (nkeys + a.split - 1) / a.split;
                 if (ns > a.max_split)
                     fake::violation("row at " + std::to_string(p) + " needs " + std::to_string(ns) +

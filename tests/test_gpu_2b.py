@@ -106,6 +106,23 @@ def test_2b_decode_split_merge_paths(model2b, D):
     g.close()
 
 
+def test_2b_decode_grown_splits(model2b, D):
+    """One-row calls whose full layers read 4501+ keys with max_ctx 4608: 64
+    workgroups per kv head take 71-key splits (the grown split), so every
+    workgroup's ninth load step holds keys."""
+    cfg, w = model2b
+    k, v = _rows(cfg, 4500, 1, seed=8)
+    say("2b kv_load 4500 + 3 decode (grown splits)")
+    g = D.Dory(cfg, w, max_ctx=4608, max_chunk=512)
+    o = O.Oracle(cfg, w, max_ctx=4608)
+    g.kv_load(k, v, "last_loop", 1)
+    o.kv_load(k, v, "last_loop", 1)
+    toks = synth.make_tokens(3, cfg["vocab"], seq=11)
+    calls = [toks[i:i + 1] for i in range(3)]
+    check_pair(run_pair(g, o, calls, 4, "last_loop"), COS, DLOGIT, "2b ctx4500 decode")
+    g.close()
+
+
 def test_2b_chunk_past_the_window(model2b, D):
     """A multi-row call whose rows cross the 1024-key sliding window, on a
     loaded context (the prefill path: tiled GEMMs, multi-row attention)."""
