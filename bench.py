@@ -210,13 +210,14 @@ def measured_peaks():
                    "8 slices, and a loop of v_mfma_f32_32x32x16_bf16 from registers; HIP events"}
 
 
-def launch_floor(cfg, ctx, loops):
+def launch_floor(cfg, ctx, loops, sliding_merged=True):
     """A measured ceiling for a decode token made of one kernel per step: the
     probe's streaming read (dory_probe) timed back to back at the size of each
     kernel of the token (each projection's weights, each attention's cache rows,
-    a 64 KB read for each split merge), buffers rotating past the Infinity
-    Cache, summed over the token's 121 kernels.  What a kernel costs beyond its
-    read at that size is its own excess."""
+    a 64 KB read for each split merge launched on its own: the full layers', and
+    the sliding layers' unless they merge inside the attention kernel), buffers
+    rotating past the Infinity Cache, summed over the token's kernels.  What a
+    kernel costs beyond its read at that size is its own excess."""
     import torch
     from looped_normalized_gpt_amd import dory
     stream = torch.cuda.current_stream()
@@ -267,7 +268,8 @@ def launch_floor(cfg, ctx, loops):
         else:
             per["qkvg GEMV"] += 1
             per["O GEMV"] += 1
-            per["merge"] += 1
+            if kind != "S" or not sliding_merged:
+                per["merge"] += 1
             per["sliding attention" if kind == "S" else "full attention"] += 1
     floor = sum(us[k] * n for k, n in per.items())
     return {"us_per_read": us, "launches_per_token": per, "token_floor_us": round(floor, 1),
@@ -458,6 +460,7 @@ def run_decode(args, q8, gate=None):
     gu_us = time_stage(dory, g, "gateup", args.stage_reps, stream)
     stages = {st: round(time_stage(dory, g, st, 96, stream), 2) for st in ("qkvg", "attn", "o", "down", "head")}
     stages["gateup"] = round(gu_us, 2)
+    sliding_merged = g.xcd_merge()
     g.close()
     gu_gbs = gu_bytes / (gu_us * 1e-6) / 1e9
     log("bench: the vendor GEMV on the gate|up shape (reference only)")
@@ -467,7 +470,7 @@ def run_decode(args, q8, gate=None):
 
     log("bench: measured peaks and the per-launch floor of a token")
     peaks = measured_peaks()
-    floor = launch_floor(cfg, ctx, loops)
+    floor = launch_floor(cfg, ctx, loops, sliding_merged)
     cpu = cpu1 = None
     if not args.no_cpu_baseline:
         log("bench: CPU baseline (oracle), all host cores and one core")
