@@ -739,13 +739,20 @@ __global__ __launch_bounds__(256) void k_attn_dec(AttnArgs a) {
 //      vector REP, the new key: lane j holds elements j and j+64, which are
 //      exactly the pairs RoPE rotates, so RoPE, the unit norm and the sq scale
 //      run in registers and one sync publishes them.  Every K and V load of the
-//      split is issued behind these loads, 16 bytes per lane, 8 keys a step.
+//      split is issued behind these loads, 16 bytes per lane, 8 keys a step
+//      (the key field and 1/sqrt(hd) are folded into the queries).
+// REP = 4 (one q head a wave): the scores come from the registers that hold
+// the keys, summed over the half wave by a reduce-scatter (described where it
+// runs); the softmax of head w runs in wave w; the values accumulate in
+// registers and the 8 key groups' sums meet in LDS.  Other REP:
 //   1. The split's K and V rows go to LDS in fp32 (q8_2f: codes times their
-//      scales; the key field and 1/sqrt(hd) are folded into the queries).
+//      scales).
 //   2. Wave w takes heads w, w+4, ..: lane e scores key e against the head's
 //      query from LDS, and the softmax of the head's 64 keys stays in the wave.
 //   3. Lane l accumulates channels 2l, 2l+1 over the 64 keys, taking each
 //      key's weight from its lane (readlane), and stores the partial.
+// EXT = 1 (REP = 4, merge kernel): the split grows past 64 keys (a ninth load
+// step, up to 72) so max_split workgroups cover the row's keys.
 // XM = 1 (one row, a.xcnt set): the splits are merged in the kernel, inside
 // one XCD.  A 1-D grid whose workgroup L runs on XCD L % 8 (the dispatcher
 // deals workgroups to the XCDs in turn; launch_xcd_check confirms it at
