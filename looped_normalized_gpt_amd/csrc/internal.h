@@ -196,10 +196,10 @@ inline bool gemm_reads_fp32_a(int wtype, bool have_bf16, int M, int K, int lda) 
 // Split-K count that fills the chip with 128 x 128 tiles (1 where it does not apply).
 inline int gemm_pick_splits(int wtype, bool have_bf16, int M, int N, int K) {
     if (!gemm_splits_ok(wtype, have_bf16, M, K, 1)) return 1;
-    if (M <= 64) {  // about 256 workgroups of 64 weight rows, at least 4 K blocks each
+    if (M <= 64) {  // about 256 workgroups of 64 weight rows, at least 2 K blocks each
         const int tiles = (N + 63) / 64;
         int S = 1;
-        while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K / 128 >= 4 * S * 2) S *= 2;
+        while (S * 2 <= kMaxKParts && tiles * S * 2 <= 256 && K / 128 >= 2 * S * 2) S *= 2;
         return S;
     }
     const int tiles = ((M + 127) / 128) * ((N + 127) / 128);
