@@ -224,11 +224,76 @@ __device__ inline void resolve_row(const Resolve &rs, int r, int H, float *xs, f
 }
 
 // The same step with the inputs already in registers.  Thread tid holds the
-// float4 groups at 4*tid + 1024*jj (jj < EPT/4) of the row in slots
-// 4*jj .. 4*jj+3 (zeros past H).  h, o, al, in: the residual, the sub-layer
-// output, |alpha| and the loop input.  No global loads, so it can run while a
-// caller's earlier loads are still in flight.
-__device__ __forceinline__ int reg_index(int j) { return 4 * (int)threadIdx.x + 1024 * (j >> 2) + (j & 3); }
+// row's elements elem_index<MAP>(j) in slots j < EPT (zeros past H): MAP 0, the
+// float4 groups at 4*tid + 1024*jj; MAP 1, the GEMV's dot layout, 8
+// consecutive elements of each 512-wide chunk (wave + 4c) at lane*8 (slots
+// 8c .. 8c+7).  h, o, al, in: the residual, the sub-layer output, |alpha| and
+// the loop input.  No global loads, so it can run while a caller's earlier
+// loads are still in flight.
+template <int MAP>
+__device__ __forceinline__ int elem_index(int j) {
+    if (MAP == 0) return 4 * (int)threadIdx.x + 1024 * (j >> 2) + (j & 3);
+    return (((int)threadIdx.x >> 6) + 4 * (j >> 3)) * 512 + ((int)threadIdx.x & 63) * 8 + (j & 7);
+}
+__device__ __forceinline__ int reg_index(int j) { return elem_index<0>(j); }
+
+// Row sums of R = 4, 8, 16 or 32 values a lane, by a reduce-scatter: each
+// step pairs lanes that differ in one bit (the swap of 16 lanes, row mirror,
+// half-row mirror, the two quad permutes) and halves what a lane holds, so
+// lane i ends with value i % R summed over its R-lane group; rotations inside
+// the 16-lane row and the swap of 16 lanes then add the groups of its 32-lane
+// half.  Lanes whose lane % 32 < R return row lane % 32 summed over their half
+// of the wave.
+template <int BIT, int R>
+__device__ __forceinline__ void rs_step(const float (&v)[R], float (&out)[R / 2], int lane) {
+    const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+    for (int k = 0; k < R / 2; ++k) {
+        const float send = hi ? v[k] : v[R / 2 + k], keep = hi ? v[R / 2 + k] : v[k];
+        const float got = BIT == 4   ? swap16(send)
+                          : BIT == 3 ? dpp<0x140>(send)
+                          : BIT == 2 ? dpp<0x141>(send)
+                          : BIT == 1 ? dpp<0x4E>(send)
+                                     : dpp<0xB1>(send);
+        out[k] = keep + got;
+    }
+}
+template <int R>
+__device__ __forceinline__ float row_sums_rs(const float (&v)[R], int lane) {
+    static_assert(R == 4 || R == 8 || R == 16 || R == 32, "rows a lane");
+    float r;
+    if constexpr (R == 32) {
+        float t16[16], t8[8], t4[4], t2[2], t1[1];
+        rs_step<4, 32>(v, t16, lane);
+        rs_step<3, 16>(t16, t8, lane);
+        rs_step<2, 8>(t8, t4, lane);
+        rs_step<1, 4>(t4, t2, lane);
+        rs_step<0, 2>(t2, t1, lane);
+        return t1[0];
+    } else if constexpr (R == 16) {
+        float t8[8], t4[4], t2[2], t1[1];
+        rs_step<3, 16>(v, t8, lane);
+        rs_step<2, 8>(t8, t4, lane);
+        rs_step<1, 4>(t4, t2, lane);
+        rs_step<0, 2>(t2, t1, lane);
+        r = t1[0];
+    } else if constexpr (R == 8) {
+        float t4[4], t2[2], t1[1];
+        rs_step<2, 8>(v, t4, lane);
+        rs_step<1, 4>(t4, t2, lane);
+        rs_step<0, 2>(t2, t1, lane);
+        r = t1[0];
+        r += dpp<0x128>(r);  // row_ror:8
+    } else {
+        float t2[2], t1[1];
+        rs_step<1, 4>(v, t2, lane);
+        rs_step<0, 2>(t2, t1, lane);
+        r = t1[0];
+        r += dpp<0x128>(r);  // row_ror:8
+        r += dpp<0x124>(r);  // row_ror:4
+    }
+    return r + swap16(r);
+}
 
 // The record's tap row of pass `pass`, row r, rows of n floats (null: no tap).
 __device__ __forceinline__ float *tap_row(const CallRec *rec, int pass, int r, int n) {
@@ -240,10 +305,12 @@ __device__ __forceinline__ float *tap_row(const CallRec *rec, int pass, int r, i
 // tap: where the writer stores e for the record's tap (row r of pass
 // rs.tap_pass), or null; callers read the record's pointer ahead, with their
 // other loads.
-template <int EPT>
+// xo: if not null, the resulting x, slot for slot (the GEMV's dots read it from
+// registers).
+template <int EPT, int MAP = 0>
 __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float (&h)[EPT], const float (&o)[EPT],
                                     const float (&al)[EPT], const float (&in)[EPT], float *xs, float *red,
-                                    bool writer, float *tap) {
+                                    bool writer, float *tap, float *xo = nullptr) {
     float e[EPT];
     if (!rs.slerp) {
 #pragma unroll
@@ -271,14 +338,14 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
     if (writer && tap) {
 #pragma unroll
         for (int j = 0; j < EPT; j += 4)
-            if (reg_index(j) < H) *reinterpret_cast<float4 *>(tap + reg_index(j)) = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
+            if (elem_index<MAP>(j) < H) *reinterpret_cast<float4 *>(tap + elem_index<MAP>(j)) = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
     }
     if (rs.loop_op == kLoopEnter) {
         float s = 0.f;
 #pragma unroll
         for (int j = 0; j < EPT; j += 4) {
-            if (writer && reg_index(j) < H)
-                *reinterpret_cast<float4 *>(rs.inp + (size_t)r * H + reg_index(j)) =
+            if (writer && elem_index<MAP>(j) < H)
+                *reinterpret_cast<float4 *>(rs.inp + (size_t)r * H + elem_index<MAP>(j)) =
                     make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
         }
 #pragma unroll
@@ -293,8 +360,8 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
         if (rs.loop_op == kLoopExit && writer && rs.e_out)
 #pragma unroll
             for (int j = 0; j < EPT; j += 4)
-                if (reg_index(j) < H)
-                    *reinterpret_cast<float4 *>(rs.e_out + (size_t)r * H + reg_index(j)) =
+                if (elem_index<MAP>(j) < H)
+                    *reinterpret_cast<float4 *>(rs.e_out + (size_t)r * H + elem_index<MAP>(j)) =
                         make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
         float s = 0.f;
 #pragma unroll
@@ -306,8 +373,8 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
             if (writer && rs.st)  // batches: every row's loop state
 #pragma unroll
                 for (int j = 0; j < EPT; j += 4)
-                    if (reg_index(j) < H)
-                        *reinterpret_cast<float4 *>(rs.st + (size_t)r * H + reg_index(j)) =
+                    if (elem_index<MAP>(j) < H)
+                        *reinterpret_cast<float4 *>(rs.st + (size_t)r * H + elem_index<MAP>(j)) =
                             make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
             if (r >= rs.n_next) return;  // this row's loops are over (uniform over the workgroup)
             float s2 = 0.f;
@@ -321,9 +388,12 @@ __device__ inline void resolve_regs(const Resolve &rs, int r, int H, const float
             for (int j = 0; j < EPT; ++j) e[j] *= f;
         }
     }
+    if (xo)
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) xo[j] = e[j];
 #pragma unroll
     for (int j = 0; j < EPT; j += 4) {
-        const int i = reg_index(j);
+        const int i = elem_index<MAP>(j);
         if (i < H) {
             const float4 v = make_float4(e[j], e[j + 1], e[j + 2], e[j + 3]);
             if (xs) *reinterpret_cast<float4 *>(xs + i) = v;

@@ -9,10 +9,12 @@
 // workgroup for the larger matrices, so fewer workgroups repeat the prologue).  The K axis is cut in
 // 512-element chunks (64 lanes x 8 elements = one 16-byte bf16 load per lane),
 // dealt round-robin to the 4 waves; a wave issues the loads of all its chunks
-// for all its rows before the prologue runs, then reduces each row over its 64
-// lanes, and the 4 wave partials are added through LDS.
+// for all its rows before the prologue runs.  Each lane's prologue inputs are
+// the 8 elements of each of its chunks that its dot products take, so x stays
+// in registers; a reduce-scatter leaves each row's sum over a half wave in one
+// lane, and the 8 half-wave partials of a row are added through LDS.
 //
-// Prologues build x in LDS:
+// Prologues build x (in registers):
 //   kProResolve: the previous sub-layer's slerp and the loop mix (Resolve);
 //                workgroup 0 also stores the new residual, loop input and tap.
 //   kProEmbed:   kProResolve for the very first pass of a one-row call, its
@@ -92,9 +94,9 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     constexpr int WR = EPI == kEpiPair ? 2 * ROWS : ROWS;
     constexpr int EPT = 8 * MAXC;  // prologue elements per thread: K <= 2048 * MAXC
     static_assert(ROWS >= 1 && ROWS <= 64 && (ROWS & (ROWS - 1)) == 0, "ROWS: a power of two");
-    float *xs = smem;              // [K]
+    float *xs = smem;              // [K] (the logits-free head path)
     float *red = smem + a.K;       // [16]: two reduction slots
-    float *part = red + 16;        // [4][WR]
+    float *part = red + 16;        // [8][WR]: half-wave partials
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row0 = blockIdx.x * ROWS;
     const int K = a.K, N = a.N;
@@ -108,9 +110,10 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         return;
     }
 
-    // 1. The prologue's inputs, as float4 groups at 4*tid + 1024*jj.  Every load
-    // is unconditional (out-of-range groups re-read group 0 and are zeroed), so
-    // the compiler can count them and wait for exactly these below.
+    // 1. The prologue's inputs, the float4 groups of this lane's dot elements
+    // (elem_index<1>).  Every load is unconditional (out-of-range groups re-read
+    // group 0 and are zeroed), so the compiler can count them and wait for
+    // exactly these below.
     float ph[EPT], po[EPT], pa[EPT], pi[EPT];
     {
         const float *src = (RES ? rs.h : a.src) + (size_t)a.row * K;
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
         }
 #pragma unroll
         for (int jj = 0; jj < EPT / 4; ++jj) {
-            const int i = 4 * tid + 1024 * jj;
+            const int i = elem_index<1>(4 * jj);
             const int ic = i < K ? i : 0;
             float4 v;
             if (PRO == kProEmbed) {
@@ -222,34 +225,32 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     }
     asm volatile("" ::"v"(e0), "v"(e1), "v"(out_row), "v"(tap));
 
-    // 3. x in LDS.
+    // 3. x in registers, slot for slot with the dot elements.
+    float xr[EPT];
     if (RES) {
 #pragma unroll
         for (int jj = 0; jj < EPT / 4; ++jj)
-            if (4 * tid + 1024 * jj >= K)
+            if (elem_index<1>(4 * jj) >= K)
 #pragma unroll
                 for (int c = 0; c < 4; ++c) ph[4 * jj + c] = po[4 * jj + c] = pa[4 * jj + c] = pi[4 * jj + c] = 0.f;
-        resolve_regs<EPT>(rs, a.row, K, ph, po, pa, pi, xs, red, blockIdx.x == 0, tap);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) xr[j] = 0.f;
+        resolve_regs<EPT, 1>(rs, a.row, K, ph, po, pa, pi, nullptr, red, blockIdx.x == 0, tap, xr);
     } else {
         float f = 1.f;
         if (PRO == kProNorm) {
             float s = 0.f;
 #pragma unroll
             for (int j = 0; j < EPT; ++j)
-                if (reg_index(j) < K) s += ph[j] * ph[j];
+                if (elem_index<1>(j) < K) s += ph[j] * ph[j];
             f = norm_factor(block_sum(s, red, 0));
         }
 #pragma unroll
-        for (int jj = 0; jj < EPT / 4; ++jj) {
-            const int i = 4 * tid + 1024 * jj;
-            if (i < K)
-                *reinterpret_cast<float4 *>(xs + i) =
-                    make_float4(ph[4 * jj] * f, ph[4 * jj + 1] * f, ph[4 * jj + 2] * f, ph[4 * jj + 3] * f);
-        }
+        for (int j = 0; j < EPT; ++j) xr[j] = ph[j] * f;
     }
-    __syncthreads();
 
-    // 4. Dot products, wave reductions, the 4 wave partials through LDS.
+    // 4. Dot products; each row's sum over a half wave by the reduce-scatter,
+    // the 8 half-wave partials of a row through LDS.
     float acc[WR];
 #pragma unroll
     for (int j = 0; j < WR; ++j) acc[j] = 0.f;
@@ -257,27 +258,30 @@ __global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
     for (int c = 0; c < MAXC; ++c) {
         const int k0 = (wave + 4 * c) * 512 + lane * 8;
         if (k0 < K) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(xs + k0);
-            const float4 x1 = *reinterpret_cast<const float4 *>(xs + k0 + 4);
+            const float4 x0 = make_float4(xr[8 * c], xr[8 * c + 1], xr[8 * c + 2], xr[8 * c + 3]);
+            const float4 x1 = make_float4(xr[8 * c + 4], xr[8 * c + 5], xr[8 * c + 6], xr[8 * c + 7]);
 #pragma unroll
             for (int j = 0; j < WR; ++j) acc[j] += wv[j][c].dot(x0, x1);
         }
     }
-#pragma unroll
-    for (int j = 0; j < WR; ++j) {
-        const float v = wave_sum63(acc[j]);
-        if (lane == 63) part[wave * WR + j] = valid[j] ? v : 0.f;
+    {
+        const float v = row_sums_rs<WR>(acc, lane);
+        if ((lane & 31) < WR) part[(2 * wave + (lane >> 5)) * WR + (lane & 31)] = v;
     }
     __syncthreads();
     if (tid < ROWS) {
         const int n = row0 + tid;
         if (n < N) {
-            float v = part[tid] + part[WR + tid] + part[2 * WR + tid] + part[3 * WR + tid];
+            float v = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v += part[q * WR + tid];
             if (EPI == kEpiStore) {
                 a.y[n] = v;
             } else if (EPI == kEpiPair) {
                 const int j = ROWS + tid;
-                float b = part[j] + part[WR + j] + part[2 * WR + j] + part[3 * WR + j];
+                float b = 0.f;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) b += part[q * WR + j];
                 float g = v * e0;
                 a.y[n] = g / (1.0f + expf(-g)) * (b * e1);
             } else {
@@ -292,7 +296,7 @@ hipError_t launch_r(const GemvArgs &a, hipStream_t s) {
     const int nch = (a.K + 511) / 512;
     const int maxc = (nch + 3) / 4;
     dim3 grid((a.N + ROWS - 1) / ROWS), block(256);
-    const size_t lds = sizeof(float) * (a.K + 16 + 4 * 2 * ROWS);
+    const size_t lds = sizeof(float) * (a.K + 16 + 8 * 2 * ROWS);
     switch (maxc) {
         case 1: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 1, ROWS>), grid, block, lds, s, a); break;
         case 2: hipLaunchKernelGGL((k_gemv<WT, PRO, EPI, 2, ROWS>), grid, block, lds, s, a); break;
